@@ -1,0 +1,159 @@
+"""fp64 CPU oracle for the KDA gated delta-rule recurrence.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP
+library never calls it, and the two share no code.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, double precision, a token
+loop: forget, predict, correct and write, read).  This module only converts
+inputs to contiguous float64 arrays, reorders the [B, T, H, d] token layout
+into per-unit blocks, and calls the C library through ctypes.
+
+Pins: every function here is pinned by ``tests/test_oracle.py`` against
+closed forms, brute force and invariants stated on the pages; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc into ``oracle/libkda_oracle.so``."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC", "-shared",
+             "-pthread", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kda_oracle_forward.restype = ctypes.c_int
+        lib.kda_oracle_forward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                           ctypes.c_long, ctypes.c_long, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_double, ctypes.c_int]
+        lib.kda_oracle_step.restype = ctypes.c_int
+        lib.kda_oracle_step.argtypes = [dp, dp, dp, dp, dp, dp, dp,
+                                        ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_double, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    """Exact widening of a stored tensor/array (fp32, bf16, fp64) to float64."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16 has no numpy dtype
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def forward_units(q, k, v, alpha, beta, initial_state=None, scale=None, threads=0,
+                  want_o=True):
+    """Token loop over independent units.
+
+    q, k, alpha: [U, T, dk]; v: [U, T, dv]; beta: [U, T];
+    initial_state: [U, dk, dv] or None (zero state).
+    Returns (o [U, T, dv] or None, final_state [U, dk, dv]), float64.
+    """
+    q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
+    s0 = _f64(initial_state)
+    U, T, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (U, T, dk) and alpha.shape == (U, T, dk)
+    assert v.shape == (U, T, dv) and beta.shape == (U, T)
+    if s0 is not None:
+        assert s0.shape == (U, dk, dv)
+    if scale is None:
+        scale = dk ** -0.5
+    o = np.zeros((U, T, dv), np.float64) if want_o else None
+    sT = np.zeros((U, dk, dv), np.float64)
+    rc = _load().kda_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(s0), _ptr(o), _ptr(sT), U, T, dk, dv,
+                                    float(scale), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_forward failed with %d" % rc)
+    return o, sT
+
+
+def forward(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, scale=None,
+            threads=0, heads=None):
+    """Oracle in the library's token layout.
+
+    Dense:  q, k, alpha [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
+            initial_state [B, H, dk, dv] or None.
+    Varlen: B == 1, cu_seqlens (length N+1, host ints) splits T into N
+            sequences; initial_state [N, H, dk, dv] or None.
+    heads:  optional list of head indices to evaluate (a sample); the result
+            then holds only those heads, in that order.
+    Returns (o [B, T, Hs, dv], final_state [B or N, Hs, dk, dv]), float64.
+    """
+    q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
+    s0 = _f64(initial_state)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    hs = list(range(H)) if heads is None else list(heads)
+    sel = np.asarray(hs, dtype=np.int64)
+    if cu_seqlens is None:
+        starts = [(b, 0, T) for b in range(B)]
+    else:
+        assert B == 1
+        cu = [int(c) for c in cu_seqlens]
+        starts = [(0, cu[n], cu[n + 1] - cu[n]) for n in range(len(cu) - 1)]
+    o_all = np.zeros((B, T, len(hs), dv), np.float64)
+    s_all = np.zeros((len(starts), len(hs), dk, dv), np.float64)
+    for n, (b, t0, L) in enumerate(starts):
+        def units(x):  # [L, Hs, d] -> [Hs, L, d]
+            return np.ascontiguousarray(np.moveaxis(x[b, t0:t0 + L][:, sel], 1, 0))
+        init = None if s0 is None else s0[n][sel]
+        o_u, s_u = forward_units(units(q), units(k), units(v), units(alpha),
+                                 np.ascontiguousarray(beta[b, t0:t0 + L][:, sel].T),
+                                 init, scale=scale, threads=threads)
+        o_all[b, t0:t0 + L] = np.moveaxis(o_u, 0, 1)
+        s_all[n] = s_u
+    return o_all, s_all
+
+
+def step(q, k, v, alpha, beta, state, scale=None, threads=0):
+    """One decode step.  q, k, alpha [N, H, dk]; v [N, H, dv]; beta [N, H];
+    state [N, H, dk, dv].  Returns (o [N, H, dv], new_state), float64; the
+    input state is not modified."""
+    q, k, v, alpha, beta, st = (_f64(x) for x in (q, k, v, alpha, beta, state))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if scale is None:
+        scale = dk ** -0.5
+    st = st.reshape(N * H, dk, dv).copy()
+    o = np.zeros((N * H, dv), np.float64)
+    rc = _load().kda_oracle_step(_ptr(np.ascontiguousarray(q.reshape(N * H, dk))),
+                                 _ptr(np.ascontiguousarray(k.reshape(N * H, dk))),
+                                 _ptr(np.ascontiguousarray(v.reshape(N * H, dv))),
+                                 _ptr(np.ascontiguousarray(alpha.reshape(N * H, dk))),
+                                 _ptr(np.ascontiguousarray(beta.reshape(N * H))),
+                                 _ptr(st), _ptr(o), N * H, dk, dv, float(scale), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_step failed with %d" % rc)
+    return o.reshape(N, H, dv), st.reshape(N, H, dk, dv)

@@ -1,0 +1,278 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Every pin is a function ``pin(impl, rng) -> error`` where ``impl`` maps one
+unit's inputs (q, k, v, alpha, beta, s0, scale) to (o [T, dv], S_T [dk, dv]).
+The oracle must meet each pin to ~1e-12; every planted mistake in
+``mutants.py`` must fail at least one pin by a wide margin.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import brute
+import mutants
+import oracle
+
+TOL = 1e-11
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def oracle_impl(q, k, v, alpha, beta, s0, scale):
+    o, s = oracle.forward_units(q[None], k[None], v[None], alpha[None], beta[None],
+                                s0[None], scale=scale, threads=1)
+    return o[0], s[0]
+
+
+def unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def rel(a, b):
+    den = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den)
+
+
+def draw(rng, T, dk, dv, s0_std=0.3):
+    q = unit(rng.standard_normal((T, dk)))
+    k = unit(rng.standard_normal((T, dk)))
+    v = rng.standard_normal((T, dv))
+    alpha = 1.0 / (1.0 + np.exp(-rng.normal(2.0, 1.0, (T, dk))))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(T)))
+    s0 = s0_std * rng.standard_normal((dk, dv))
+    return q, k, v, alpha, beta, s0
+
+
+# ---------------------------------------------------------------- the pins
+
+def pin_requery(impl, rng, dk=6, dv=6, T=7):
+    """beta = 1 and a unit-norm key: right after the write, querying the state
+    with that key gives back the written value exactly (bugfactory.tech news
+    3610, second paragraph).  The read uses q_t = k_t, so o_t = scale * v_t."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    beta[:] = 1.0
+    q = k.copy()
+    o, _ = impl(q, k, v, alpha, beta, s0, 0.5)
+    return rel(o, 0.5 * v)
+
+
+def pin_orthogonal(impl, rng, dk=6, dv=5, T=6):
+    """Directions orthogonal to the current key are only decayed
+    (bugfactory.tech news 3610, second paragraph, with the decay-first order of
+    the third and fourth paragraphs): for x orthogonal to k_t,
+    S_t^T x = S_{t-1}^T Diag(alpha_t) x.  S_{t-1} comes from the same
+    implementation run on the prefix."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    x = rng.standard_normal(dk)
+    x -= (x @ k[-1]) * k[-1]
+    q[-1] = x
+    o, _ = impl(q, k, v, alpha, beta, s0, 1.0)
+    _, s_prev = impl(q[:-1], k[:-1], v[:-1], alpha[:-1], beta[:-1], s0, 1.0)
+    return rel(o[-1], s_prev.T @ (alpha[-1] * x))
+
+
+def pin_deltanet(impl, rng, dk=5, dv=4, T=9):
+    """alpha = 1: the matrix form of DeltaNet in the |v><k| convention
+    (bugfactory.tech news 3610, second paragraph)."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    alpha[:] = 1.0
+    o, s = impl(q, k, v, alpha, beta, s0, 0.7)
+    o_r, s_r = brute.deltanet_matrix_form(q, k, v, beta, s0, 0.7)
+    return max(rel(o, o_r), rel(s, s_r))
+
+
+def pin_gated_deltanet(impl, rng, dk=5, dv=4, T=9):
+    """alpha_t constant across channels: Gated DeltaNet, the whole memory
+    scaled by a scalar before the delta step (bugfactory.tech news 3610, third
+    paragraph; the per-head scalar gate row of the table in "Kimi Delta
+    Attention", section "一、Diag(α_t)：通道级遗忘")."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    g = 1.0 / (1.0 + np.exp(-rng.normal(1.0, 1.0, T)))
+    alpha = np.repeat(g[:, None], dk, axis=1)
+    o, s = impl(q, k, v, alpha, beta, s0, 0.7)
+    o_r, s_r = brute.deltanet_matrix_form(q, k, v, beta, s0, 0.7, gate=g)
+    return max(rel(o, o_r), rel(s, s_r))
+
+
+def pin_brute_force(impl, rng, dk=4, dv=3, T=6):
+    """Unrolled product of the per-token transitions A_t = (I - beta k k^T)
+    Diag(alpha) ("Kimi Delta Attention", section "KDA 的更新式")."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    # non-unit keys and arbitrary beta, so no special structure helps
+    k = k * rng.uniform(0.5, 1.5, (T, 1))
+    o, s = impl(q, k, v, alpha, beta, s0, 0.9)
+    o_r, s_r = brute.product_of_transitions(q, k, v, alpha, beta, s0, 0.9)
+    return max(rel(o, o_r), rel(s, s_r))
+
+
+def pin_linear_attention(impl, rng, dk=8, dv=5, T=6):
+    """Orthonormal keys, beta = 1, alpha = 1, zero start: the delta rule never
+    has anything to erase, so the result is plain causal linear attention,
+    S_T = K^T V and O = scale tril(Q K^T) V (the additive update of "Kimi Delta
+    Attention", section "先建立直觉：从缓存到状态")."""
+    qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = qm[:T].copy()  # orthonormal rows
+    q = rng.standard_normal((T, dk))
+    v = rng.standard_normal((T, dv))
+    alpha = np.ones((T, dk))
+    beta = np.ones(T)
+    o, s = impl(q, k, v, alpha, beta, np.zeros((dk, dv)), 0.4)
+    o_r, s_r = brute.causal_linear_attention(q, k, v, 0.4)
+    return max(rel(o, o_r), rel(s, s_r))
+
+
+def pin_no_write(impl, rng, dk=5, dv=4, T=7):
+    """beta = 0: nothing is written, the state only decays per channel:
+    S_t = Diag(prod_{i<=t} alpha_i) S0 and o_t = scale S_t^T q_t ("Kimi Delta
+    Attention", section "一、Diag(α_t)：通道级遗忘")."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    beta[:] = 0.0
+    o, s = impl(q, k, v, alpha, beta, s0, 1.3)
+    cum = np.cumprod(alpha, axis=0)
+    o_r = np.stack([1.3 * (cum[t][:, None] * s0).T @ q[t] for t in range(T)])
+    return max(rel(o, o_r), rel(s, cum[-1][:, None] * s0))
+
+
+def pin_gradient_step(impl, rng, dk=5, dv=4, T=5):
+    """The delta write is one gradient-descent step of size beta on
+    L(S) = 1/2 ||S^T k - v||^2, taken at the decayed state (bugfactory.tech news
+    3610, second paragraph; the Widrow-Hoff / LMS view on the kongchang.com
+    page, section "Delta规则如何解决这一问题？").  The gradient is taken by
+    central differences, which are exact for a quadratic up to rounding."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    k = k * 1.7  # a non-unit key so the step size matters
+    _, s_prev = impl(q[:-1], k[:-1], v[:-1], alpha[:-1], beta[:-1], s0, 1.0)
+    _, s_t = impl(q, k, v, alpha, beta, s0, 1.0)
+    s_tilde = alpha[-1][:, None] * s_prev
+
+    def loss(S):
+        r = S.T @ k[-1] - v[-1]
+        return 0.5 * float(r @ r)
+
+    h = 1e-3
+    grad = np.zeros_like(s_tilde)
+    for i in range(dk):
+        for j in range(dv):
+            e = np.zeros_like(s_tilde)
+            e[i, j] = h
+            grad[i, j] = (loss(s_tilde + e) - loss(s_tilde - e)) / (2 * h)
+    return rel(s_t, s_tilde - beta[-1] * grad)
+
+
+def pin_superposition(impl, rng, dk=5, dv=4, T=8):
+    """For fixed (q, k, alpha, beta) the map (S0, V) -> (O, S_T) is linear: the
+    update equation of "Kimi Delta Attention", section "KDA 的更新式", is
+    affine in S and in v_t."""
+    q, k, v1, alpha, beta, s1 = draw(rng, T, dk, dv)
+    v2 = rng.standard_normal((T, dv))
+    s2 = rng.standard_normal((dk, dv))
+    c = -0.75
+    o1, f1 = impl(q, k, v1, alpha, beta, s1, 1.0)
+    o2, f2 = impl(q, k, v2, alpha, beta, s2, 1.0)
+    o3, f3 = impl(q, k, v1 + c * v2, alpha, beta, s1 + c * s2, 1.0)
+    return max(rel(o3, o1 + c * o2), rel(f3, f1 + c * f2))
+
+
+def pin_resume(impl, rng, dk=5, dv=4, T=9, split=4):
+    """The fixed-size state is all that is carried between segments (the
+    chunk-wise form on the kongchang.com page, section "硬件效率的优化策略"):
+    running x1 then x2 from x1's final state equals running x1 || x2."""
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    o, s = impl(q, k, v, alpha, beta, s0, 1.0)
+    oa, sa = impl(q[:split], k[:split], v[:split], alpha[:split], beta[:split], s0, 1.0)
+    ob, sb = impl(q[split:], k[split:], v[split:], alpha[split:], beta[split:], sa, 1.0)
+    return max(rel(o, np.concatenate([oa, ob])), rel(s, sb))
+
+
+def pin_rewrite(impl, rng, dk=6, dv=5):
+    """The same key written twice with beta = 1, alpha = 1 keeps only the
+    latest value; nothing accumulates ("Kimi Delta Attention", section
+    "二、I − β_t k_t k_tᵀ：delta 规则")."""
+    k1 = unit(rng.standard_normal(dk))
+    k = np.stack([k1, k1])
+    v = rng.standard_normal((2, dv))
+    q = k.copy()
+    o, _ = impl(q, k, v, np.ones((2, dk)), np.ones(2), rng.standard_normal((dk, dv)), 1.0)
+    return rel(o[1], v[1])
+
+
+PINS = [pin_requery, pin_orthogonal, pin_deltanet, pin_gated_deltanet, pin_brute_force,
+        pin_linear_attention, pin_no_write, pin_gradient_step, pin_superposition,
+        pin_resume, pin_rewrite]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_oracle_meets_pin(pin, seed):
+    err = pin(oracle_impl, np.random.default_rng(seed))
+    tol = 1e-8 if pin is pin_gradient_step else TOL
+    assert err < tol, (pin.__name__, err)
+
+
+@pytest.mark.parametrize("mistake", mutants.MISTAKES)
+def test_every_mutant_fails_a_pin(mistake):
+    impl = mutants.make(mistake)
+    worst = 0.0
+    for pin in PINS:
+        try:
+            worst = max(worst, pin(impl, np.random.default_rng(7)))
+        except ValueError:  # a shape-breaking mistake fails outright
+            worst = np.inf
+    assert worst > 1e-3, (mistake, worst)
+
+
+def test_worked_example():
+    """A 2x2 two-token example worked by hand from the four steps (forget,
+    predict, correct and write, read); see tests/golden/worked_2x2.json."""
+    with open(os.path.join(GOLDEN, "worked_2x2.json")) as f:
+        g = json.load(f)
+    arr = {key: np.asarray(val, dtype=np.float64) for key, val in g["inputs"].items()}
+    o, s = oracle_impl(arr["q"], arr["k"], arr["v"], arr["alpha"], arr["beta"], arr["s0"],
+                       float(g["inputs"]["scale"]))
+    assert rel(o, np.asarray(g["expected"]["o"])) < 1e-14
+    assert rel(s, np.asarray(g["expected"]["state"])) < 1e-14
+
+
+def test_empty_sequence_keeps_state():
+    rng = np.random.default_rng(3)
+    s0 = rng.standard_normal((1, 4, 3))
+    e = np.zeros((1, 0, 4))
+    o, s = oracle.forward_units(e, e, np.zeros((1, 0, 3)), e, np.zeros((1, 0)), s0)
+    assert o.shape == (1, 0, 3)
+    assert np.array_equal(s, s0)
+
+
+def test_layouts_and_varlen_match_units():
+    """The [B, T, H, d] wrapper, the varlen split and the decode step are
+    re-arrangements of the same unit loop (units are independent; a decode step
+    is one token)."""
+    rng = np.random.default_rng(4)
+    B, T, H, dk, dv = 2, 11, 3, 4, 5
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    a = rng.uniform(0.3, 1.0, (B, T, H, dk))
+    b = rng.uniform(0.0, 1.0, (B, T, H))
+    s0 = rng.standard_normal((B, H, dk, dv))
+    o, s = oracle.forward(q, k, v, a, b, s0)
+    for bb in range(B):
+        for h in range(H):
+            o_u, s_u = oracle_impl(q[bb, :, h], k[bb, :, h], v[bb, :, h], a[bb, :, h],
+                                   b[bb, :, h], s0[bb, h], dk ** -0.5)
+            assert rel(o[bb, :, h], o_u) < 1e-15 and rel(s[bb, h], s_u) < 1e-15
+    # varlen: pack both batch rows as two sequences plus an empty one
+    cu = [0, T, T, 2 * T]
+    pk = lambda x: x.reshape((1, B * T) + x.shape[2:])
+    s0v = np.concatenate([s0[:1], rng.standard_normal((1, H, dk, dv)), s0[1:]])
+    ov, sv = oracle.forward(pk(q), pk(k), pk(v), pk(a), pk(b), s0v, cu_seqlens=cu)
+    assert rel(ov[0], pk(o)[0]) < 1e-15
+    assert np.array_equal(sv[1], s0v[1])
+    assert rel(sv[[0, 2]], s) < 1e-15
+    # head sample
+    oh, sh = oracle.forward(q, k, v, a, b, s0, heads=[2, 0])
+    assert np.array_equal(oh, o[:, :, [2, 0]]) and np.array_equal(sh, s[:, [2, 0]])
+    # one decode step == forward with T = 1
+    o1, st1 = oracle.step(q[:, 0], k[:, 0], v[:, 0], a[:, 0], b[:, 0], s0)
+    of, sf = oracle.forward(q[:, :1], k[:, :1], v[:, :1], a[:, :1], b[:, :1], s0)
+    assert np.array_equal(o1, of[:, 0]) and np.array_equal(st1, sf)

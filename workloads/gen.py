@@ -1,0 +1,97 @@
+"""Seeded generators.  Values are drawn in float64 with torch's generator on
+the target device (numpy-free so full-size workloads can be drawn on the GPU),
+then rounded once to the storage dtype (round-to-nearest-even for bf16).
+Draw order is fixed: [lengths], q, k, v, beta logits, alpha logits, S0."""
+import torch
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _normal(shape, g, device, mean=0.0, std=1.0):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float64)
+    return x * std + mean if (mean != 0.0 or std != 1.0) else x
+
+
+def _unit(x):
+    return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+
+
+def draw_chunk(B, T, H, dk, dv, dtype="bf16", alpha_mu=4.0, alpha_sigma=1.0, s0_std=None,
+               num_states=None, seed=0, device="cpu", lengths=None):
+    """Draw one chunked-forward input set.
+
+    Returns a dict with q, k [B,T,H,dk] and v [B,T,H,dv] in the storage dtype,
+    alpha [B,T,H,dk] and beta [B,T,H] in float32, initial_state
+    [num_states or B, H, dk, dv] float32 (or None), on ``device``.
+    """
+    g = _gen(device, seed)
+    dt = _DT[dtype]
+    q = _unit(_normal((B, T, H, dk), g, device)).to(dt)
+    k = _unit(_normal((B, T, H, dk), g, device)).to(dt)
+    v = _normal((B, T, H, dv), g, device).to(dt)
+    beta = torch.sigmoid(_normal((B, T, H), g, device)).to(torch.float32)
+    alpha = torch.sigmoid(_normal((B, T, H, dk), g, device, alpha_mu, alpha_sigma)).to(torch.float32)
+    ns = B if num_states is None else num_states
+    s0 = None
+    if s0_std is not None:
+        s0 = _normal((ns, H, dk, dv), g, device, 0.0, s0_std).to(torch.float32)
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), alpha=alpha.contiguous(),
+                beta=beta.contiguous(), initial_state=s0)
+
+
+def varlen_lengths(num_seqs, lo, hi, seed):
+    """Integer lengths uniform on [lo, hi] inclusive, drawn on the CPU."""
+    g = _gen("cpu", 1000003 + int(seed))
+    return [int(x) for x in torch.randint(lo, hi + 1, (num_seqs,), generator=g)]
+
+
+def chunk_inputs(cfg, device="cpu", T=None, B=None, H=None, seed=None):
+    """Inputs of a chunked-forward workload; T/B/H override the sizes for
+    reduced versions.  Varlen workloads also get cu_seqlens (host list and an
+    int32 tensor on ``device``)."""
+    seed = cfg.seed if seed is None else seed
+    H = cfg.H if H is None else H
+    if cfg.num_seqs:
+        lens = varlen_lengths(cfg.num_seqs, cfg.len_range[0], cfg.len_range[1], seed)
+        if T is not None:  # reduced: scale every length down, keep the mix
+            total = sum(lens)
+            lens = [max(1, (l * T) // total) for l in lens]
+        cu = [0]
+        for l in lens:
+            cu.append(cu[-1] + l)
+        d = draw_chunk(1, cu[-1], H, cfg.dk, cfg.dv, cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std,
+                       num_states=len(lens), seed=seed, device=device)
+        d["cu_seqlens_host"] = cu
+        d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=device)
+        return d
+    d = draw_chunk(cfg.B if B is None else B, cfg.T if T is None else T, H, cfg.dk, cfg.dv,
+                   cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std, seed=seed, device=device)
+    d["cu_seqlens_host"] = None
+    d["cu_seqlens"] = None
+    return d
+
+
+def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None):
+    """Decode workload: initial state [N,H,dk,dv] float32 and per-step inputs
+    stacked on a leading step axis: q, k [S,N,H,dk], v [S,N,H,dv] (storage
+    dtype), alpha [S,N,H,dk], beta [S,N,H] float32."""
+    seed = cfg.seed if seed is None else seed
+    N = cfg.B if N is None else N
+    H = cfg.H if H is None else H
+    steps = cfg.steps if steps is None else steps
+    g = _gen(device, seed)
+    dt = _DT[cfg.dtype]
+    state = _normal((N, H, cfg.dk, cfg.dv), g, device, 0.0, cfg.s0_std).to(torch.float32)
+    q = _unit(_normal((steps, N, H, cfg.dk), g, device)).to(dt)
+    k = _unit(_normal((steps, N, H, cfg.dk), g, device)).to(dt)
+    v = _normal((steps, N, H, cfg.dv), g, device).to(dt)
+    beta = torch.sigmoid(_normal((steps, N, H), g, device)).to(torch.float32)
+    alpha = torch.sigmoid(_normal((steps, N, H, cfg.dk), g, device, cfg.alpha_mu)).to(torch.float32)
+    return dict(state=state.contiguous(), q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
+                alpha=alpha.contiguous(), beta=beta.contiguous())
