@@ -1,0 +1,193 @@
+"""libkda: the Kimi Delta Attention (KDA) gated delta-rule recurrence on MI355X.
+
+A thin Python binding over the C ABI in ``include/kda.h``.  It only checks
+and marshals arguments: torch supplies device memory, output allocation and
+the current stream; every step of the computation runs in the HIP kernels of
+``libkda.so``.  There is no fallback: if the library is missing or was built
+for another GPU, the calls fail.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
+           "kda_status_string", "kda_version", "KDAError", "LIB_PATH", "load_library"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+_STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
+           3: "KDA_ERROR_MISALIGNED", 4: "KDA_ERROR_INSUFFICIENT_WORKSPACE", 5: "KDA_ERROR_HIP"}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, kda_status_string(status)))
+
+
+def load_library():
+    """Load libkda.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libkda.so not found at %s; build it first "
+                              "(python -c 'import __graft_entry__ as g; g.build()')" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, fp = ctypes.c_void_p, ctypes.c_void_p
+        ip = ctypes.POINTER(ctypes.c_int)
+        i, f, sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.kda_chunk_fwd.restype = i
+        lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
+                                      vp, ip, i, f, i, vp, sz, vp]
+        lib.kda_recurrent_step.restype = i
+        lib.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, vp]
+        lib.kda_chunk_fwd_workspace_size.restype = sz
+        lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_status_string.argtypes = [i]
+        lib.kda_version.restype = i
+        lib.kda_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def kda_status_string(status):
+    if _lib is None and not os.path.exists(LIB_PATH):
+        return _STATUS.get(int(status), "unknown status")
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_version():
+    return load_library().kda_version()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype=torch.bfloat16):
+    code = KDA_DTYPE_BF16 if dtype == torch.bfloat16 else KDA_DTYPE_F32
+    return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, code))
+
+
+def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
+                  cu_seqlens_host=None, scale=None, output_final_state=True,
+                  final_state=None, o=None, chunk_size=64):
+    """Chunk-wise KDA forward.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype);
+    alpha: [B, T, H, dk] fp32; beta: [B, T, H] fp32;
+    initial_state: [B or N, H, dk, dv] fp32 or None (zero start).
+    Varlen: B == 1 and cu_seqlens (int32 device tensor of N+1 offsets) with
+    its host copy cu_seqlens_host (list or CPU tensor; derived with a copy if
+    omitted).  final_state may be passed (e.g. initial_state itself for an
+    in-place update); o may be passed as a preallocated output.
+    Returns (o, final_state or None).
+    """
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(q, "q", dt, dev)
+    _check(k, "k", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    _check(alpha, "alpha", torch.float32, dev, (B, T, H, dk))
+    _check(beta, "beta", torch.float32, dev, (B, T, H))
+    num_seqs = 0
+    cu_dev = None
+    cu_host_arr = None
+    if cu_seqlens is not None or cu_seqlens_host is not None:
+        if cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.to("cpu")
+        host = [int(x) for x in (cu_seqlens_host.tolist() if isinstance(cu_seqlens_host, torch.Tensor)
+                                 else cu_seqlens_host)]
+        if cu_seqlens is None:
+            cu_seqlens = torch.tensor(host, dtype=torch.int32, device=dev)
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (len(host),))
+        num_seqs = len(host) - 1
+        cu_dev = cu_seqlens
+        cu_host_arr = (ctypes.c_int * len(host))(*host)
+    nstates = num_seqs if num_seqs > 0 else B
+    sshape = (nstates, H, dk, dv)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.float32, dev, sshape)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dt, dev, (B, T, H, dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", torch.float32, dev, sshape)
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, code))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                           _ptr(initial_state), _ptr(o), _ptr(final_state),
+                           B, T, H, dk, dv, code, _ptr(cu_dev), cu_host_arr, num_seqs,
+                           float(scale) if scale is not None else 0.0, int(chunk_size),
+                           _ptr(ws), ws_bytes, _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def kda_recurrent_step(q, k, v, alpha, beta, state, scale=None, o=None):
+    """One decode step; ``state`` [N, H, dk, dv] fp32 is updated in place.
+    q, k: [N, H, dk]; v: [N, H, dv]; alpha: [N, H, dk] fp32; beta: [N, H] fp32.
+    Returns o [N, H, dv]."""
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(q, "q", dt, dev)
+    _check(k, "k", dt, dev, (N, H, dk))
+    _check(v, "v", dt, dev, (N, H, dv))
+    _check(alpha, "alpha", torch.float32, dev, (N, H, dk))
+    _check(beta, "beta", torch.float32, dev, (N, H))
+    _check(state, "state", torch.float32, dev, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dt, dev, (N, H, dv))
+    st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                                _ptr(o), N, H, dk, dv, code,
+                                float(scale) if scale is not None else 0.0, _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_recurrent_step")
+    return o

@@ -1,0 +1,43 @@
+// kda_launch.h -- internal launchers behind the C ABI.  Arguments are
+// already validated by kda_api.cpp; these only choose an instantiation and
+// enqueue it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct StepArgs {
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    float *state;
+    void *o;
+    int N, H, dk, dv;
+    bool bf16;
+    float scale;
+};
+
+hipError_t launch_recurrent_step(const StepArgs &a, hipStream_t stream);
+
+struct ChunkArgs {
+    const void *q, *k, *v;
+    const float *alpha, *beta;
+    const float *s0;
+    void *o;
+    float *sT;
+    int B, T, H, dk, dv;
+    bool bf16;
+    const int *cu_seqlens;  // device, NULL in dense mode
+    int num_seqs;           // 0 in dense mode
+    int *order;             // device workspace for the longest-first order (varlen), or NULL
+    float scale;
+    int dvt;                // value columns per workgroup (0 = choose)
+};
+
+hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
+
+// value-column tile the planner picks for a given number of units
+int plan_chunk_dvt(int units, int dv, bool bf16);
+
+}  // namespace kda

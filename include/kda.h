@@ -1,0 +1,137 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) gated delta-rule
+ * recurrence on AMD Instinct MI355X (gfx950).
+ *
+ * The method.  Per independent unit (one batch entry or packed sequence, one
+ * head) the state S is a dk x dv fp32 matrix (row = key channel, column =
+ * value channel).  For each token t in order:
+ *   forget   S~  = Diag(alpha_t) S_{t-1}          alpha_t in (0,1]^dk
+ *   predict  vh  = S~^T k_t
+ *   write    S_t = S~ + beta_t k_t (v_t - vh)^T   beta_t scalar per token/head
+ *   read     o_t = scale * S_t^T q_t              scale = dk^{-1/2} by default
+ * Source: "Kimi Delta Attention" (daiw.net, Kimi K3 manual), section
+ * "KDA 的更新式" (the update S_t = (I - beta k k^T) Diag(alpha) S_{t-1}
+ * + beta k v^T) and sections "一" (per-channel alpha) and "二" (delta rule);
+ * bugfactory.tech news 3610, second to fourth paragraphs (the order forget,
+ * predict, correct, write, read, and the dk^{-1/2} read scale).  The fifth
+ * paragraph there names the two compute modes exposed here: a chunk-wise mode
+ * for training and long contexts, and a token-by-token recurrent mode for
+ * decoding.
+ *
+ * Conventions shared by every entry point:
+ *  - Memory.  All tensor pointers are DEVICE pointers owned by the caller;
+ *    tensors are dense, row-major (last index fastest).  Alignment: the
+ *    chunk-wise q, k and alpha 8 bytes (read in pairs), the decode state 16
+ *    bytes (read as float4), every other pointer its element size.  The
+ *    library keeps no state between calls and allocates no device memory.
+ *  - Streams.  Work is enqueued on `stream` (0 = the null stream) and the
+ *    call returns without synchronising.  A launch failure returns
+ *    KDA_ERROR_HIP; faults inside a kernel surface at the caller's next
+ *    synchronisation.
+ *  - Errors.  Arguments are validated on the host before anything is
+ *    enqueued; on any error nothing is launched and no output is touched.
+ *    The library never prints, throws across the ABI or aborts.
+ *  - Thread safety.  Entry points are reentrant.
+ *  - Supported shapes.  dk, dv in {64, 128}; chunk_size == 64.
+ *  - Numerical domain.  alpha in (0, 1] (alpha = 1 is exact: DeltaNet).  The
+ *    chunk-wise kernel scales keys by cumulative decays referenced to the
+ *    middle of each 64-token chunk, so the product of alpha over any 32
+ *    consecutive tokens of a chunk must stay above 2^-126 per channel
+ *    (roughly: mean alpha above 0.066 over a half chunk); beyond that, results
+ *    overflow.  The recurrent step has no such limit.  NaN/Inf propagate.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_SUCCESS = 0,
+    KDA_ERROR_INVALID_VALUE = 1,          /* null pointer, negative size, bad cu_seqlens, overlap */
+    KDA_ERROR_NOT_SUPPORTED = 2,          /* dk/dv/chunk_size outside the supported set */
+    KDA_ERROR_MISALIGNED = 3,             /* a pointer breaks the alignment rules above */
+    KDA_ERROR_INSUFFICIENT_WORKSPACE = 4, /* workspace smaller than kda_chunk_fwd_workspace_size() */
+    KDA_ERROR_HIP = 5                     /* the HIP runtime rejected a launch */
+} kda_status;
+
+typedef enum {
+    KDA_DTYPE_F32 = 0,  /* q, k, v and o are float32 */
+    KDA_DTYPE_BF16 = 1  /* q, k, v and o are bfloat16; o is rounded to nearest even */
+} kda_dtype;
+
+/*
+ * Device workspace (bytes) that kda_chunk_fwd needs.  Dense calls
+ * (num_seqs == 0) need none; packed variable-length calls need 4 bytes per
+ * sequence (rounded up to 256), used to order sequences longest first.
+ * Returns 0 for arguments kda_chunk_fwd would reject.
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                    kda_dtype dtype);
+
+/*
+ * Chunk-wise forward (64-token chunks) over whole sequences.
+ * Source: the chunk-wise mode of bugfactory.tech news 3610, fifth paragraph,
+ * and the chunk-parallel scheme on the kongchang.com page, section
+ * "硬件效率的优化策略" (matrix products inside a chunk, the state carried
+ * between chunks).
+ *
+ * Dense mode (cu_seqlens_dev == NULL, num_seqs == 0):
+ *   q, k    [B, T, H, dk]  dtype
+ *   v, o    [B, T, H, dv]  dtype        (o is written)
+ *   alpha   [B, T, H, dk]  float32
+ *   beta    [B, T, H]      float32
+ *   initial_state, final_state  [B, H, dk, dv] float32
+ * Packed variable-length mode (num_seqs >= 1, B == 1):
+ *   sequence n occupies tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the
+ *   T = cu_seqlens[num_seqs] packed tokens; states are [num_seqs, H, dk, dv].
+ *   cu_seqlens_dev (device) and cu_seqlens_host (host) hold the same
+ *   num_seqs + 1 non-decreasing int32 offsets starting at 0; the host copy is
+ *   used for validation and launch planning without a device sync.
+ *   Empty sequences are allowed (final = initial).
+ * initial_state == NULL means a zero start.  final_state == NULL skips the
+ * state store.  initial_state == final_state updates the state in place.
+ * scale <= 0 selects dk^{-1/2}.  chunk_size must be 64.
+ * workspace: device memory of at least kda_chunk_fwd_workspace_size() bytes
+ * (may be NULL when that is 0).  Outputs must not overlap inputs except for
+ * the in-place state.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *alpha,
+                         const float *beta, const float *initial_state, void *o,
+                         float *final_state, int B, int T, int H, int dk, int dv,
+                         kda_dtype dtype, const int *cu_seqlens_dev,
+                         const int *cu_seqlens_host, int num_seqs, float scale,
+                         int chunk_size, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * One decode step, state updated in place.
+ * Source: the fused recurrent mode of bugfactory.tech news 3610, fifth
+ * paragraph (the sequence is processed token by token, state tiles updated
+ * independently per batch entry and head); one call is one token.
+ *   q, k   [N, H, dk]  dtype
+ *   v, o   [N, H, dv]  dtype     (o is written)
+ *   alpha  [N, H, dk]  float32
+ *   beta   [N, H]      float32
+ *   state  [N, H, dk, dv] float32, read and rewritten
+ * scale <= 0 selects dk^{-1/2}.  o must not overlap state or the inputs.
+ */
+kda_status kda_recurrent_step(const void *q, const void *k, const void *v, const float *alpha,
+                              const float *beta, float *state, void *o, int N, int H, int dk,
+                              int dv, kda_dtype dtype, float scale, hipStream_t stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *kda_status_string(kda_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

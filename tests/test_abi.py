@@ -1,0 +1,174 @@
+"""The C-ABI library loads without a GPU, exports every symbol kda.h declares,
+and rejects every invalid argument before any HIP call (so these run on the
+CPU with fake, never-dereferenced device addresses)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIB = os.path.join(ROOT, "gated_delta_rule_38_amd", "libkda.so")
+
+SUCCESS, INVALID, NOT_SUPPORTED, MISALIGNED, WORKSPACE, HIP = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    import gated_delta_rule_38_amd as kda
+    return kda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
+              "kda_status_string", "kda_version"]:
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings_cover_every_code(lib):
+    names = [lib.kda_status_string(i).decode() for i in range(6)]
+    assert names == ["KDA_SUCCESS", "KDA_ERROR_INVALID_VALUE", "KDA_ERROR_NOT_SUPPORTED",
+                     "KDA_ERROR_MISALIGNED", "KDA_ERROR_INSUFFICIENT_WORKSPACE", "KDA_ERROR_HIP"]
+    assert lib.kda_status_string(99).decode() == "unknown status"
+    assert lib.kda_version() >= 100
+
+
+# fake device addresses, far apart and 256-byte aligned; never dereferenced
+BASE = 0x7F0000000000
+GAP = 1 << 36
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * GAP + off)
+
+
+def chunk_call(lib, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), s0=fake(5), o=fake(6),
+             sT=fake(7), B=2, T=100, H=4, dk=128, dv=128, dt=1, cu_dev=None, cu_host=None,
+             num_seqs=0, scale=0.0, chunk=64, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"], a["o"],
+                             a["sT"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"],
+                             a["cu_dev"], a["cu_host"], a["num_seqs"], a["scale"], a["chunk"],
+                             a["ws"], a["ws_bytes"], a["stream"])
+
+
+def step_call(lib, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), state=fake(5),
+             o=fake(6), N=8, H=4, dk=128, dv=128, dt=1, scale=0.0, stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_step(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["state"],
+                                  a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dt"], a["scale"],
+                                  a["stream"])
+
+
+def host_cu(vals):
+    return (ctypes.c_int * len(vals))(*vals)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(T=-3), INVALID),
+    (dict(H=-1), INVALID),
+    (dict(dk=96), NOT_SUPPORTED),
+    (dict(dv=256), NOT_SUPPORTED),
+    (dict(chunk=128), NOT_SUPPORTED),
+    (dict(q=None), INVALID),
+    (dict(alpha=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(k=fake(1, 4)), MISALIGNED),
+    (dict(alpha=fake(3, 4)), MISALIGNED),
+    (dict(v=fake(2, 1)), MISALIGNED),
+    (dict(beta=fake(4, 2)), MISALIGNED),
+    (dict(sT=fake(7, 2)), MISALIGNED),
+    (dict(o=fake(0, 64)), INVALID),          # output inside q
+    (dict(sT=fake(3, 256)), INVALID),        # final state inside alpha
+    (dict(sT=fake(6, 512)), INVALID),        # final state inside o
+    (dict(sT=fake(5, 256)), INVALID),        # partial overlap with the initial state
+    (dict(cu_dev=fake(8)), INVALID),         # cu_seqlens without num_seqs
+])
+def test_chunk_rejects_before_any_hip_call(lib, kw, code):
+    assert chunk_call(lib, **kw) == code
+
+
+def test_chunk_varlen_validation(lib):
+    cu = host_cu([0, 10, 10, 40])
+    good = dict(B=1, T=40, num_seqs=3, cu_dev=fake(8), cu_host=cu, ws=fake(9), ws_bytes=256)
+    ws = lib.kda_chunk_fwd_workspace_size(1, 40, 4, 128, 128, 3, 1)
+    assert ws == 256
+    assert chunk_call(lib, **dict(good, ws=None, ws_bytes=0)) == WORKSPACE
+    assert chunk_call(lib, **dict(good, ws_bytes=128)) == WORKSPACE
+    assert chunk_call(lib, **dict(good, B=2)) == INVALID
+    assert chunk_call(lib, **dict(good, T=41)) == INVALID
+    assert chunk_call(lib, **dict(good, cu_host=host_cu([0, 10, 5, 40]))) == INVALID
+    assert chunk_call(lib, **dict(good, cu_host=host_cu([1, 10, 10, 40]))) == INVALID
+    assert chunk_call(lib, **dict(good, cu_host=None)) == INVALID
+    assert chunk_call(lib, **dict(good, cu_dev=None)) == INVALID
+    assert chunk_call(lib, **dict(good, cu_dev=fake(8, 2))) == MISALIGNED
+    assert chunk_call(lib, **dict(good, ws=fake(0, 256))) == INVALID  # workspace inside q
+    assert chunk_call(lib, **dict(good, ws=fake(9, 2))) == MISALIGNED
+
+
+def test_workspace_size(lib):
+    assert lib.kda_chunk_fwd_workspace_size(2, 100, 4, 128, 128, 0, 1) == 0
+    assert lib.kda_chunk_fwd_workspace_size(1, 100, 4, 128, 128, 64, 1) == 256
+    assert lib.kda_chunk_fwd_workspace_size(1, 100, 4, 128, 128, 65, 1) == 512
+    assert lib.kda_chunk_fwd_workspace_size(1, 100, 4, 96, 128, 65, 1) == 0
+
+
+def test_chunk_empty_is_a_noop(lib):
+    # no units: returns before any HIP call
+    assert chunk_call(lib, B=0) == SUCCESS
+    assert chunk_call(lib, H=0) == SUCCESS
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), INVALID),
+    (dict(N=-1), INVALID),
+    (dict(dk=32), NOT_SUPPORTED),
+    (dict(dv=100), NOT_SUPPORTED),
+    (dict(state=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(q=fake(0, 1)), MISALIGNED),
+    (dict(alpha=fake(3, 2)), MISALIGNED),
+    (dict(state=fake(5, 8)), MISALIGNED),
+    (dict(o=fake(5, 1024)), INVALID),        # output inside the state
+    (dict(state=fake(3, 0)), INVALID),       # state aliasing alpha
+])
+def test_step_rejects_before_any_hip_call(lib, kw, code):
+    assert step_call(lib, **kw) == code
+
+
+def test_step_empty_is_a_noop(lib):
+    assert step_call(lib, N=0) == SUCCESS
+
+
+def test_python_binding_checks_arguments():
+    import torch
+    import gated_delta_rule_38_amd as kda
+    q = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(TypeError):
+        kda.kda_chunk_fwd(q.to(torch.float16), q, q, q, q[..., 0])
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(q, q[:, :2], q, q, q[..., 0])
