@@ -1,0 +1,203 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one kda_chunk_fwd call over the headline workload (bf16, B=4,
+H=16, T=4096, dk=dv=128, chunk 64, nonzero initial state), inputs already
+resident in HBM.  value = tokens per second (B*T tokens per step).  The same
+line also carries the decode workload (256 sequences x 32 heads, d=128, fp32
+state in place, 100 consecutive steps) as GB/s against the HBM roofline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--calib-copy] [--skip-decode]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "chunk_fwd_kernel": os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc", "chunk_fwd.hip"),
+    "recurrent_step_kernel": os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc",
+                                          "recurrent_step.hip"),
+}
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when absent or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def chunk_bytes(B, T, H, dk, dv, es=2, nstates=None):
+    """Algorithmic HBM bytes of one chunk-wise forward: every input read once,
+    every output written once."""
+    ns = B if nstates is None else nstates
+    tok = B * T * H
+    return (tok * (2 * dk * es + dv * es + dk * 4 + 4 + dv * es)  # q, k, v, alpha, beta, o
+            + 2 * ns * H * dk * dv * 4)                            # initial + final state
+
+
+def decode_bytes(N, H, dk, dv, es=2):
+    """Algorithmic HBM bytes of one decode step."""
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + dk * 4 + 4 + dv * es)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the workload shards by (batch, head) with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_38_amd as kda
+    from workloads import CONFIGS, gen
+
+    dev = torch.device("cuda:0")
+    kda.load_library()
+    cfg = CONFIGS[1]
+    d = gen.chunk_inputs(cfg, device=dev)
+    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
+                          o=o, final_state=fs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)  # the launch stream of kda_chunk_fwd
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens = B * T
+    value = tokens * args.steps / (ms * args.steps / 1e3)
+    alg = chunk_bytes(B, T, H, dk, dv)
+    achieved = alg / (ms / 1e3) / 1e9
+    traffic = measured_traffic("chunk_fwd_kernel")
+
+    out = {
+        "metric": "KDA chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_chunk_fwd bf16 B4 H16 T4096 dk128 dv128 chunk64, "
+                               "initial state N(0,0.02)",
+                   "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": 64,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_ms": ms},
+        "timed_wall_s": wall,
+    }
+
+    if not args.skip_decode:
+        dc = CONFIGS[3]
+        dd = gen.decode_inputs(dc, device=dev)
+        state = dd["state"].clone()
+        od = torch.empty((dc.B, dc.H, dc.dv), dtype=torch.bfloat16, device=dev)
+        sargs = [[dd[n][t] for n in ("q", "k", "v", "alpha", "beta")] for t in range(dc.steps)]
+        warm = state.clone()
+        for t in range(3):
+            kda.kda_recurrent_step(*sargs[t], warm, o=od)
+        torch.cuda.synchronize()
+        del warm
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for t in range(dc.steps):
+            kda.kda_recurrent_step(*sargs[t], state, o=od)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        us = f0.elapsed_time(f1) * 1e3 / dc.steps
+        dbytes = decode_bytes(dc.B, dc.H, dc.dk, dc.dv)
+        gbs = dbytes / (us / 1e6) / 1e9
+        out["decode"] = {
+            "workload": "kda_recurrent_step bf16 N256 H32 dk128 dv128, fp32 state in place, "
+                        "100 consecutive steps",
+            "us_per_step": us, "tokens_per_s": dc.B / (us / 1e6),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("recurrent_step_kernel"),
+                         "kernel": "recurrent_step_kernel",
+                         "algorithmic_bytes_per_launch": dbytes},
+        }
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = src.numel() * 4
+
+    if not args.no_cpu_baseline:
+        import oracle
+        # one unit per (batch, head): [B*H, T, d] blocks of the stored inputs
+        def units(x):
+            x = x.cpu()
+            return x.transpose(1, 2).reshape((B * H, T) + tuple(x.shape[3:])).contiguous()
+        host = {n: units(d[n]) for n in ("q", "k", "v", "alpha", "beta")}
+        s0 = d["initial_state"].cpu().reshape(B * H, dk, dv)
+        cores = min(len(os.sched_getaffinity(0)), B * H)
+        c0 = time.perf_counter()
+        oracle.forward_units(host["q"], host["k"], host["v"], host["alpha"], host["beta"], s0,
+                             threads=cores)
+        cw = time.perf_counter() - c0
+        out["cpu_baseline"] = {"value": tokens / cw, "unit": "tokens/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": "the whole B4 H16 T4096 workload (64 (batch, head) "
+                                         "units x 4096 tokens), fp64 token loop incl. input "
+                                         "widening; wall %.2f s" % cw}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

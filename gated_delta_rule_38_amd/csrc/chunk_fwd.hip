@@ -86,28 +86,67 @@ struct ChunkLayout {
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Raw loads of one chunk row slice for phase 0: CPT = DK/64 channels per lane.
+// CPT = DK/64 consecutive channels of one token row, kept in registers in
+// their stored form between the prefetch and the use one chunk later, so the
+// loads stay in flight across the intervening work.
 template <typename Tin, int CPT>
-struct RowVec;
-template <> struct RowVec<bf16_t, 1> {
-    static __device__ __forceinline__ void ld(const bf16_t* p, float* x) { x[0] = to_f32(*p); }
+struct RawRow;
+template <> struct RawRow<bf16_t, 1> {
+    typedef uint16_t T;
+    static __device__ __forceinline__ T ld(const bf16_t* p) {
+        return *reinterpret_cast<const uint16_t*>(p);
+    }
+    static __device__ __forceinline__ void unpack(T w, float* x) {
+        x[0] = __uint_as_float(uint32_t(w) << 16);
+    }
 };
-template <> struct RowVec<bf16_t, 2> {
-    static __device__ __forceinline__ void ld(const bf16_t* p, float* x) {
-        uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+template <> struct RawRow<bf16_t, 2> {
+    typedef uint32_t T;
+    static __device__ __forceinline__ T ld(const bf16_t* p) {
+        return *reinterpret_cast<const uint32_t*>(p);
+    }
+    static __device__ __forceinline__ void unpack(T w, float* x) {
         x[0] = __uint_as_float(w << 16);
         x[1] = __uint_as_float(w & 0xffff0000u);
     }
 };
-template <> struct RowVec<float, 1> {
-    static __device__ __forceinline__ void ld(const float* p, float* x) { x[0] = *p; }
+template <> struct RawRow<float, 1> {
+    typedef float T;
+    static __device__ __forceinline__ T ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void unpack(T w, float* x) { x[0] = w; }
 };
-template <> struct RowVec<float, 2> {
-    static __device__ __forceinline__ void ld(const float* p, float* x) {
-        float2 w = *reinterpret_cast<const float2*>(p);
-        x[0] = w.x; x[1] = w.y;
+template <> struct RawRow<float, 2> {
+    typedef float2 T;
+    static __device__ __forceinline__ T ld(const float* p) {
+        return *reinterpret_cast<const float2*>(p);
     }
+    static __device__ __forceinline__ void unpack(T w, float* x) { x[0] = w.x; x[1] = w.y; }
 };
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Store N consecutive operand elements to LDS with the widest aligned writes.
+template <typename Top, int N>
+__device__ __forceinline__ void store_run(Top* p, const Top* v) {
+    if constexpr (sizeof(Top) * N >= 16) {
+#pragma unroll
+        for (int i = 0; i < N * (int)sizeof(Top) / 16; ++i) {
+            uint4 u;
+            __builtin_memcpy(&u, v + i * (16 / sizeof(Top)), 16);
+            reinterpret_cast<uint4*>(p)[i] = u;
+        }
+    } else if constexpr (sizeof(Top) * N == 8) {
+        uint2 u;
+        __builtin_memcpy(&u, v, 8);
+        *reinterpret_cast<uint2*>(p) = u;
+    } else if constexpr (sizeof(Top) * N == 4) {
+        uint32_t u;
+        __builtin_memcpy(&u, v, 4);
+        *reinterpret_cast<uint32_t*>(p) = u;
+    } else {
+        *p = v[0];
+    }
+}
 
 // A k32 fragment gathered with a stride (8 scalar LDS reads), used where the
 // row-contiguous copy of an operand is not kept.
@@ -192,7 +231,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
     Tin* __restrict__ go = static_cast<Tin*>(p.o);
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;     // wavefront
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront (uniform)
     const int l = tid & 63;     // lane
     const int ln = l & 15;      // C-layout column / fragment row
     const int lg = l >> 4;      // lane group
@@ -221,57 +260,60 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
     }
 
     // ---- prefetch registers for phase 0 (row block w, channels l*CPT..) ----
-    float rq[16][CPT], rk[16][CPT], ra[16][CPT];
-    float rbeta = 0.f;
-    float rv[NJT][4];
+    // Rows past the end of the sequence load the last valid row (always in
+    // bounds) and are replaced by the padding values when unpacked.
+    using RQ = RawRow<Tin, CPT>;
+    using RA = RawRow<float, CPT>;
+    typename RQ::T pq[16], pk[16];
+    typename RA::T pa[16];
+    float pbeta = 0.f;
+    Tin pv[NJT][4];
     const int c0 = l * CPT;
     auto load_qka = [&](int ch) {
         const int base_r = ch * CH + w * 16;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int t = base_r + r;
-            if (t < len) {
-                const size_t off = ((size_t)(t0 + t) * H + h) * DK + c0;
-                RowVec<Tin, CPT>::ld(gq + off, rq[r]);
-                RowVec<Tin, CPT>::ld(gk + off, rk[r]);
-                RowVec<float, CPT>::ld(ga + off, ra[r]);
-            } else {
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) { rq[r][c] = 0.f; rk[r][c] = 0.f; ra[r][c] = 1.f; }
-            }
+            const int t = min(base_r + r, len - 1);
+            const size_t off = ((size_t)(t0 + t) * H + h) * DK + c0;
+            pq[r] = RQ::ld(gq + off);
+            pk[r] = RQ::ld(gk + off);
+            pa[r] = RA::ld(ga + off);
         }
-        if (w == 0) {
-            const int t = ch * CH + l;
-            rbeta = (t < len) ? gb[(size_t)(t0 + t) * H + h] : 0.f;
-        }
+        if (w == 0) pbeta = gb[(size_t)(t0 + min(ch * CH + l, len - 1)) * H + h];
     };
     auto load_v = [&](int ch) {
 #pragma unroll
         for (int jb = 0; jb < NJT; ++jb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = ch * CH + w * 16 + lg * 4 + e;
-                rv[jb][e] = (t < len)
-                    ? to_f32(gv[((size_t)(t0 + t) * H + h) * DV + col0 + jb * 16 + ln]) : 0.f;
+                const int t = min(ch * CH + w * 16 + lg * 4 + e, len - 1);
+                pv[jb][e] = gv[((size_t)(t0 + t) * H + h) * DV + col0 + jb * 16 + ln];
             }
     };
 
     const int nch = (len + CH - 1) / CH;
     if (nch > 0) { load_qka(0); load_v(0); }
 
-    float pm_s[STW][4], pn_s[STW][4];  // per owned state tile: Pm, Pn of its 4 rows
+    float pn_s[STW][4], pnm_s[STW][4];  // per owned state tile: Pn and Pn/Pm of its 4 rows
 
     for (int ch = 0; ch < nch; ++ch) {
         // ================= phase 0a: running products inside row block w ======
         float pr[16][CPT];
+        const int nvalid = len - (ch * CH + w * 16);  // valid rows of this row block
         {
             float run[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) run[c] = 1.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < 16; ++r) {
+                float a[CPT];
+                RA::unpack(pa[r], a);
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) { run[c] *= ra[r][c]; pr[r][c] = run[c]; }
+                for (int c = 0; c < CPT; ++c) {
+                    run[c] *= (r < nvalid) ? a[c] : 1.f;
+                    pr[r][c] = run[c];
+                }
+            }
 #pragma unroll
             for (int c = 0; c < CPT; ++c) sTot[w * DK + c0 + c] = run[c];
         }
@@ -285,28 +327,33 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
                 const float t0v = sTot[0 * DK + c0 + c], t1v = sTot[1 * DK + c0 + c];
                 const float t2v = sTot[2 * DK + c0 + c];
                 pre[c] = (w == 0) ? 1.f : (w == 1) ? t0v : (w == 2) ? t0v * t1v : t0v * t1v * t2v;
-                ipm[c] = 1.f / (t0v * t1v);  // 1 / P_31
+                ipm[c] = fast_rcp(t0v * t1v);  // 1 / P_31
             }
+            Top kct[CPT][16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = w * 16 + r;
+                float kx[CPT], qx[CPT];
+                RQ::unpack(pk[r], kx);
+                RQ::unpack(pq[r], qx);
                 Top kr[CPT], qr[CPT], kc[CPT];
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
+                    const float kv = (r < nvalid) ? kx[c] : 0.f;
+                    const float qv = (r < nvalid) ? qx[c] : 0.f;
                     const float ratio = pre[c] * pr[r][c] * ipm[c];  // P_row / P_31
-                    kr[c] = from_f32<Top>(rk[r][c] * ratio);
-                    qr[c] = from_f32<Top>(rq[r][c] * ratio);
-                    kc[c] = from_f32<Top>(rk[r][c] / ratio);
+                    kr[c] = from_f32<Top>(kv * ratio);
+                    qr[c] = from_f32<Top>(qv * ratio);
+                    kc[c] = from_f32<Top>(kv * fast_rcp(ratio));
+                    kct[c][r] = kc[c];
                 }
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) {
-                    sKr[row * LDK + c0 + c] = kr[c];
-                    sQr[row * LDK + c0 + c] = qr[c];
-                    if (!L::KCT_ONLY) sKc[row * LDK + c0 + c] = kc[c];
-                    sKcT[(c0 + c) * LDC + row] = kc[c];
-                }
+                store_run<Top, CPT>(sKr + row * LDK + c0, kr);
+                store_run<Top, CPT>(sQr + row * LDK + c0, qr);
+                if (!L::KCT_ONLY) store_run<Top, CPT>(sKc + row * LDK + c0, kc);
             }
-            if (w == 0) sBeta[l] = rbeta;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) store_run<Top, 16>(sKcT + (c0 + c) * LDC + w * 16, kct[c]);
+            if (w == 0) sBeta[l] = (ch * CH + l < len) ? pbeta : 0.f;
             // state operand SP = (Pm * S0)^T and the per-row decays kept for phase 4
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
@@ -319,9 +366,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
                         const int c = ct * 16 + lg * 4 + e;
                         const float a0 = sTot[c], a1 = sTot[DK + c];
                         const float a2 = sTot[2 * DK + c], a3 = sTot[3 * DK + c];
-                        pm_s[i][e] = a0 * a1;
-                        pn_s[i][e] = a0 * a1 * a2 * a3;
-                        sp[e] = pm_s[i][e] * S[i][e];
+                        const float pm = a0 * a1;
+                        pn_s[i][e] = pm * a2 * a3;
+                        pnm_s[i][e] = a2 * a3;  // Pn / Pm
+                        sp[e] = pm * S[i][e];
                     }
                     M::st4(sSP + (jj * 16 + ln) * LDK + ct * 16 + lg * 4, sp);
                 }
@@ -386,7 +434,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
                 }
                 f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = rv[jb][e] - cx[e];
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = ch * CH + w * 16 + lg * 4 + e < len;
+                    x[e] = (ok ? to_f32(pv[jb][e]) : 0.f) - cx[e];
+                }
                 M::st4(sX + (jb * 16 + ln) * LDC + w * 16 + lg * 4, x);
                 oi[jb] = co;  // stays in registers until phase 4
             }
@@ -399,12 +450,24 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
             // diagonal blocks: lane (block a = lg, column j = ln) solves L_aa x = e_j
             float x[16];
             const float* La = sLd + lg * 16 * L::LDL;
+            float4 lrow[16][4];  // strictly lower part of the lane's block, issued at once
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == ln) ? 1.f : 0.f;
+            for (int r = 1; r < 16; ++r)
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc -= La[r * L::LDL + i] * x[i];
-                x[r] = acc;
+                for (int q4 = 0; q4 < 4; ++q4)
+                    if (q4 * 4 < r) lrow[r][q4] = *reinterpret_cast<const float4*>(La + r * L::LDL + q4 * 4);
+            // right-looking: once x[i] is final, remove it from every later row;
+            // the updates of one step are independent of each other
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                for (int r = i + 1; r < 16; ++r) {
+                    const float4 v4 = lrow[r][i / 4];
+                    const float lv = (i % 4 == 0) ? v4.x : (i % 4 == 1) ? v4.y : (i % 4 == 2) ? v4.z : v4.w;
+                    x[r] -= lv * x[i];
+                }
             }
             Top* Dr = sDr + (size_t)w * 4 * 16 * LDD;  // row-major copy, this wave only
             Top* Dc = sDc + (size_t)w * 4 * 16 * LDD;  // column-major copy
@@ -518,7 +581,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        S[i][e] = pn_s[i][e] * S[i][e] + (pn_s[i][e] / pm_s[i][e]) * acc[e];
+                        S[i][e] = pn_s[i][e] * S[i][e] + pnm_s[i][e] * acc[e];
                 }
             }
         }
