@@ -1,0 +1,88 @@
+// chunk_common.h -- pieces shared by the chunk-wise forward kernels: kernel
+// parameters, the XCD-aware work-item mapping and small LDS helpers.
+#pragma once
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+#include <type_traits>
+
+namespace kda {
+
+constexpr int CH = 64;  // chunk length
+
+struct KParams {
+    const void *q, *k, *v;
+    const float *alpha, *beta, *s0;
+    void *o;
+    float *sT;
+    const int *cu_seqlens;
+    const int *order;
+    int B, T, H, dv, units, njt_all;
+    float scale;
+};
+
+struct WorkItem {
+    bool valid;
+    int h, seq, jt, len;
+    long t0;
+};
+
+// Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
+// Block b serves unit rank 8*(slot / njt) + b%8 and value tile slot % njt with
+// slot = b / 8, so the value tiles of one unit share an XCD (and its L2) and
+// are dispatched next to each other.  Unit rank r is head r % H of the
+// (r / H)-th sequence in the order given by p.order (identity if NULL).
+__device__ __forceinline__ WorkItem decode_work(const KParams& p) {
+    WorkItem wi;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    const int slot = bid >> 3;
+    wi.jt = slot % p.njt_all;
+    const int urank = (slot / p.njt_all) * 8 + xcd;
+    wi.valid = urank < p.units;
+    if (!wi.valid) return wi;
+    wi.h = urank % p.H;
+    const int srank = urank / p.H;
+    wi.seq = p.order ? p.order[srank] : srank;
+    if (p.cu_seqlens) {
+        wi.t0 = p.cu_seqlens[wi.seq];
+        wi.len = p.cu_seqlens[wi.seq + 1] - (int)wi.t0;
+    } else {
+        wi.t0 = (long)wi.seq * p.T;
+        wi.len = p.T;
+    }
+    return wi;
+}
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Store N consecutive operand elements to LDS with the widest aligned writes.
+template <typename Top, int N>
+__device__ __forceinline__ void store_run(Top* p, const Top* v) {
+    if constexpr (sizeof(Top) * N >= 16) {
+#pragma unroll
+        for (int i = 0; i < N * (int)sizeof(Top) / 16; ++i) {
+            uint4 u;
+            __builtin_memcpy(&u, v + i * (16 / sizeof(Top)), 16);
+            reinterpret_cast<uint4*>(p)[i] = u;
+        }
+    } else if constexpr (sizeof(Top) * N == 8) {
+        uint2 u;
+        __builtin_memcpy(&u, v, 8);
+        *reinterpret_cast<uint2*>(p) = u;
+    } else if constexpr (sizeof(Top) * N == 4) {
+        uint32_t u;
+        __builtin_memcpy(&u, v, 4);
+        *reinterpret_cast<uint32_t*>(p) = u;
+    } else {
+        *p = v[0];
+    }
+}
+
+
+// the pipelined bf16 chunk kernel (chunk_fwd_bf16.hip)
+hipError_t launch_chunk_bf16(const KParams& p, int dk, int dvt, hipStream_t stream);
+bool chunk_bf16_supports(int dvt);
+
+}  // namespace kda

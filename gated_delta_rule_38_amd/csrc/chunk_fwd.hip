@@ -37,12 +37,10 @@
 // columns (decays, Gram matrices, T) is recomputed by every column tile of a
 // unit; tiles of one unit are placed on the same XCD so their shared q, k,
 // alpha reads hit the same L2.
-#include "kda_device.h"
-#include "kda_launch.h"
+#include "chunk_common.h"
 
 namespace kda {
 
-constexpr int CH = 64;  // chunk length
 constexpr int NTH = 256;
 
 template <typename Top, int DK, int DVT>
@@ -123,30 +121,6 @@ template <> struct RawRow<float, 2> {
     static __device__ __forceinline__ void unpack(T w, float* x) { x[0] = w.x; x[1] = w.y; }
 };
 
-__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-
-// Store N consecutive operand elements to LDS with the widest aligned writes.
-template <typename Top, int N>
-__device__ __forceinline__ void store_run(Top* p, const Top* v) {
-    if constexpr (sizeof(Top) * N >= 16) {
-#pragma unroll
-        for (int i = 0; i < N * (int)sizeof(Top) / 16; ++i) {
-            uint4 u;
-            __builtin_memcpy(&u, v + i * (16 / sizeof(Top)), 16);
-            reinterpret_cast<uint4*>(p)[i] = u;
-        }
-    } else if constexpr (sizeof(Top) * N == 8) {
-        uint2 u;
-        __builtin_memcpy(&u, v, 8);
-        *reinterpret_cast<uint2*>(p) = u;
-    } else if constexpr (sizeof(Top) * N == 4) {
-        uint32_t u;
-        __builtin_memcpy(&u, v, 4);
-        *reinterpret_cast<uint32_t*>(p) = u;
-    } else {
-        *p = v[0];
-    }
-}
 
 // A k32 fragment gathered with a stride (8 scalar LDS reads), used where the
 // row-contiguous copy of an operand is not kept.
@@ -165,16 +139,6 @@ __device__ __forceinline__ Mma<bf16_t>::F32 gather32<bf16_t>(const bf16_t* p, in
     return f;
 }
 
-struct KParams {
-    const void *q, *k, *v;
-    const float *alpha, *beta, *s0;
-    void *o;
-    float *sT;
-    const int *cu_seqlens;
-    const int *order;
-    int B, T, H, dv, units, njt_all;
-    float scale;
-};
 
 template <typename Tin, int DK, int DVT>
 __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
@@ -202,26 +166,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
     float* sTot = reinterpret_cast<float*>(smem + L::oTot);
     float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
 
-    // ---- work item: XCD-aware (blocks are dealt round-robin to 8 XCDs) ----
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int slot = bid >> 3;
-    const int jt = slot % p.njt_all;
-    const int urank = (slot / p.njt_all) * 8 + xcd;
-    if (urank >= p.units) return;
-    const int H = p.H;
-    const int h = urank % H;
-    const int srank = urank / H;
-    const int seq = p.order ? p.order[srank] : srank;
-    long t0;
-    int len;
-    if (p.cu_seqlens) {
-        t0 = p.cu_seqlens[seq];
-        len = p.cu_seqlens[seq + 1] - (int)t0;
-    } else {
-        t0 = (long)seq * p.T;
-        len = p.T;
-    }
+    const WorkItem wi = decode_work(p);
+    if (!wi.valid) return;
+    const int H = p.H, h = wi.h, seq = wi.seq, jt = wi.jt, len = wi.len;
+    const long t0 = wi.t0;
     const int DV = p.dv;
     const Tin* __restrict__ gq = static_cast<const Tin*>(p.q);
     const Tin* __restrict__ gk = static_cast<const Tin*>(p.k);
@@ -657,9 +605,9 @@ static hipError_t launch_chunk_dk(const ChunkArgs& a, int dvt, const int* order,
 }
 
 int plan_chunk_dvt(int units, int dv, bool bf16) {
-    (void)bf16;
-    // widest value tile that still gives every compute unit a workgroup
-    for (int dvt = 64; dvt >= 16; dvt /= 2)
+    // widest value tile that still gives every compute unit a workgroup; the
+    // pipelined bf16 kernel holds at most 32 columns per workgroup
+    for (int dvt = bf16 ? 32 : 64; dvt >= 16; dvt /= 2)
         if (dvt <= dv && (long)units * (dv / dvt) >= 256) return dvt;
     return 16;
 }
@@ -679,6 +627,16 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
     }
     int dvt = a.dvt > 0 ? a.dvt : plan_chunk_dvt(units, a.dv, a.bf16);
     if (dvt > a.dv) dvt = a.dv;
+    if (a.bf16 && !a.generic && chunk_bf16_supports(dvt)) {
+        KParams p;
+        p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.beta = a.beta; p.s0 = a.s0;
+        p.o = a.o; p.sT = a.sT; p.cu_seqlens = a.cu_seqlens; p.order = order;
+        p.B = a.B; p.T = a.T; p.H = a.H; p.dv = a.dv;
+        p.units = units;
+        p.njt_all = a.dv / dvt;
+        p.scale = a.scale;
+        return launch_chunk_bf16(p, a.dk, dvt, stream);
+    }
     if (a.bf16)
         return a.dk == 128 ? launch_chunk_dk<bf16_t, 128>(a, dvt, order, stream)
                            : launch_chunk_dk<bf16_t, 64>(a, dvt, order, stream);

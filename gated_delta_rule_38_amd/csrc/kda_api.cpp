@@ -53,6 +53,11 @@ float default_scale(float scale, int dk) {
     return 1.0f / sqrtf((float)dk);
 }
 
+bool env_generic() {
+    const char* s = getenv("KDA_CHUNK_GENERIC");
+    return s && s[0] == '1';
+}
+
 int env_dvt() {
     const char* s = getenv("KDA_CHUNK_DVT");
     if (!s) return 0;
@@ -170,6 +175,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
         a.order = (varlen && num_seqs <= 65536) ? static_cast<int*>(workspace) : nullptr;
         a.scale = default_scale(scale, dk);
         a.dvt = env_dvt();
+        a.generic = env_generic();
         return kda::launch_chunk_fwd(a, stream) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
     } catch (...) {
         return KDA_ERROR_HIP;

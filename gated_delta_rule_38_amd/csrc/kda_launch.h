@@ -33,6 +33,7 @@ struct ChunkArgs {
     int *order;             // device workspace for the longest-first order (varlen), or NULL
     float scale;
     int dvt;                // value columns per workgroup (0 = choose)
+    bool generic;           // bf16 through the generic kernel (A/B checks)
 };
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);

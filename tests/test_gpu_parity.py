@@ -53,20 +53,26 @@ def ref(d, heads=None):
 
 
 class dvt_env:
-    """Force the value-column tile width of the chunk kernel."""
-    def __init__(self, dvt):
-        self.dvt = dvt
+    """Force the value-column tile width of the chunk kernel and, optionally,
+    route bf16 through the generic (fp32-capable) chunk kernel."""
+    def __init__(self, dvt, generic=False):
+        self.vals = {"KDA_CHUNK_DVT": str(dvt) if dvt else None,
+                     "KDA_CHUNK_GENERIC": "1" if generic else None}
 
     def __enter__(self):
-        self.old = os.environ.get("KDA_CHUNK_DVT")
-        if self.dvt:
-            os.environ["KDA_CHUNK_DVT"] = str(self.dvt)
+        self.old = {k: os.environ.get(k) for k in self.vals}
+        for k, v in self.vals.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
     def __exit__(self, *a):
-        if self.old is None:
-            os.environ.pop("KDA_CHUNK_DVT", None)
-        else:
-            os.environ["KDA_CHUNK_DVT"] = self.old
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 # ------------------------------------------------------------ chunk forward
@@ -101,6 +107,22 @@ def test_chunk_small(kda, idx):
     d = gen.draw_chunk(B, T, H, dk, dv, dt, alpha_mu=3.0, s0_std=s0, seed=100 + idx,
                        device=dev())
     with dvt_env(dvt):
+        o, s = run(kda, d)
+    torch.cuda.synchronize()
+    ro, rs = ref(d)
+    assert rel(o, ro) <= TOL[dt]
+    assert rel(s, rs) <= TOL[dt]
+
+
+@pytest.mark.parametrize("idx", [i for i, c in enumerate(CASES) if c[0] == "bf16"],
+                         ids=["-".join(str(x) for x in c) for c in CASES if c[0] == "bf16"])
+def test_chunk_small_generic_kernel(kda, idx):
+    """The bf16 cases through the generic kernel too (both paths stay green)."""
+    case = CASES[idx]
+    dt, B, T, H, dk, dv, s0, dvt = case
+    d = gen.draw_chunk(B, T, H, dk, dv, dt, alpha_mu=3.0, s0_std=s0, seed=100 + idx,
+                       device=dev())
+    with dvt_env(dvt, generic=True):
         o, s = run(kda, d)
     torch.cuda.synchronize()
     ro, rs = ref(d)
