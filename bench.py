@@ -21,16 +21,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc")
+# the sources each timed kernel is compiled from (its counters go stale when any changes)
 KERNEL_SOURCES = {
-    "chunk_fwd_kernel": os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc", "chunk_fwd.hip"),
-    "recurrent_step_kernel": os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc",
-                                          "recurrent_step.hip"),
+    "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "chunk_common.h", "kda_device.h"],
+    "recurrent_step_kernel": ["recurrent_step.hip", "kda_device.h"],
 }
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel):
@@ -41,7 +45,7 @@ def measured_traffic(kernel):
             rec = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+    if rec.get("source_sha256_16") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -111,7 +115,7 @@ def main():
     value = tokens * args.steps / (ms * args.steps / 1e3)
     alg = chunk_bytes(B, T, H, dk, dv)
     achieved = alg / (ms / 1e3) / 1e9
-    traffic = measured_traffic("chunk_fwd_kernel")
+    traffic = measured_traffic("chunk_fwd_bf16_kernel")
 
     out = {
         "metric": "KDA chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline",
@@ -132,7 +136,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunk_fwd_kernel", "algorithmic_bytes_per_launch": alg,
+                     "kernel": "chunk_fwd_bf16_kernel", "algorithmic_bytes_per_launch": alg,
                      "avg_launch_ms": ms},
         "timed_wall_s": wall,
     }
