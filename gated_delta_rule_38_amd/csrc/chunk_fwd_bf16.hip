@@ -245,16 +245,20 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         // pc0..pc0+CPL-1 and rows 4rg..4rg+3; a 16-lane row holds one channel
         // group, so the scan over row groups runs inside DPP rows.
         const int pw = w - NJT;
-        // register file carried from one chunk to the next: raw q, k, alpha
-        // rows of chunk c+2 and the Kc^T pairs of chunk c+1
-        uint32_t RQ[2 * CPL], RK[2 * CPL], RA[4 * CPL], RT[2 * CPL];
+        // registers carried across chunks: two sets of raw q, k, alpha rows
+        // (chunks of even and odd index, loaded three chunks ahead) and the
+        // Kc^T pairs of the chunk whose operands were built last
+        struct Raw { uint32_t q[2 * CPL], k[2 * CPL], a[4 * CPL]; };
+        Raw R0, R1;
+        uint32_t RT[2 * CPL];
 #pragma unroll
-        for (int i = 0; i < 2 * CPL; ++i) { RQ[i] = 0u; RK[i] = 0u; RT[i] = 0u; }
+        for (int i = 0; i < 2 * CPL; ++i) { R0.q[i] = R0.k[i] = R1.q[i] = R1.k[i] = 0u; RT[i] = 0u; }
 #pragma unroll
-        for (int i = 0; i < 4 * CPL; ++i) RA[i] = 0u;
-        auto ra_f = [&](int i) { return __uint_as_float(RA[i]); };
+        for (int i = 0; i < 4 * CPL; ++i) R0.a[i] = R1.a[i] = 0u;
 
-        auto p_load = [&](int ch) {  // raw q, k, alpha rows of chunk ch
+        // descriptors and lane offsets of the raw q, k, alpha rows of chunk ch
+        struct Src { Rsrc rq, rk, ra; uint32_t qo, ao; };
+        auto p_src = [&](int ch) {
             const int lx = (int)opaque((uint32_t)l);
             const int pc0 = pw * (DK / 4) + (lx >> 4) * CPL, pr0 = (lx & 15) * 4;
             const size_t e0 = ((size_t)(t0 + (long)ch * CH) * H + h) * DK;
@@ -263,33 +267,39 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             // issuing them anyway keeps the count of loads in flight the same
             // on every path, so the waits for them stay exact)
             const int nr = __builtin_amdgcn_readfirstlane(max(0, min(len - ch * CH, CH)));
-            const Rsrc rq = make_rsrc(gq + e0, (uint32_t)nr * rsq);
-            const Rsrc rk = make_rsrc(gk + e0, (uint32_t)nr * rsq);
-            const Rsrc ra = make_rsrc(ga + e0, (uint32_t)nr * rsa);
-            const uint32_t qo = (uint32_t)pr0 * rsq + (uint32_t)pc0 * 2;
-            const uint32_t ao = (uint32_t)pr0 * rsa + (uint32_t)pc0 * 4;
+            Src sr;
+            sr.rq = make_rsrc(gq + e0, (uint32_t)nr * rsq);
+            sr.rk = make_rsrc(gk + e0, (uint32_t)nr * rsq);
+            sr.ra = make_rsrc(ga + e0, (uint32_t)nr * rsa);
+            sr.qo = (uint32_t)pr0 * rsq + (uint32_t)pc0 * 2;
+            sr.ao = (uint32_t)pr0 * rsa + (uint32_t)pc0 * 4;
+            return sr;
+        };
+        auto ld_qk = [&](const Src& sr, Raw& R, int rr) {  // q and k of the lane's row rr
+            if constexpr (CPL == 8) {
+                const u32x4 q4 = __builtin_amdgcn_raw_buffer_load_b128(sr.rq, sr.qo + rr * rsq, 0, 0);
+                const u32x4 k4 = __builtin_amdgcn_raw_buffer_load_b128(sr.rk, sr.qo + rr * rsq, 0, 0);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                if constexpr (CPL == 8) {
-                    const u32x4 q4 = __builtin_amdgcn_raw_buffer_load_b128(rq, qo + rr * rsq, 0, 0);
-                    const u32x4 k4 = __builtin_amdgcn_raw_buffer_load_b128(rk, qo + rr * rsq, 0, 0);
-                    const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(ra, ao + rr * rsa, 0, 0);
-                    const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(ra, ao + rr * rsa + 16, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        RQ[4 * rr + i] = q4[i]; RK[4 * rr + i] = k4[i];
-                        RA[8 * rr + i] = a0[i]; RA[8 * rr + 4 + i] = a1[i];
-                    }
-                } else {
-                    const u32x2 q2 = __builtin_amdgcn_raw_buffer_load_b64(rq, qo + rr * rsq, 0, 0);
-                    const u32x2 k2 = __builtin_amdgcn_raw_buffer_load_b64(rk, qo + rr * rsq, 0, 0);
-                    const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(ra, ao + rr * rsa, 0, 0);
-                    RQ[2 * rr] = q2[0]; RQ[2 * rr + 1] = q2[1];
-                    RK[2 * rr] = k2[0]; RK[2 * rr + 1] = k2[1];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) RA[4 * rr + i] = a4[i];
-                }
+                for (int i = 0; i < 4; ++i) { R.q[4 * rr + i] = q4[i]; R.k[4 * rr + i] = k4[i]; }
+            } else {
+                const u32x2 q2 = __builtin_amdgcn_raw_buffer_load_b64(sr.rq, sr.qo + rr * rsq, 0, 0);
+                const u32x2 k2 = __builtin_amdgcn_raw_buffer_load_b64(sr.rk, sr.qo + rr * rsq, 0, 0);
+                R.q[2 * rr] = q2[0]; R.q[2 * rr + 1] = q2[1];
+                R.k[2 * rr] = k2[0]; R.k[2 * rr + 1] = k2[1];
             }
+        };
+        auto ld_a = [&](const Src& sr, Raw& R, int rr) {  // alpha of the lane's row rr
+#pragma unroll
+            for (int j = 0; j < CPL / 4; ++j) {
+                const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr.ra, sr.ao + rr * rsa + 16 * j, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) R.a[CPL * rr + 4 * j + i] = a4[i];
+            }
+        };
+        auto p_load = [&](int ch, Raw& R) {  // raw q, k, alpha rows of chunk ch
+            const Src sr = p_src(ch);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) { ld_qk(sr, R, rr); ld_a(sr, R, rr); }
         };
         auto p_write_kct = [&]() {
             const int lx = (int)opaque((uint32_t)l);
@@ -298,8 +308,15 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             for (int c = 0; c < CPL; ++c)
                 *reinterpret_cast<uint2*>(sKcT + (pc0 + c) * LDC + pr0) = make_uint2(RT[2 * c], RT[2 * c + 1]);
         };
-        // decayed operands of chunk ch into parity buffer ch & 1 (Kc^T kept in RT)
-        auto p_operands = [&](int ch) {
+        // Decayed operands of chunk ch into parity buffer ch & 1 (Kc^T kept in
+        // RT).  The raw rows of chunk chl are loaded into R as its rows of
+        // chunk ch are used up, so the loads spread over the computation.
+        auto p_operands = [&](int ch, Raw& R, int chl) {
+            const Src sr = p_src(chl);
+            uint32_t* RQ = R.q;
+            uint32_t* RK = R.k;
+            uint32_t* RA = R.a;
+            auto ra_f = [&](int i) { return __uint_as_float(RA[i]); };
             const int lx = (int)opaque((uint32_t)l);
             const int rg = lx & 15;
             const int pc0 = pw * (DK / 4) + (lx >> 4) * CPL, pr0 = rg * 4;
@@ -322,6 +339,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                 for (int rr = 1; rr < 4; ++rr) { run *= ra_f(CPL * rr + c); pr[rr][c] = run; }
                 inc[c] = run;
             }
+            ld_a(sr, R, 0);  // alpha of row 0 is used up
+            __builtin_amdgcn_sched_barrier(0);  // keep each batch of loads where it is issued
             // inclusive product over row groups 0..rg of the same channels
 #pragma unroll
             for (int c = 0; c < CPL; ++c) inc[c] = mul_row_shr1(inc[c]);
@@ -392,6 +411,9 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                     *reinterpret_cast<uint2*>(qr_b + to) = make_uint2(qr[0], qr[1]);
                     *reinterpret_cast<uint2*>(sKc + to) = make_uint2(kc[0], kc[1]);
                 }
+                ld_qk(sr, R, rr);                 // q, k of row rr are used up
+                if (rr < 3) ld_a(sr, R, rr + 1);  // and alpha of row rr + 1
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
@@ -399,22 +421,29 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         // loads return zero and it writes zero operands into the parity buffer
         // nobody reads any more; in exchange no path skips a load or a use of
         // loaded registers, which keeps the waits for loads in flight exact.
-        p_load(0);
-        p_operands(0);
-        p_load(1);
+        //   segment 1: Kc^T(c); operands of c+1 from its raw set, which
+        //              meanwhile receives the rows of c+3
+        //   segment 2: Gram blocks of c+1
+        auto step = [&](int ch, Raw& R) {
+            p_write_kct();  // Kc^T of chunk ch (its Kc came with the operands one chunk ago)
+            p_operands(ch + 1, R, ch + 3);
+            __syncthreads();
+            gram_share(ch + 1, pw);
+            __syncthreads();
+        };
+        p_load(0, R0);
+        p_load(1, R1);
+        p_operands(0, R0, 2);
         __syncthreads();
         gram_share(0, pw);
         __syncthreads();
-        for (int ch = 0; ch < nch; ++ch) {
-            // segment 1
-            p_write_kct();  // Kc^T of chunk ch (its Kc came with the operands one chunk ago)
-            p_operands(ch + 1);
-            p_load(ch + 2);
-            __syncthreads();
-            // segment 2
-            gram_share(ch + 1, pw);
-            __syncthreads();
+        // two chunks per trip so each raw set keeps fixed registers
+        int ch = 0;
+        for (; ch + 1 < nch; ch += 2) {
+            step(ch, R1);
+            step(ch + 1, R0);
         }
+        if (ch < nch) step(ch, R1);
         return;
     }
 
@@ -483,6 +512,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 #pragma unroll
             for (int r = 0; r < 16; ++r) sD[lg * BLK + r * LDB + ln] = (bf16_t)xs[r];
         };
+        __builtin_amdgcn_s_setprio(2);  // between the consumers and the producers
         h_load(0);
         h_write_beta(0);
         h_write_vt();
