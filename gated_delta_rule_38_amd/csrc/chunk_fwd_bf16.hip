@@ -78,7 +78,7 @@ __device__ __forceinline__ int tok_off(int row, int ch) {
 // the same value in every lane of this lane's 16-lane row: lane LANE's
 template <int LANE>
 __device__ __forceinline__ float row_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + LANE, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + LANE, 0xf, 0xf, false));
 }
 
 // A copy of x that the compiler cannot see through.  Values derived from it
@@ -100,10 +100,9 @@ __device__ __forceinline__ float row_shr(float x, float old) {
 // states a DPP read needs after a VALU write of its source.
 #define KDA_MUL_ROW_SHR(NAME, D)                                                              \
     __device__ __forceinline__ float NAME(float x) {                                          \
-        float r = x;                                                                          \
-        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_shr:" #D                        \
-                     " row_mask:0xf bank_mask:0xf" : "+v"(r) : "v"(x));                       \
-        return r;                                                                             \
+        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:" #D                        \
+                     " row_mask:0xf bank_mask:0xf" : "+v"(x));                                \
+        return x;                                                                             \
     }
 KDA_MUL_ROW_SHR(mul_row_shr1, 1)
 KDA_MUL_ROW_SHR(mul_row_shr2, 2)
@@ -512,7 +511,6 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 #pragma unroll
             for (int r = 0; r < 16; ++r) sD[lg * BLK + r * LDB + ln] = (bf16_t)xs[r];
         };
-        __builtin_amdgcn_s_setprio(2);  // between the consumers and the producers
         h_load(0);
         h_write_beta(0);
         h_write_vt();
@@ -535,9 +533,10 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     }
 
     // ============================================================ consumers
-    // The consumers carry the serial state chain: let the SIMD arbiter prefer
-    // them over the producer waves they share a SIMD with.
-    __builtin_amdgcn_s_setprio(3);
+    // The consumers carry the serial state chain.  In segment 2 it is the
+    // longest path, so the SIMD arbiter is told to prefer them there over the
+    // producers they share a SIMD with; in segment 1 they have slack and the
+    // producers the longest path, so there they take default priority.
     const int cj = w;                        // consumer column tile
     const int colw = jt * DVT + cj * 16;     // first value column of this wave
     const int col = colw + ln;               // this lane's value column
@@ -606,6 +605,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     for (int ch = 0; ch < nch; ++ch) {
         const int par = ch & 1;
         // ======================= segment 1 =======================
+        __builtin_amdgcn_s_setprio(0);
         {
             const int lx = (int)opaque((uint32_t)l);  // addresses recomputed per chunk
             const int ln = lx & 15, lg = lx >> 4;
@@ -639,6 +639,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         }
         __syncthreads();
         // ======================= segment 2 =======================
+        __builtin_amdgcn_s_setprio(3);
         {
             const int lx = (int)opaque((uint32_t)l);  // addresses recomputed per chunk
             const int ln = lx & 15, lg = lx >> 4;

@@ -57,10 +57,13 @@ struct Mma<bf16_t> {
         return F16{*reinterpret_cast<const bf16x4*>(p)};
     }
     static __device__ __forceinline__ F16 pack16(f32x4 c) {
-        F16 f;
-        f.v[0] = (bf16_t)c[0]; f.v[1] = (bf16_t)c[1];
-        f.v[2] = (bf16_t)c[2]; f.v[3] = (bf16_t)c[3];
-        return f;
+        // two paired conversions (v_cvt_pk_bf16_f32), not four single ones
+        bf16x2v lo, hi;
+        lo[0] = (bf16_t)c[0]; lo[1] = (bf16_t)c[1];
+        hi[0] = (bf16_t)c[2]; hi[1] = (bf16_t)c[3];
+        typedef unsigned u2v __attribute__((ext_vector_type(2)));
+        u2v w = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+        return F16{__builtin_bit_cast(bf16x4, w)};
     }
     static __device__ __forceinline__ f32x4 k32(F32 a, F32 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
