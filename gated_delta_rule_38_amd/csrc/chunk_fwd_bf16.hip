@@ -22,16 +22,15 @@
 //   producers (4 waves, dk/4 key channels each): decays and the operands
 //     Kr, Qr, Kc, Kc^T of chunk c+1, the q, k, alpha prefetch of chunk c+2,
 //     and Gram blocks of chunk c+1;
-//   helper (last wave): the inverses D_a of chunk c, beta and the V slice
-//     (loaded two chunks ahead), and Gram blocks.
+//   helper (last wave): the inverses D_a of chunk c, beta and V^T of chunk
+//     c+1 (loaded a chunk earlier), and Gram blocks.
 // Two workgroup barriers per chunk:
 //   segment 1: consumers - O of chunk c-1; X and Qr (Pm*S0) of chunk c
 //              producers - Kc^T(c); operands of chunk c+1; loads of chunk c+2
-//              helper    - beta(c+1); D_a of chunk c (from the diagonal Gram blocks)
-//   segment 2: consumers - solve, next state, Pm*S0 of chunk c+1 (O of chunk c
-//              follows in segment 1 of chunk c+1, where the consumers have slack)
+//              helper    - beta, V^T(c+1); loads of chunk c+2; D_a of chunk c
+//   segment 2: consumers - solve, next state (O of chunk c follows in
+//              segment 1 of chunk c+1, where the consumers have slack)
 //              producers, helper - Gram blocks of chunk c+1
-//              helper    - V^T(c+1); beta and V loads of chunk c+2
 // What a segment writes and another segment of the same chunk reads is
 // single-buffered; what is written one chunk ahead is double-buffered by
 // chunk parity.
@@ -79,6 +78,30 @@ __device__ __forceinline__ int tok_off(int row, int ch) {
 template <int LANE>
 __device__ __forceinline__ float row_bcast(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + LANE, 0xf, 0xf, false));
+}
+
+// Kc^T is kept with its rows (key channels) and columns (tokens) permuted
+// inside groups of 32 so that matrix-core operands can be taken straight from
+// accumulator registers.  A 16x16 accumulator tile gives lane (n, g) four
+// consecutive indices 4g..4g+3 of its tile; two tiles t, t+1 together give the
+// lane eight indices of one 32-group, which a 32-deep step consumes as the
+// lane's run 8g..8g+7.  A contraction does not depend on how its index is
+// ordered as long as both operands use one order, so:
+//  - state tile ct, lane group g, element e holds key channel
+//    32 (ct/2) + 8g + 4 (ct%2) + e; paired tiles then supply channels
+//    32s + 8g + 0..7 in natural order, matching Kr and Qr;
+//  - Kc^T row r holds the channel that the update's tile r/16 puts at row r%16;
+//  - solve blocks 2s and 2s+1 supply tokens 32s + 4g + 0..3 and
+//    32s + 16 + 4g + 0..3 as the run 8g..8g+7, so Kc^T column 32s + 8g + 4h + e
+//    holds token 32s + 16h + 4g + e.
+__device__ __forceinline__ int kct_row(int c) {  // Kc^T row of key channel c
+    return ((c >> 5) * 2 + ((c >> 2) & 1)) * 16 + ((c >> 3) & 3) * 4 + (c & 3);
+}
+__device__ __forceinline__ int kct_col(int t) {  // Kc^T column of token t
+    return (t & ~31) + ((t >> 2) & 3) * 8 + ((t >> 4) & 1) * 4 + (t & 3);
+}
+__device__ __forceinline__ int state_ch(int ct, int g, int e) {  // channel of S[ct][e] in lane group g
+    return (ct >> 1) * 32 + g * 8 + (ct & 1) * 4 + e;
 }
 
 // A copy of x that the compiler cannot see through.  Values derived from it
@@ -133,19 +156,14 @@ struct Lay6 {
     static constexpr size_t bM = bLo + (size_t)6 * BLK * 2;     // M_ab, b <= a: 10 blocks
     static constexpr size_t bVec = bM + (size_t)10 * BLK * 2;   // fp32 Pm, Pn, Pn/Pm [3][DK]
     static constexpr size_t bBeta = bVec + (size_t)3 * DK * 4;  // fp32 [64]
-    static constexpr size_t szBuf = (bBeta + CH * 4 + 15) / 16 * 16;
+    static constexpr size_t bVT = bBeta + CH * 4;               // bf16 V^T [DVT][LDV]
+    static constexpr size_t szBuf = (bVT + (size_t)DVT * LDV * 2 + 15) / 16 * 16;
     // single copies
     static constexpr size_t oKcT = 2 * szBuf;                   // [DK][LDC]
     static constexpr size_t oKc = oKcT + (size_t)DK * LDC * 2;  // [64][LDK]
     static constexpr size_t oLd = oKc + szTok;                  // fp32 [4][16 cols][LDL]
     static constexpr size_t oD = oLd + (size_t)4 * 16 * LDL * 4;  // D_a, 4 blocks row-major
-    static constexpr size_t oVT = oD + (size_t)4 * BLK * 2;     // bf16 V^T [DVT][LDV]
-    // consumer-private scratch
-    static constexpr size_t cSP = 0;                            // [16][LDK] bf16: (Pm*S0)^T
-    static constexpr size_t cU = cSP + (size_t)16 * LDK * 2;    // [16][LDC] bf16: U^T
-    static constexpr size_t szC = (cU + (size_t)16 * LDC * 2 + 15) / 16 * 16;
-    static constexpr size_t oCons = oVT + (size_t)DVT * LDV * 2;
-    static constexpr size_t bytes = oCons + NJT * szC;
+    static constexpr size_t bytes = oD + (size_t)4 * BLK * 2;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -163,7 +181,6 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     bf16_t* sKc = reinterpret_cast<bf16_t*>(smem + L::oKc);
     float* sLd = reinterpret_cast<float*>(smem + L::oLd);
     bf16_t* sD = reinterpret_cast<bf16_t*>(smem + L::oD);
-    bf16_t* sVT = reinterpret_cast<bf16_t*>(smem + L::oVT);
 
     const WorkItem wi = decode_work(p);
     if (!wi.valid) return;
@@ -188,29 +205,14 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     const float* __restrict__ gb = p.beta;
 
     // ---------------------------------------------------------- Gram blocks
-    // Block (a, b), b <= a, of chunk ch: lane holds A[16a + ln][16b + 4lg + e]
+    // Blocks (a, b), b <= a, of chunk ch: lane holds A[16a + ln][16b + 4lg + e]
     // and M likewise.  Diagonal blocks go to sLd (fp32, strictly lower part of
-    // L_aa, column-major) and M; the others to -L_ab and M.  Jobs are numbered
-    // jn = a (a + 1) / 2 + b and dealt to the producers and the helper.
-    auto gram_job = [&](int ch, int jn) {
-        const int lx = (int)opaque((uint32_t)l);
-        const int ln = lx & 15, lg = lx >> 4;
-        const int par = ch & 1;
-        const bf16_t* kr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bKr));
-        const bf16_t* qr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bQr));
-        const int a = (jn >= 6) ? 3 : (jn >= 3) ? 2 : (jn >= 1) ? 1 : 0;
-        const int b = jn - a * (a + 1) / 2;
-        f32x4 cA = zero4(), cM = zero4();
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            const auto fa = Mf::ld32(sKc + tok_off<LDK>(b * 16 + ln, s * 32 + lg * 8));
-            const auto fk = Mf::ld32(kr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
-            const auto fq = Mf::ld32(qr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
-            cA = Mf::k32(fa, fk, cA);
-            cM = Mf::k32(fa, fq, cM);
-        }
-        const float br = reinterpret_cast<const float*>(buf(par, L::bBeta))[a * 16 + ln];
+    // L_aa, column-major) and M; the others to -L_ab and M.  A worker takes
+    // one or two blocks of one block row a, so the Kr and Qr fragments of the
+    // row are read from LDS once for both.
+    auto gram_out = [&](int par, int a, int b, f32x4 cA, f32x4 cM, float br, int ln, int lg) __attribute__((always_inline)) {
         bf16_t* m_b = reinterpret_cast<bf16_t*>(buf(par, L::bM));
+        const int jn = a * (a + 1) / 2 + b;
         if (a == b) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -229,13 +231,41 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             Mf::st4(m_b + jn * BLK + ln * LDB + lg * 4, cM);
         }
     };
-    // worker k of the NP + 1 Gram workers (producers, then the helper) takes jobs k, k + NP + 1, ...
-    auto gram_share = [&](int ch, int k) {
+    auto gram_row = [&](int ch, int a, int b0, int nb) __attribute__((always_inline)) {  // blocks (a, b0 .. b0 + nb - 1)
+        const int lx = (int)opaque((uint32_t)l);
+        const int ln = lx & 15, lg = lx >> 4;
+        const int par = ch & 1;
+        const bf16_t* kr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bKr));
+        const bf16_t* qr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bQr));
+        f32x4 cA[2] = {zero4(), zero4()}, cM[2] = {zero4(), zero4()};
 #pragma unroll
-        for (int t = 0; t < (10 + NP) / (NP + 1); ++t) {
-            const int jn = k + t * (NP + 1);
-            if (jn < 10) gram_job(ch, jn);
+        for (int s = 0; s < DK / 32; ++s) {
+            const auto fk = Mf::ld32(kr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
+            const auto fq = Mf::ld32(qr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (j < nb) {
+                    const auto fa = Mf::ld32(sKc + tok_off<LDK>((b0 + j) * 16 + ln, s * 32 + lg * 8));
+                    cA[j] = Mf::k32(fa, fk, cA[j]);
+                    cM[j] = Mf::k32(fa, fq, cM[j]);
+                }
+            }
         }
+        const float br = reinterpret_cast<const float*>(buf(par, L::bBeta))[a * 16 + ln];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (j < nb) gram_out(par, a, b0 + j, cA[j], cM[j], br, ln, lg);
+    };
+    // worker k of the NP + 1 Gram workers (producers, then the helper):
+    // rows 3 (two workers), 2 and 1 take two blocks each; the last worker
+    // takes the diagonal blocks (2, 2) and (0, 0)
+    auto gram_share = [&](int ch, int k) __attribute__((always_inline)) {
+        static_assert(NP == 4, "five Gram workers");
+        if (k == 0) gram_row(ch, 3, 0, 2);
+        else if (k == 1) gram_row(ch, 3, 2, 2);
+        else if (k == 2) gram_row(ch, 2, 0, 2);
+        else if (k == 3) gram_row(ch, 1, 0, 2);
+        else { gram_row(ch, 2, 2, 1); gram_row(ch, 0, 0, 1); }
     };
 
     if (w >= NJT && w < NJT + NP) {
@@ -305,7 +335,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const int pc0 = pw * (DK / 4) + (lx >> 4) * CPL, pr0 = (lx & 15) * 4;
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                *reinterpret_cast<uint2*>(sKcT + (pc0 + c) * LDC + pr0) = make_uint2(RT[2 * c], RT[2 * c + 1]);
+                *reinterpret_cast<uint2*>(sKcT + kct_row(pc0 + c) * LDC + kct_col(pr0)) =
+                    make_uint2(RT[2 * c], RT[2 * c + 1]);
         };
         // Decayed operands of chunk ch into parity buffer ch & 1 (Kc^T kept in
         // RT).  The raw rows of chunk chl are loaded into R as its rows of
@@ -472,13 +503,13 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             reinterpret_cast<float*>(buf(ch & 1, L::bBeta))[(int)opaque((uint32_t)l)] = __uint_as_float(HB);
         };
         // V^T: for each of the lane's 8 columns, its RPV rows as one run
-        auto h_write_vt = [&]() {
+        auto h_write_vt = [&](int ch) {
             const int lx = (int)opaque((uint32_t)l);
             const int rq = lx % (64 / RPV), cg = lx / (64 / RPV);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-                bf16_t* dst = sVT + (cg * 8 + c) * L::LDV + RPV * rq;
+                bf16_t* dst = reinterpret_cast<bf16_t*>(buf(ch & 1, L::bVT)) + (cg * 8 + c) * L::LDV + RPV * rq;
                 const uint32_t w01 = __builtin_amdgcn_perm(HV[4 + c / 2], HV[c / 2], sel);  // rows 0, 1
                 if constexpr (RPV == 4) {
                     const uint32_t w23 = __builtin_amdgcn_perm(HV[12 + c / 2], HV[8 + c / 2], sel);
@@ -513,20 +544,21 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         };
         h_load(0);
         h_write_beta(0);
-        h_write_vt();
+        h_write_vt(0);
         h_load(1);
         __syncthreads();
         gram_share(0, NP);
         __syncthreads();
         for (int ch = 0; ch < nch; ++ch) {
-            // segment 1
+            // segment 1: beta and V^T of chunk ch + 1 into its parity buffer,
+            // loads of chunk ch + 2, then D of chunk ch
             h_write_beta(ch + 1);
-            h_dsolve();  // D of chunk ch
+            h_write_vt(ch + 1);
+            h_load(ch + 2);
+            h_dsolve();
             __syncthreads();
             // segment 2
             gram_share(ch + 1, NP);
-            h_write_vt();  // V^T of chunk ch + 1
-            h_load(ch + 2);
             __syncthreads();
         }
         return;
@@ -537,6 +569,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // longest path, so the SIMD arbiter is told to prefer them there over the
     // producers they share a SIMD with; in segment 1 they have slack and the
     // producers the longest path, so there they take default priority.
+    // The state, U and Pm*S stay in registers: the operand orders set out at
+    // kct_row let each product take them as they are.
     const int cj = w;                        // consumer column tile
     const int colw = jt * DVT + cj * 16;     // first value column of this wave
     const int col = colw + ln;               // this lane's value column
@@ -544,36 +578,22 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     const size_t sbase = ((size_t)wi.seq * H + h) * DK * DV;
 
     f32x4 S[NCT], Y[4], OI[4];  // state slice, beta-scaled X, Qr (Pm S0)
+    Mf::F16 UP[4];              // U of the last solved chunk, packed (B operand layout)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         S[ct] = zero4();
         if (p.s0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[ct][e] = p.s0[sbase + (size_t)(ct * 16 + lg * 4 + e) * DV + col];
+            for (int e = 0; e < 4; ++e) S[ct][e] = p.s0[sbase + (size_t)state_ch(ct, lg, e) * DV + col];
         }
     }
-    // (Pm * S)^T of chunk ch as the B operand of X and Qr (Pm*S): written by
-    // the chunk before (right after it updates S), or here for chunk 0
-    auto c_write_sp = [&](int ch) {
-        const int lx = (int)opaque((uint32_t)l);
-        const int ln = lx & 15, lg = lx >> 4;
-        bf16_t* cSP = reinterpret_cast<bf16_t*>(smem + L::oCons + cj * L::szC + L::cSP);
-        const float* vec = reinterpret_cast<const float*>(buf(ch & 1, L::bVec));
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const float4 pm = ld4(vec + ct * 16 + lg * 4);
-            f32x4 sp = {pm.x * S[ct][0], pm.y * S[ct][1], pm.z * S[ct][2], pm.w * S[ct][3]};
-            Mf::st4(cSP + ln * LDK + ct * 16 + lg * 4, sp);
-        }
-    };
-    // O_a = scale (OI_a + sum_{b<=a} M_ab U_b) of chunk ch, k-steps of 32 tokens;
-    // run in the consumers' first segment of chunk ch + 1 (M, U^T and OI of
-    // chunk ch are still in place there) or after the last chunk
+    // O_a = scale (OI_a + sum_{b<=a} M_ab U_b) of chunk ch, one 16-token block
+    // of U per step; run in the consumers' first segment of chunk ch + 1 (M and
+    // OI of chunk ch are still in place there) or after the last chunk
     auto c_out = [&](int ch) {
         const int lx = (int)opaque((uint32_t)l);
         const int ln = lx & 15, lg = lx >> 4;
         const bf16_t* m_b = reinterpret_cast<const bf16_t*>(buf(ch & 1, L::bM));
-        const bf16_t* cU = reinterpret_cast<const bf16_t*>(smem + L::oCons + cj * L::szC + L::cU);
         const Rsrc ro = make_rsrc(go + ((size_t)(t0 + (long)ch * CH) * H + h) * DV + colw,
                                   (uint32_t)min(len - ch * CH, CH) * rsv);
         const uint32_t ob = (uint32_t)ln * 2 + (uint32_t)lg * 4 * rsv;  // row 4lg, column colw + ln
@@ -581,26 +601,24 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         for (int a = 0; a < 4; ++a) {
             f32x4 co = OI[a];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 0 || a >= 2) {
-                    const int b = 2 * s + (lg >> 1);  // block of this lane's 8 k-values
-                    Mf::F32 fm;
-                    if (b <= a)
-                        fm = Mf::ld32(m_b + (a * (a + 1) / 2 + b) * BLK + ln * LDB + (lg & 1) * 8);
-                    else
-                        fm.v = bf16x8{};
-                    const auto fu = Mf::ld32(cU + ln * LDC + s * 32 + lg * 8);
-                    co = Mf::k32(fm, fu, co);
-                }
-            }
+            for (int b = 0; b <= a; ++b)
+                co = Mf::k16(Mf::ld16(m_b + (a * (a + 1) / 2 + b) * BLK + ln * LDB + lg * 4), UP[b], co);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16_t)(p.scale * co[e])),
                                                       ro, ob + (uint32_t)(a * 16 + e) * rsv, 0, 0);
         }
     };
+    // the pair of state tiles 2s, 2s+1 times Pm, as one 32-deep B operand
+    auto sp_frag = [&](const float* pm, int s) {
+        const int g = (int)opaque((uint32_t)l) >> 4;
+        const float4 m0 = ld4(pm + s * 32 + g * 8), m1 = ld4(pm + s * 32 + g * 8 + 4);
+        const f32x4 a = {m0.x * S[2 * s][0], m0.y * S[2 * s][1], m0.z * S[2 * s][2], m0.w * S[2 * s][3]};
+        const f32x4 b = {m1.x * S[2 * s + 1][0], m1.y * S[2 * s + 1][1], m1.z * S[2 * s + 1][2],
+                         m1.w * S[2 * s + 1][3]};
+        return Mf::F32{__builtin_shufflevector(Mf::pack16(a).v, Mf::pack16(b).v, 0, 1, 2, 3, 4, 5, 6, 7)};
+    };
     __syncthreads();
-    c_write_sp(0);
     __syncthreads();
     for (int ch = 0; ch < nch; ++ch) {
         const int par = ch & 1;
@@ -610,13 +628,14 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const int lx = (int)opaque((uint32_t)l);  // addresses recomputed per chunk
             const int ln = lx & 15, lg = lx >> 4;
             if (ch > 0) c_out(ch - 1);
-            const bf16_t* cSP = reinterpret_cast<const bf16_t*>(smem + L::oCons + cj * L::szC + L::cSP);
             const bf16_t* kr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bKr));
             const bf16_t* qr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bQr));
             const float* beta = reinterpret_cast<const float*>(buf(par, L::bBeta));
+            const float* vec = reinterpret_cast<const float*>(buf(par, L::bVec));
+            const bf16_t* vt_b = reinterpret_cast<const bf16_t*>(buf(par, L::bVT));
             Mf::F32 fs[DK / 32];
 #pragma unroll
-            for (int s = 0; s < DK / 32; ++s) fs[s] = Mf::ld32(cSP + ln * LDK + s * 32 + lg * 8);
+            for (int s = 0; s < DK / 32; ++s) fs[s] = sp_frag(vec, s);
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 f32x4 cx = zero4(), co = zero4();
@@ -628,7 +647,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                     co = Mf::k32(fq, fs[s], co);
                 }
                 const float4 b4 = ld4(beta + a * 16 + lg * 4);
-                const uint2 v4 = *reinterpret_cast<const uint2*>(sVT + (cj * 16 + ln) * L::LDV + a * 16 + lg * 4);
+                const uint2 v4 = *reinterpret_cast<const uint2*>(vt_b + (cj * 16 + ln) * L::LDV + a * 16 + lg * 4);
                 // beta_r (v_r - (Kr Pm S0)_r); rows past the end have v = beta = 0
                 Y[a][0] = b4.x * (lo_f(v4.x) - cx[0]);
                 Y[a][1] = b4.y * (hi_f(v4.x) - cx[1]);
@@ -643,42 +662,39 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         {
             const int lx = (int)opaque((uint32_t)l);  // addresses recomputed per chunk
             const int ln = lx & 15, lg = lx >> 4;
-            bf16_t* cU = reinterpret_cast<bf16_t*>(smem + L::oCons + cj * L::szC + L::cU);
             const bf16_t* lo_b = reinterpret_cast<const bf16_t*>(buf(par, L::bLo));
             const float* vec = reinterpret_cast<const float*>(buf(par, L::bVec));
             // U_a = D_a (Y_a - sum_{b<a} L_ab U_b); lo_b holds -L_ab
-            f32x4 U[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 f32x4 acc = Y[a];
 #pragma unroll
                 for (int b = 0; b < a; ++b) {
                     const auto fl = Mf::ld16(lo_b + (a * (a - 1) / 2 + b) * BLK + ln * LDB + lg * 4);
-                    acc = Mf::k16(fl, Mf::pack16(U[b]), acc);
+                    acc = Mf::k16(fl, UP[b], acc);
                 }
                 const auto fd = Mf::ld16(sD + a * BLK + ln * LDB + lg * 4);
-                U[a] = Mf::k16(fd, Mf::pack16(acc), zero4());
-                Mf::st4(cU + ln * LDC + a * 16 + lg * 4, U[a]);
+                UP[a] = Mf::pack16(Mf::k16(fd, Mf::pack16(acc), zero4()));
             }
-            wave_sync_lds();
-            // S <- Pn*S0 + (Pn/Pm) (Kc^T U)
+            // S <- Pn*S0 + (Pn/Pm) (Kc^T U); blocks 2s, 2s+1 of U form k-step s
+            Mf::F32 fu[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                fu[s].v = __builtin_shufflevector(UP[2 * s].v, UP[2 * s + 1].v, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const auto fk = Mf::ld32(sKcT + (ct * 16 + ln) * LDC + s * 32 + lg * 8);
-                    const auto fu = Mf::ld32(cU + ln * LDC + s * 32 + lg * 8);
-                    acc = Mf::k32(fk, fu, acc);
-                }
-                const float4 pn = ld4(vec + DK + ct * 16 + lg * 4);
-                const float4 pnm = ld4(vec + 2 * DK + ct * 16 + lg * 4);
+                for (int s = 0; s < 2; ++s)
+                    acc = Mf::k32(Mf::ld32(sKcT + (ct * 16 + ln) * LDC + s * 32 + lg * 8), fu[s], acc);
+                const int c0 = state_ch(ct, lg, 0);
+                const float4 pn = ld4(vec + DK + c0);
+                const float4 pnm = ld4(vec + 2 * DK + c0);
                 S[ct][0] = pn.x * S[ct][0] + pnm.x * acc[0];
                 S[ct][1] = pn.y * S[ct][1] + pnm.y * acc[1];
                 S[ct][2] = pn.z * S[ct][2] + pnm.z * acc[2];
                 S[ct][3] = pn.w * S[ct][3] + pnm.w * acc[3];
             }
-            c_write_sp(ch + 1);  // Pm of chunk ch + 1 came with its operands in segment 1
         }
         __syncthreads();
     }
@@ -689,7 +705,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                p.sT[sbase + (size_t)(ct * 16 + lg * 4 + e) * DV + col] = S[ct][e];
+                p.sT[sbase + (size_t)state_ch(ct, lg, e) * DV + col] = S[ct][e];
     }
 }
 
