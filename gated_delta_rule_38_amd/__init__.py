@@ -104,7 +104,7 @@ def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype=torch.bfloat16
 
 def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
                   cu_seqlens_host=None, scale=None, output_final_state=True,
-                  final_state=None, o=None, chunk_size=64):
+                  final_state=None, o=None, chunk_size=64, workspace=None):
     """Chunk-wise KDA forward.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype);
@@ -113,7 +113,9 @@ def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
     Varlen: B == 1 and cu_seqlens (int32 device tensor of N+1 offsets) with
     its host copy cu_seqlens_host (list or CPU tensor; derived with a copy if
     omitted).  final_state may be passed (e.g. initial_state itself for an
-    in-place update); o may be passed as a preallocated output.
+    in-place update); o may be passed as a preallocated output, and
+    workspace as a uint8 device tensor of at least
+    kda_chunk_fwd_workspace_size() bytes (else one is allocated per call).
     Returns (o, final_state or None).
     """
     lib = load_library()
@@ -154,7 +156,14 @@ def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
     elif final_state is not None:
         _check(final_state, "final_state", torch.float32, dev, sshape)
     ws_bytes = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, code))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < ws_bytes:
+            raise ValueError("workspace holds %d bytes, the call needs %d" % (workspace.numel(), ws_bytes))
+        ws = workspace
+        ws_bytes = workspace.numel()
+    else:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                            _ptr(initial_state), _ptr(o), _ptr(final_state),
                            B, T, H, dk, dv, code, _ptr(cu_dev), cu_host_arr, num_seqs,
