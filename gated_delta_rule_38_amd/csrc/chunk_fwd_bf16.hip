@@ -18,15 +18,15 @@
 // one role for the whole kernel:
 //   consumers (waves 0..NJT-1): one 16-column slice of the fp32 state each,
 //     in registers; they run the serial chain of chunk c (X, the solve, O,
-//     the next state) at raised issue priority;
+//     the next state), at raised issue priority where it is the longest path;
 //   producers (4 waves, dk/4 key channels each): decays and the operands
-//     Kr, Qr, Kc, Kc^T of chunk c+1, the q, k, alpha prefetch of chunk c+2,
+//     Kr, Qr, Kc, Kc^T of chunk c+1, the q, k, alpha prefetch of chunk c+3,
 //     and Gram blocks of chunk c+1;
 //   helper (last wave): the inverses D_a of chunk c, beta and V^T of chunk
 //     c+1 (loaded a chunk earlier), and Gram blocks.
 // Two workgroup barriers per chunk:
 //   segment 1: consumers - O of chunk c-1; X and Qr (Pm*S0) of chunk c
-//              producers - Kc^T(c); operands of chunk c+1; loads of chunk c+2
+//              producers - Kc^T(c); operands of chunk c+1; loads of chunk c+3
 //              helper    - beta, V^T(c+1); loads of chunk c+2; D_a of chunk c
 //   segment 2: consumers - solve, next state (O of chunk c follows in
 //              segment 1 of chunk c+1, where the consumers have slack)
