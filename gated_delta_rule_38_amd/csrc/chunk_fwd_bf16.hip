@@ -18,16 +18,19 @@
 // one role for the whole kernel:
 //   consumers (waves 0..NJT-1): one 16-column slice of the fp32 state each,
 //     in registers; they run the serial chain of chunk c (X, the solve, O,
-//     the next state), at raised issue priority where it is the longest path;
+//     the next state);
 //   producers (4 waves, dk/4 key channels each): decays and the operands
 //     Kr, Qr, Kc, Kc^T of chunk c+1, the q, k, alpha prefetch of chunk c+3,
 //     and Gram blocks of chunk c+1;
-//   helper (last wave): the inverses D_a of chunk c, beta and V^T of chunk
-//     c+1 (loaded a chunk earlier), and Gram blocks.
+//   helper (last wave): the inverses D_a and Pn of chunk c, beta and V^T of
+//     chunk c+1 (loaded a chunk earlier), and Gram blocks.
+// In each segment the waves on its longest path (producers in segment 1,
+// consumers in segment 2) take raised issue priority over the waves they
+// share a SIMD with.
 // Two workgroup barriers per chunk:
 //   segment 1: consumers - O of chunk c-1; X and Qr (Pm*S0) of chunk c
 //              producers - Kc^T(c); operands of chunk c+1; loads of chunk c+3
-//              helper    - beta, V^T(c+1); loads of chunk c+2; D_a of chunk c
+//              helper    - Pn(c); beta, V^T(c+1); loads of chunk c+2; D_a(c)
 //   segment 2: consumers - solve, next state (O of chunk c follows in
 //              segment 1 of chunk c+1, where the consumers have slack)
 //              producers, helper - Gram blocks of chunk c+1
@@ -74,12 +77,6 @@ template <int LDK>
 __device__ __forceinline__ int tok_off(int row, int ch) {
     return row * LDK + ((((ch >> 3) ^ (row >> 4)) & 3) | ((ch >> 3) & ~3)) * 8 + (ch & 7);
 }
-// the same value in every lane of this lane's 16-lane row: lane LANE's
-template <int LANE>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + LANE, 0xf, 0xf, false));
-}
-
 // Kc^T is kept with its rows (key channels) and columns (tokens) permuted
 // inside groups of 32 so that matrix-core operands can be taken straight from
 // accumulator registers.  A 16x16 accumulator tile gives lane (n, g) four
@@ -127,11 +124,30 @@ __device__ __forceinline__ float row_shr(float x, float old) {
                      " row_mask:0xf bank_mask:0xf" : "+v"(x));                                \
         return x;                                                                             \
     }
-KDA_MUL_ROW_SHR(mul_row_shr1, 1)
-KDA_MUL_ROW_SHR(mul_row_shr2, 2)
 KDA_MUL_ROW_SHR(mul_row_shr4, 4)
 KDA_MUL_ROW_SHR(mul_row_shr8, 8)
 #undef KDA_MUL_ROW_SHR
+// x * (x of lane l - D mod 16) inside this lane's 16-lane row
+#define KDA_MUL_ROW_ROR(NAME, D)                                                              \
+    __device__ __forceinline__ float NAME(float x) {                                          \
+        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_ror:" #D                        \
+                     " row_mask:0xf bank_mask:0xf" : "+v"(x));                                \
+        return x;                                                                             \
+    }
+KDA_MUL_ROW_ROR(mul_row_ror4, 4)
+KDA_MUL_ROW_ROR(mul_row_ror8, 8)
+#undef KDA_MUL_ROW_ROR
+// y in the 16-lane rows selected by ROWS (bit r = lanes 16r..16r+15), x elsewhere
+template <int ROWS>
+__device__ __forceinline__ float rows_sel(float x, float y) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(y), 0xE4, ROWS, 0xf, false));
+}
+// exchange between 16-lane rows: (a, b) -> ([a0 b0 a2 b2], [a1 b1 a3 b3]) by rows
+__device__ __forceinline__ void swap_rows16(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
 
 template <int DK, int DVT>
 struct Lay6 {
@@ -270,9 +286,12 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 
     if (w >= NJT && w < NJT + NP) {
         // ========================================================= producers
-        // Lane (cq = l/16, rg = l%16) of producer pw owns key channels
-        // pc0..pc0+CPL-1 and rows 4rg..4rg+3; a 16-lane row holds one channel
-        // group, so the scan over row groups runs inside DPP rows.
+        // Lane (cq = l%4, rg = l/4) of producer pw owns key channels
+        // pc0..pc0+CPL-1 and rows 4rg..4rg+3.  The four lanes of a quad read
+        // one token's channels of this producer, so each load instruction
+        // touches one 64-byte run per quad (one cache access, where lanes of
+        // one channel group spread over rows would cost one access per lane);
+        // 16-lane row r then holds tokens 16r..16r+15.
         const int pw = w - NJT;
         // registers carried across chunks: two sets of raw q, k, alpha rows
         // (chunks of even and odd index, loaded three chunks ahead) and the
@@ -289,7 +308,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         struct Src { Rsrc rq, rk, ra; uint32_t qo, ao; };
         auto p_src = [&](int ch) {
             const int lx = (int)opaque((uint32_t)l);
-            const int pc0 = pw * (DK / 4) + (lx >> 4) * CPL, pr0 = (lx & 15) * 4;
+            const int pc0 = pw * (DK / 4) + (lx & 3) * CPL, pr0 = (lx >> 2) * 4;
             const size_t e0 = ((size_t)(t0 + (long)ch * CH) * H + h) * DK;
             // rows of this chunk inside the sequence (0 past the last chunk: the
             // loads then fall outside the range, read nothing and return zero;
@@ -332,7 +351,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         };
         auto p_write_kct = [&]() {
             const int lx = (int)opaque((uint32_t)l);
-            const int pc0 = pw * (DK / 4) + (lx >> 4) * CPL, pr0 = (lx & 15) * 4;
+            const int pc0 = pw * (DK / 4) + (lx & 3) * CPL, pr0 = (lx >> 2) * 4;
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
                 *reinterpret_cast<uint2*>(sKcT + kct_row(pc0 + c) * LDC + kct_col(pr0)) =
@@ -348,8 +367,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             uint32_t* RA = R.a;
             auto ra_f = [&](int i) { return __uint_as_float(RA[i]); };
             const int lx = (int)opaque((uint32_t)l);
-            const int rg = lx & 15;
-            const int pc0 = pw * (DK / 4) + (lx >> 4) * CPL, pr0 = rg * 4;
+            const int rg = lx >> 2;
+            const int pc0 = pw * (DK / 4) + (lx & 3) * CPL, pr0 = rg * 4;
             const int par = ch & 1;
             const int nval = len - ch * CH;
             if (nval < CH) {  // alpha of rows past the end of the sequence is 1
@@ -371,38 +390,43 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             }
             ld_a(sr, R, 0);  // alpha of row 0 is used up
             __builtin_amdgcn_sched_barrier(0);  // keep each batch of loads where it is issued
-            // inclusive product over row groups 0..rg of the same channels
+            // Products over the chunk's tokens, per channel.  w: over the
+            // lane's 16-lane row through its last token (tokens 16r..pr0+3);
+            // z: over the whole row (tokens 16r..16r+15), in every lane.
+            float w[CPL];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_shr1(inc[c]);
+            for (int c = 0; c < CPL; ++c) w[c] = inc[c];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_shr2(inc[c]);
+            for (int c = 0; c < CPL; ++c) w[c] = mul_row_shr4(w[c]);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_shr4(inc[c]);
+            for (int c = 0; c < CPL; ++c) w[c] = mul_row_shr8(w[c]);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_shr8(inc[c]);
-            // Pm, 1/Pm and Pn from row groups 7 and 15 of the same channel group
-            float ri[CPL], pm[CPL], ipm[CPL], pn[CPL], f[CPL], g[CPL];
+            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_ror4(inc[c]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_ror8(inc[c]);
+            // With row totals z0..z3, Pm = z0 z1 and P_t / Pm = w_t F where F
+            // is 1/(z0 z1), 1/z1, 1 and z2 in rows 0..3.  After the row
+            // exchange a = (z0, z0, z2, z2) and b = (z1, z1, z3, z3) by row,
+            // so a b is Pm in rows 0, 1 and Pn / Pm in rows 2, 3.
+            float f[CPL], g[CPL], pq[CPL];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                ri[c] = fast_rcp(inc[c]);  // 1 / P through row pr0 + 3
-                pm[c] = row_bcast<7>(inc[c]);
-                ipm[c] = row_bcast<7>(ri[c]);
-                pn[c] = row_bcast<15>(inc[c]);
+                float a = inc[c], b = inc[c];
+                swap_rows16(a, b);
+                pq[c] = a * b;
+                const float u = rows_sel<0x8>(rows_sel<0x1>(b, pq[c]), a);  // z0z1, z1, z3, z2
+                const float ru = fast_rcp(u);
+                const float fr = rows_sel<0x4>(rows_sel<0x8>(ru, a), 1.f);
+                f[c] = row_shr<4>(w[c], 1.f) * fr;  // P through row pr0 - 1, over Pm
+                g[c] = fast_rcp(w[c] * fr);         // Pm / P through row pr0 + 3
             }
+            // Pm from the first lanes of row 0, Pn / Pm from the first lanes of
+            // row 2; the helper forms Pn from the two
+            if (rg == 0 || rg == 8) {
+                float* vec = reinterpret_cast<float*>(buf(par, L::bVec)) + (rg == 0 ? 0 : 2 * DK);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                f[c] = row_shr<1>(inc[c], 1.f) * ipm[c];  // P through row pr0 - 1, over Pm
-                g[c] = pm[c] * ri[c];                       // Pm / P through row pr0 + 3
-            }
-            if (rg == 0) {
-                float* vec = reinterpret_cast<float*>(buf(par, L::bVec));
-#pragma unroll
-                for (int c = 0; c < CPL; c += 4) {
-                    *reinterpret_cast<float4*>(vec + pc0 + c) = make_float4(pm[c], pm[c + 1], pm[c + 2], pm[c + 3]);
-                    *reinterpret_cast<float4*>(vec + DK + pc0 + c) = make_float4(pn[c], pn[c + 1], pn[c + 2], pn[c + 3]);
-                    *reinterpret_cast<float4*>(vec + 2 * DK + pc0 + c) =
-                        make_float4(pn[c] * ipm[c], pn[c + 1] * ipm[c + 1], pn[c + 2] * ipm[c + 2], pn[c + 3] * ipm[c + 3]);
-                }
+                for (int c = 0; c < CPL; c += 4)
+                    *reinterpret_cast<float4*>(vec + pc0 + c) = make_float4(pq[c], pq[c + 1], pq[c + 2], pq[c + 3]);
             }
             bf16_t* kr_b = reinterpret_cast<bf16_t*>(buf(par, L::bKr));
             bf16_t* qr_b = reinterpret_cast<bf16_t*>(buf(par, L::bQr));
@@ -455,9 +479,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         //              meanwhile receives the rows of c+3
         //   segment 2: Gram blocks of c+1
         auto step = [&](int ch, Raw& R) {
+            __builtin_amdgcn_s_setprio(2);
             p_write_kct();  // Kc^T of chunk ch (its Kc came with the operands one chunk ago)
             p_operands(ch + 1, R, ch + 3);
             __syncthreads();
+            __builtin_amdgcn_s_setprio(0);
             gram_share(ch + 1, pw);
             __syncthreads();
         };
@@ -479,14 +505,16 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 
     if (w == NJT + NP) {
         // ============================================================ helper
-        // beta of a chunk (lane = row) and its V slice: lane (rq = l % (64/RPV),
-        // cg = l / (64/RPV)) holds rows RPV*rq .. +RPV-1, slice columns 8cg..8cg+7
+        // beta of a chunk (lane = row) and its V slice: lane (cg = l % (DVT/8),
+        // rq = l / (DVT/8)) holds rows RPV*rq .. +RPV-1, slice columns
+        // 8cg..8cg+7 (consecutive lanes read one row's columns, so the loads
+        // coalesce)
         uint32_t HB = 0u, HV[4 * RPV];
 #pragma unroll
         for (int i = 0; i < 4 * RPV; ++i) HV[i] = 0u;
         auto h_load = [&](int ch) {  // beta and V rows of chunk ch (zero past the end)
             const int lx = (int)opaque((uint32_t)l);
-            const int rq = lx % (64 / RPV), cg = lx / (64 / RPV);
+            const int rq = lx / (DVT / 8), cg = lx % (DVT / 8);
             const int nr = __builtin_amdgcn_readfirstlane(max(0, min(len - ch * CH, CH)));
             const size_t tok = (size_t)(t0 + (long)ch * CH) * H + h;
             const Rsrc rb = make_rsrc(gb + tok, (uint32_t)nr * rsb);
@@ -499,13 +527,22 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                 HV[4 * i] = v4[0]; HV[4 * i + 1] = v4[1]; HV[4 * i + 2] = v4[2]; HV[4 * i + 3] = v4[3];
             }
         };
+        auto h_pn = [&](int ch) {  // Pn = Pm (Pn / Pm) of chunk ch, per key channel
+            float* vec = reinterpret_cast<float*>(buf(ch & 1, L::bVec));
+            const int lx = (int)opaque((uint32_t)l);
+#pragma unroll
+            for (int c = 0; c < DK / 64; ++c) {
+                const int kc = lx + 64 * c;
+                vec[DK + kc] = vec[kc] * vec[2 * DK + kc];
+            }
+        };
         auto h_write_beta = [&](int ch) {
             reinterpret_cast<float*>(buf(ch & 1, L::bBeta))[(int)opaque((uint32_t)l)] = __uint_as_float(HB);
         };
         // V^T: for each of the lane's 8 columns, its RPV rows as one run
         auto h_write_vt = [&](int ch) {
             const int lx = (int)opaque((uint32_t)l);
-            const int rq = lx % (64 / RPV), cg = lx / (64 / RPV);
+            const int rq = lx / (DVT / 8), cg = lx % (DVT / 8);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
@@ -550,8 +587,9 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         gram_share(0, NP);
         __syncthreads();
         for (int ch = 0; ch < nch; ++ch) {
-            // segment 1: beta and V^T of chunk ch + 1 into its parity buffer,
-            // loads of chunk ch + 2, then D of chunk ch
+            // segment 1: Pn of chunk ch; beta and V^T of chunk ch + 1 into its
+            // parity buffer, loads of chunk ch + 2, then D of chunk ch
+            h_pn(ch);
             h_write_beta(ch + 1);
             h_write_vt(ch + 1);
             h_load(ch + 2);
@@ -567,8 +605,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // ============================================================ consumers
     // The consumers carry the serial state chain.  In segment 2 it is the
     // longest path, so the SIMD arbiter is told to prefer them there over the
-    // producers they share a SIMD with; in segment 1 they have slack and the
-    // producers the longest path, so there they take default priority.
+    // producers they share a SIMD with; in segment 1 they have slack and take
+    // the lowest priority.
     // The state, U and Pm*S stay in registers: the operand orders set out at
     // kct_row let each product take them as they are.
     const int cj = w;                        // consumer column tile
@@ -577,7 +615,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     bf16_t* __restrict__ go = static_cast<bf16_t*>(p.o);
     const size_t sbase = ((size_t)wi.seq * H + h) * DK * DV;
 
-    f32x4 S[NCT], Y[4], OI[4];  // state slice, beta-scaled X, Qr (Pm S0)
+    f32x4 S[NCT], Y[4], OI[4];  // state slice, beta-scaled X, (Qr (Pm S0))^T
     Mf::F16 UP[4];              // U of the last solved chunk, packed (B operand layout)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -589,24 +627,24 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     }
     // O_a = scale (OI_a + sum_{b<=a} M_ab U_b) of chunk ch, one 16-token block
     // of U per step; run in the consumers' first segment of chunk ch + 1 (M and
-    // OI of chunk ch are still in place there) or after the last chunk
+    // OI of chunk ch are still in place there) or after the last chunk.  The
+    // products are taken with their operands swapped, which yields O_a^T: lane
+    // (n, g) then holds value columns 4g..4g+3 of token n, one 8-byte store.
     auto c_out = [&](int ch) {
         const int lx = (int)opaque((uint32_t)l);
         const int ln = lx & 15, lg = lx >> 4;
         const bf16_t* m_b = reinterpret_cast<const bf16_t*>(buf(ch & 1, L::bM));
         const Rsrc ro = make_rsrc(go + ((size_t)(t0 + (long)ch * CH) * H + h) * DV + colw,
                                   (uint32_t)min(len - ch * CH, CH) * rsv);
-        const uint32_t ob = (uint32_t)ln * 2 + (uint32_t)lg * 4 * rsv;  // row 4lg, column colw + ln
+        const uint32_t ob = (uint32_t)ln * rsv + (uint32_t)lg * 8;  // token ln, column colw + 4lg
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             f32x4 co = OI[a];
 #pragma unroll
             for (int b = 0; b <= a; ++b)
-                co = Mf::k16(Mf::ld16(m_b + (a * (a + 1) / 2 + b) * BLK + ln * LDB + lg * 4), UP[b], co);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16_t)(p.scale * co[e])),
-                                                      ro, ob + (uint32_t)(a * 16 + e) * rsv, 0, 0);
+                co = Mf::k16(UP[b], Mf::ld16(m_b + (a * (a + 1) / 2 + b) * BLK + ln * LDB + lg * 4), co);
+            const u32x2 ow = {pack2(p.scale * co[0], p.scale * co[1]), pack2(p.scale * co[2], p.scale * co[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(ow, ro, ob + (uint32_t)(a * 16) * rsv, 0, 0);
         }
     };
     // the pair of state tiles 2s, 2s+1 times Pm, as one 32-deep B operand
@@ -644,7 +682,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                     const auto fk = Mf::ld32(kr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
                     const auto fq = Mf::ld32(qr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
                     cx = Mf::k32(fk, fs[s], cx);
-                    co = Mf::k32(fq, fs[s], co);
+                    co = Mf::k32(fs[s], fq, co);  // transposed, as c_out takes it
                 }
                 const float4 b4 = ld4(beta + a * 16 + lg * 4);
                 const uint2 v4 = *reinterpret_cast<const uint2*>(vt_b + (cj * 16 + ln) * L::LDV + a * 16 + lg * 4);
