@@ -114,39 +114,114 @@ __device__ __forceinline__ float row_shr(float x, float old) {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x),
                                                       0x110 + D, 0xf, 0xf, false));
 }
-// x * (x of lane l - D) inside this lane's 16-lane row; the first D lanes of the
-// row keep x (their DPP source is outside the row and, with bound_ctrl clear,
-// the lane is not written).  One DPP multiply; the s_nop covers the wait
-// states a DPP read needs after a VALU write of its source.
-#define KDA_MUL_ROW_SHR(NAME, D)                                                              \
-    __device__ __forceinline__ float NAME(float x) {                                          \
-        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:" #D                        \
-                     " row_mask:0xf bank_mask:0xf" : "+v"(x));                                \
-        return x;                                                                             \
+// Batched cross-lane steps over the N = 4 or 8 per-channel registers of a
+// lane, one asm block each.  A DPP read needs two wait states after a VALU
+// write of its source: one s_nop covers the first two registers of a block,
+// and each later register was written at least N instructions earlier.
+#define KDA_ARGS8(x) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+#define KDA_ARGS4(x) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])
+#define KDA_SEQ8(OP) OP(0) OP(1) OP(2) OP(3) OP(4) OP(5) OP(6) OP(7)
+#define KDA_SEQ4(OP) OP(0) OP(1) OP(2) OP(3)
+// x[i] *= x[i] of lane l - 4 (row_shr) or l - 4 mod 16 (row_ror) inside the
+// lane's 16-lane row; with row_shr the first lanes of a row, which have no
+// source, keep x[i]
+#define KDA_MUL_DPP(NAME)                                                                       \
+    __device__ __forceinline__ void NAME(float (&x)[8]) {                                       \
+        asm volatile("s_nop 1\n\t" KDA_SEQ8(KDA_MUL_DPP_I_##NAME) : KDA_ARGS8(x));              \
+    }                                                                                           \
+    __device__ __forceinline__ void NAME(float (&x)[4]) {                                       \
+        asm volatile("s_nop 1\n\t" KDA_SEQ4(KDA_MUL_DPP_I_##NAME) : KDA_ARGS4(x));              \
     }
-KDA_MUL_ROW_SHR(mul_row_shr4, 4)
-KDA_MUL_ROW_SHR(mul_row_shr8, 8)
-#undef KDA_MUL_ROW_SHR
-// x * (x of lane l - D mod 16) inside this lane's 16-lane row
-#define KDA_MUL_ROW_ROR(NAME, D)                                                              \
-    __device__ __forceinline__ float NAME(float x) {                                          \
-        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_ror:" #D                        \
-                     " row_mask:0xf bank_mask:0xf" : "+v"(x));                                \
-        return x;                                                                             \
-    }
-KDA_MUL_ROW_ROR(mul_row_ror4, 4)
-KDA_MUL_ROW_ROR(mul_row_ror8, 8)
-#undef KDA_MUL_ROW_ROR
+#define KDA_MUL_DPP_I_mul_row_shr4(i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+#define KDA_MUL_DPP_I_mul_row_shr8(i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+#define KDA_MUL_DPP_I_mul_row_ror8(i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+KDA_MUL_DPP(mul_row_shr4)
+KDA_MUL_DPP(mul_row_shr8)
+KDA_MUL_DPP(mul_row_ror8)
+// z[i] = x[i] * (x[i] of lane l - 4 mod 16 inside the row), into fresh registers
+__device__ __forceinline__ void ror4_mul_into(float (&z)[8], const float (&x)[8]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_mul_f32_dpp %0, %8, %8 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %1, %9, %9 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %2, %10, %10 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %3, %11, %11 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %4, %12, %12 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %5, %13, %13 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %6, %14, %14 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %7, %15, %15 row_ror:4 row_mask:0xf bank_mask:0xf"
+                 : "=&v"(z[0]), "=&v"(z[1]), "=&v"(z[2]), "=&v"(z[3]), "=&v"(z[4]), "=&v"(z[5]), "=&v"(z[6]), "=&v"(z[7])
+                 : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+}
+__device__ __forceinline__ void ror4_mul_into(float (&z)[4], const float (&x)[4]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_mul_f32_dpp %0, %4, %4 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %1, %5, %5 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %2, %6, %6 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %3, %7, %7 row_ror:4 row_mask:0xf bank_mask:0xf"
+                 : "=&v"(z[0]), "=&v"(z[1]), "=&v"(z[2]), "=&v"(z[3])
+                 : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+}
+// f[i] *= w[i] of lane l - 4 inside the row; the first four lanes of a row
+// keep f[i]
+__device__ __forceinline__ void mul_shr4_from(float (&f)[8], const float (&w)[8]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_mul_f32_dpp %0, %8, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %1, %9, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %2, %10, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %3, %11, %3 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %4, %12, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %5, %13, %5 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %6, %14, %6 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %7, %15, %7 row_shr:4 row_mask:0xf bank_mask:0xf"
+                 : KDA_ARGS8(f)
+                 : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]));
+}
+__device__ __forceinline__ void mul_shr4_from(float (&f)[4], const float (&w)[4]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_mul_f32_dpp %0, %4, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %1, %5, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %2, %6, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "v_mul_f32_dpp %3, %7, %3 row_shr:4 row_mask:0xf bank_mask:0xf"
+                 : KDA_ARGS4(f)
+                 : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
+}
+// exchange between 16-lane rows: (a, b) -> ([a0 b0 a2 b2], [a1 b1 a3 b3]) by
+// rows, for each pair (a[i], b[i]); the trailing s_nop keeps the results two
+// wait states away from a following DPP read
+__device__ __forceinline__ void swap_rows16(float (&a)[8], float (&b)[8]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_permlane16_swap_b32 %0, %8\n\t"
+                 "v_permlane16_swap_b32 %1, %9\n\t"
+                 "v_permlane16_swap_b32 %2, %10\n\t"
+                 "v_permlane16_swap_b32 %3, %11\n\t"
+                 "v_permlane16_swap_b32 %4, %12\n\t"
+                 "v_permlane16_swap_b32 %5, %13\n\t"
+                 "v_permlane16_swap_b32 %6, %14\n\t"
+                 "v_permlane16_swap_b32 %7, %15\n\t"
+                 "s_nop 1"
+                 : KDA_ARGS8(a), KDA_ARGS8(b));
+}
+__device__ __forceinline__ void swap_rows16(float (&a)[4], float (&b)[4]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_permlane16_swap_b32 %0, %4\n\t"
+                 "v_permlane16_swap_b32 %1, %5\n\t"
+                 "v_permlane16_swap_b32 %2, %6\n\t"
+                 "v_permlane16_swap_b32 %3, %7\n\t"
+                 "s_nop 1"
+                 : KDA_ARGS4(a), KDA_ARGS4(b));
+}
+#undef KDA_MUL_DPP
+#undef KDA_MUL_DPP_I_mul_row_shr4
+#undef KDA_MUL_DPP_I_mul_row_shr8
+#undef KDA_MUL_DPP_I_mul_row_ror8
+#undef KDA_SEQ8
+#undef KDA_SEQ4
+#undef KDA_ARGS8
+#undef KDA_ARGS4
 // y in the 16-lane rows selected by ROWS (bit r = lanes 16r..16r+15), x elsewhere
 template <int ROWS>
 __device__ __forceinline__ float rows_sel(float x, float y) {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(y), 0xE4, ROWS, 0xf, false));
-}
-// exchange between 16-lane rows: (a, b) -> ([a0 b0 a2 b2], [a1 b1 a3 b3]) by rows
-__device__ __forceinline__ void swap_rows16(float& a, float& b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
 }
 
 template <int DK, int DVT>
@@ -393,40 +468,36 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             // Products over the chunk's tokens, per channel.  w: over the
             // lane's 16-lane row through its last token (tokens 16r..pr0+3);
             // z: over the whole row (tokens 16r..16r+15), in every lane.
-            float w[CPL];
+            float w[CPL], z[CPL];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) w[c] = inc[c];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) w[c] = mul_row_shr4(w[c]);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) w[c] = mul_row_shr8(w[c]);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_ror4(inc[c]);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) inc[c] = mul_row_ror8(inc[c]);
+            mul_row_shr4(w);
+            mul_row_shr8(w);
+            ror4_mul_into(z, inc);
+            mul_row_ror8(z);
             // With row totals z0..z3, Pm = z0 z1 and P_t / Pm = w_t F where F
-            // is 1/(z0 z1), 1/z1, 1 and z2 in rows 0..3.  After the row
-            // exchange a = (z0, z0, z2, z2) and b = (z1, z1, z3, z3) by row,
-            // so a b is Pm in rows 0, 1 and Pn / Pm in rows 2, 3.
-            float f[CPL], g[CPL], pq[CPL];
+            // is 1/(z0 z1), 1/z1, 1 and z2 in rows 0..3.  The row exchange
+            // gives a = (z0, z0, z2, z2) and b = (z1, z1, z3, z3) by row; with
+            // t = (z0, 1, 1, z2), u = t b is Pm in row 0 and Pn / Pm in row 3.
+            float a[CPL], u[CPL], f[CPL], g[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) a[c] = z[c];
+            swap_rows16(a, z);  // z now holds b
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                float a = inc[c], b = inc[c];
-                swap_rows16(a, b);
-                pq[c] = a * b;
-                const float u = rows_sel<0x8>(rows_sel<0x1>(b, pq[c]), a);  // z0z1, z1, z3, z2
-                const float ru = fast_rcp(u);
-                const float fr = rows_sel<0x4>(rows_sel<0x8>(ru, a), 1.f);
-                f[c] = row_shr<4>(w[c], 1.f) * fr;  // P through row pr0 - 1, over Pm
-                g[c] = fast_rcp(w[c] * fr);         // Pm / P through row pr0 + 3
+                const float t = rows_sel<0x6>(a[c], 1.f);
+                u[c] = t * z[c];
+                f[c] = rows_sel<0xC>(fast_rcp(u[c]), t);  // F
+                g[c] = fast_rcp(w[c] * f[c]);            // Pm / P through row pr0 + 3
             }
+            mul_shr4_from(f, w);  // P through row pr0 - 1, over Pm
             // Pm from the first lanes of row 0, Pn / Pm from the first lanes of
-            // row 2; the helper forms Pn from the two
-            if (rg == 0 || rg == 8) {
+            // row 3; the helper forms Pn from the two
+            if (rg == 0 || rg == 12) {
                 float* vec = reinterpret_cast<float*>(buf(par, L::bVec)) + (rg == 0 ? 0 : 2 * DK);
 #pragma unroll
                 for (int c = 0; c < CPL; c += 4)
-                    *reinterpret_cast<float4*>(vec + pc0 + c) = make_float4(pq[c], pq[c + 1], pq[c + 2], pq[c + 3]);
+                    *reinterpret_cast<float4*>(vec + pc0 + c) = make_float4(u[c], u[c + 1], u[c + 2], u[c + 3]);
             }
             bf16_t* kr_b = reinterpret_cast<bf16_t*>(buf(par, L::bKr));
             bf16_t* qr_b = reinterpret_cast<bf16_t*>(buf(par, L::bQr));
