@@ -773,17 +773,21 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const int ln = lx & 15, lg = lx >> 4;
             const bf16_t* lo_b = reinterpret_cast<const bf16_t*>(buf(par, L::bLo));
             const float* vec = reinterpret_cast<const float*>(buf(par, L::bVec));
-            // U_a = D_a (Y_a - sum_{b<a} L_ab U_b); lo_b holds -L_ab
+            // U_a = D_a (Y_a - sum_{b<a} L_ab U_b); lo_b holds -L_ab.  All
+            // fragments are read before the chain starts, so no step of the
+            // chain waits for LDS.
+            Mf::F16 fl[6], fd[4];
+#pragma unroll
+            for (int j = 0; j < 6; ++j) fl[j] = Mf::ld16(lo_b + j * BLK + ln * LDB + lg * 4);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) fd[a] = Mf::ld16(sD + a * BLK + ln * LDB + lg * 4);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 f32x4 acc = Y[a];
 #pragma unroll
-                for (int b = 0; b < a; ++b) {
-                    const auto fl = Mf::ld16(lo_b + (a * (a - 1) / 2 + b) * BLK + ln * LDB + lg * 4);
-                    acc = Mf::k16(fl, UP[b], acc);
-                }
-                const auto fd = Mf::ld16(sD + a * BLK + ln * LDB + lg * 4);
-                UP[a] = Mf::pack16(Mf::k16(fd, Mf::pack16(acc), zero4()));
+                for (int b = 0; b < a; ++b) acc = Mf::k16(fl[a * (a - 1) / 2 + b], UP[b], acc);
+                UP[a] = Mf::pack16(Mf::k16(fd[a], Mf::pack16(acc), zero4()));
             }
             // S <- Pn*S0 + (Pn/Pm) (Kc^T U); blocks 2s, 2s+1 of U form k-step s
             Mf::F32 fu[2];
