@@ -252,7 +252,7 @@ struct Lay6 {
     // single copies
     static constexpr size_t oKcT = 2 * szBuf;                   // [DK][LDC]
     static constexpr size_t oKc = oKcT + (size_t)DK * LDC * 2;  // [64][LDK]
-    static constexpr size_t oLd = oKc + szTok;                  // fp32 [4][16 cols][LDL]
+    static constexpr size_t oLd = oKc + szTok;                  // fp32 [4][16 rows][LDL]
     static constexpr size_t oD = oLd + (size_t)4 * 16 * LDL * 4;  // D_a, 4 blocks row-major
     static constexpr size_t bytes = oD + (size_t)4 * BLK * 2;
     static_assert(bytes <= 160 * 1024, "LDS budget");
@@ -298,18 +298,17 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // ---------------------------------------------------------- Gram blocks
     // Blocks (a, b), b <= a, of chunk ch: lane holds A[16a + ln][16b + 4lg + e]
     // and M likewise.  Diagonal blocks go to sLd (fp32, strictly lower part of
-    // L_aa, column-major) and M; the others to -L_ab and M.  A worker takes
+    // L_aa, row-major) and M; the others to -L_ab and M.  A worker takes
     // one or two blocks of one block row a, so the Kr and Qr fragments of the
     // row are read from LDS once for both.
     auto gram_out = [&](int par, int a, int b, f32x4 cA, f32x4 cM, float br, int ln, int lg) __attribute__((always_inline)) {
         bf16_t* m_b = reinterpret_cast<bf16_t*>(buf(par, L::bM));
         const int jn = a * (a + 1) / 2 + b;
         if (a == b) {
+            f32x4 ld;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = lg * 4 + e;
-                sLd[(a * 16 + i) * LDL + ln] = (i < ln) ? br * cA[e] : 0.f;
-            }
+            for (int e = 0; e < 4; ++e) ld[e] = (lg * 4 + e < ln) ? br * cA[e] : 0.f;
+            *reinterpret_cast<f32x4*>(sLd + (a * 16 + ln) * LDL + lg * 4) = ld;
             f32x4 mm;
 #pragma unroll
             for (int e = 0; e < 4; ++e) mm[e] = (lg * 4 + e <= ln) ? cM[e] : 0.f;
@@ -628,27 +627,33 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             }
         };
         // D_a = (I + L_aa)^{-1} of the chunk whose diagonal blocks are in sLd:
-        // lane (block lg, column ln), right-looking, fp32
+        // lane (block lg, row ln) forms row ln of D_a from D (I + L) = I,
+        // right-looking from the last column: once x[k] = D[ln][k] is final,
+        // x[k] L[k][j] leaves every x[j], j < k.  The 15 steps each read one
+        // row of L_aa (the same for the 16 lanes of a block) and the row of
+        // D goes out as two 16-byte stores.
         auto h_dsolve = [&]() {
             const int lx = (int)opaque((uint32_t)l);
             const int ln = lx & 15, lg = lx >> 4;
-            float xs[16];
+            float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) xs[r] = (r == ln) ? 1.f : 0.f;
+            for (int k = 0; k < 16; ++k) x[k] = (k == ln) ? 1.f : 0.f;
             const float* La = sLd + lg * 16 * LDL;
 #pragma unroll
-            for (int i = 0; i < 15; ++i) {
-                float colv[16];
+            for (int k = 15; k >= 1; --k) {
+                float row[16];
 #pragma unroll
-                for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
-                    const float4 v = ld4(La + i * LDL + q4 * 4);
-                    colv[q4 * 4] = v.x; colv[q4 * 4 + 1] = v.y; colv[q4 * 4 + 2] = v.z; colv[q4 * 4 + 3] = v.w;
+                for (int q4 = 0; q4 < (k + 3) / 4; ++q4) {
+                    const float4 v = ld4(La + k * LDL + q4 * 4);
+                    row[q4 * 4] = v.x; row[q4 * 4 + 1] = v.y; row[q4 * 4 + 2] = v.z; row[q4 * 4 + 3] = v.w;
                 }
 #pragma unroll
-                for (int r = i + 1; r < 16; ++r) xs[r] -= colv[r] * xs[i];
+                for (int j = 0; j < k; ++j) x[j] -= x[k] * row[j];
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sD[lg * BLK + r * LDB + ln] = (bf16_t)xs[r];
+            bf16_t* dr = sD + lg * BLK + ln * LDB;
+            *reinterpret_cast<uint4*>(dr) = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+            *reinterpret_cast<uint4*>(dr + 8) =
+                make_uint4(pack2(x[8], x[9]), pack2(x[10], x[11]), pack2(x[12], x[13]), pack2(x[14], x[15]));
         };
         h_load(0);
         h_write_beta(0);
