@@ -77,8 +77,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # the GPU reaches its steady clock only after some 10 ms of this work
-    ap.add_argument("--warmup", type=int, default=50)
+    # The shader clock climbs for some 25 ms of this work (about 1.9 to 2.35 GHz,
+    # read with s_memtime against s_memrealtime from a one-wave sampler on a second
+    # stream); 200 warm-up steps (~36 ms) put the timed steps at the steady clock.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
