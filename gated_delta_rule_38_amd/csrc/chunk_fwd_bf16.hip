@@ -22,8 +22,10 @@
 //   producers (4 waves, dk/4 key channels each): decays and the operands
 //     Kr, Qr, Kc, Kc^T of chunk c+1, the q, k, alpha prefetch of chunk c+3,
 //     and Gram blocks of chunk c+1;
-//   helper (last wave): the inverses D_a and Pn of chunk c, beta and V^T of
-//     chunk c+1 (loaded a chunk earlier), and Gram blocks.
+//   helper: the inverses D_a and Pn of chunk c, beta and V^T of chunk c+1
+//     (loaded a chunk earlier), and Gram blocks;
+//   prefetch wave (last): touches the q, k, alpha and V lines of chunk c+3
+//     so that the loads above find them in L2.
 // In each segment the waves on its longest path (producers in segment 1,
 // consumers in segment 2) take raised issue priority over the waves they
 // share a SIMD with.
@@ -229,7 +231,7 @@ struct Lay6 {
     static constexpr int NJT = DVT / 16;       // consumer waves
     static constexpr int NP = 4;               // producer waves
     static constexpr int CPL = DK / 16;        // key channels per producer lane
-    static constexpr int NW = NJT + NP + 1;    // + the helper
+    static constexpr int NW = NJT + NP + 2;    // + the helper and the prefetch wave
     static constexpr int NTH = 64 * NW;
     static constexpr int RPV = DVT / 8;        // V rows per helper lane (8 columns each)
     static constexpr int LDK = DK + 8;         // bf16 pitch of [token][channel] tiles
@@ -675,6 +677,54 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             gram_share(ch + 1, NP);
             __syncthreads();
         }
+        return;
+    }
+
+    if (w == NJT + NP + 1) {
+        // ====================================================== prefetch wave
+        // Pulls the q, k, alpha and V lines of chunk c + 3 into L2 while chunk c
+        // runs, so that the producers' loads of them (issued during chunk c + 1)
+        // and the helper's (chunk c + 2) hit L2 instead of waiting out HBM
+        // latency with some 500 lines in flight per compute unit.  Value tile jt of a unit takes
+        // rows jt*64/njt.. of the chunk, one line per lane and tensor; the
+        // four tiles together touch every line once.  Three register sets
+        // rotate, so a wait for a set's loads comes three chunks after them.
+        uint32_t P0[4] = {0u, 0u, 0u, 0u}, P1[4] = {0u, 0u, 0u, 0u}, P2[4] = {0u, 0u, 0u, 0u};
+        auto pf = [&](int ch, uint32_t (&r)[4]) {
+            const int lx = (int)opaque((uint32_t)l);
+            const int njt = p.njt_all;
+            const int nr = __builtin_amdgcn_readfirstlane(max(0, min(len - ch * CH, CH)));
+            const size_t tok = (size_t)(t0 + (long)ch * CH) * H + h;
+            const uint32_t row = (uint32_t)(jt * (CH / njt) + lx / njt), sub = (uint32_t)(lx % njt);
+            const Rsrc rq = make_rsrc(gq + tok * DK, (uint32_t)nr * rsq);
+            const Rsrc rk = make_rsrc(gk + tok * DK, (uint32_t)nr * rsq);
+            const Rsrc ra = make_rsrc(ga + tok * DK, (uint32_t)nr * rsa);
+            const Rsrc rv = make_rsrc(gv + tok * DV, (uint32_t)nr * rsv);
+            r[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, row * rsq + (sub & 1) * 128, 0, 0);
+            r[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, row * rsq + (sub & 1) * 128, 0, 0);
+            r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsa + (sub & 3) * 128, 0, 0);
+            r[3] = __builtin_amdgcn_raw_buffer_load_b32(rv, row * rsv + (sub & 1) * 128, 0, 0);
+        };
+        __syncthreads();
+        __syncthreads();
+        int ch = 0;
+        for (; ch + 2 < nch; ch += 3) {
+            pf(ch + 3, P0);
+            __syncthreads();
+            __syncthreads();
+            pf(ch + 4, P1);
+            __syncthreads();
+            __syncthreads();
+            pf(ch + 5, P2);
+            __syncthreads();
+            __syncthreads();
+        }
+        for (; ch < nch; ++ch) {
+            __syncthreads();
+            __syncthreads();
+        }
+        asm volatile("" :: "v"(P0[0]), "v"(P0[1]), "v"(P0[2]), "v"(P0[3]), "v"(P1[0]), "v"(P1[1]), "v"(P1[2]),
+                     "v"(P1[3]), "v"(P2[0]), "v"(P2[1]), "v"(P2[2]), "v"(P2[3]));
         return;
     }
 
