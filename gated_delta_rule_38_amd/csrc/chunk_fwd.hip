@@ -605,9 +605,9 @@ static hipError_t launch_chunk_dk(const ChunkArgs& a, int dvt, const int* order,
 }
 
 int plan_chunk_dvt(int units, int dv, bool bf16) {
-    // widest value tile that still gives every compute unit a workgroup; the
-    // pipelined bf16 kernel holds at most 32 columns per workgroup
-    for (int dvt = bf16 ? 32 : 64; dvt >= 16; dvt /= 2)
+    // widest value tile that still gives every compute unit a workgroup
+    (void)bf16;
+    for (int dvt = 64; dvt >= 16; dvt /= 2)
         if (dvt <= dv && (long)units * (dv / dvt) >= 256) return dvt;
     return 16;
 }

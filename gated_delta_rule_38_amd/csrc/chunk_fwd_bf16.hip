@@ -14,11 +14,11 @@
 //     U_a = D_a (beta_a X_a - sum_{b<a} L_ab U_b),   D_a = (I + L_aa)^{-1},
 // so the 64x64 inverse is never formed.
 //
-// Roles.  A workgroup owns one (unit, 16*NJT value columns); its waves keep
+// Roles.  A workgroup owns one (unit, DVT value columns); its waves keep
 // one role for the whole kernel:
-//   consumers (waves 0..NJT-1): one 16-column slice of the fp32 state each,
-//     in registers; they run the serial chain of chunk c (X, the solve, O,
-//     the next state);
+//   consumers (waves 0..NJT-1): DVT/NJT columns of the fp32 state each, in
+//     registers; they run the serial chain of chunk c (X, the solve, O, the
+//     next state);
 //   producers (4 waves, dk/4 key channels each): decays and the operands
 //     Kr, Qr, Kc, Kc^T of chunk c+1, the q, k, alpha prefetch of chunk c+3,
 //     and Gram blocks of chunk c+1;
@@ -228,7 +228,8 @@ __device__ __forceinline__ float rows_sel(float x, float y) {
 
 template <int DK, int DVT>
 struct Lay6 {
-    static constexpr int NJT = DVT / 16;       // consumer waves
+    static constexpr int NJT = DVT >= 32 ? 2 : 1;  // consumer waves
+    static constexpr int NT = DVT / 16 / NJT;      // 16-column state tiles per consumer
     static constexpr int NP = 4;               // producer waves
     static constexpr int CPL = DK / 16;        // key channels per producer lane
     static constexpr int NW = NJT + NP + 2;    // + the helper and the prefetch wave
@@ -265,7 +266,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     using L = Lay6<DK, DVT>;
     using Mf = Mma<bf16_t>;
     constexpr int LDK = L::LDK, LDC = L::LDC, LDB = L::LDB, LDL = L::LDL, BLK = L::BLK;
-    constexpr int NJT = L::NJT, NP = L::NP, CPL = L::CPL, RPV = L::RPV;
+    constexpr int NJT = L::NJT, NT = L::NT, NP = L::NP, CPL = L::CPL, RPV = L::RPV;
     constexpr int NCT = DK / 16;          // 16-row tiles of a state slice
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -619,13 +620,14 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             for (int c = 0; c < 8; ++c) {
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 bf16_t* dst = reinterpret_cast<bf16_t*>(buf(ch & 1, L::bVT)) + (cg * 8 + c) * L::LDV + RPV * rq;
-                const uint32_t w01 = __builtin_amdgcn_perm(HV[4 + c / 2], HV[c / 2], sel);  // rows 0, 1
-                if constexpr (RPV == 4) {
-                    const uint32_t w23 = __builtin_amdgcn_perm(HV[12 + c / 2], HV[8 + c / 2], sel);
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(w01, w23);
-                } else {
-                    *reinterpret_cast<uint32_t*>(dst) = w01;
-                }
+                uint32_t wr[RPV / 2];  // rows 2i, 2i + 1 of column c
+#pragma unroll
+                for (int i = 0; i < RPV / 2; ++i)
+                    wr[i] = __builtin_amdgcn_perm(HV[4 * (2 * i + 1) + c / 2], HV[4 * (2 * i) + c / 2], sel);
+                // the V^T pitch keeps runs 8-byte aligned only
+#pragma unroll
+                for (int i = 0; i < RPV / 2; i += 2)
+                    store_run<uint32_t, (RPV / 2 < 2 ? RPV / 2 : 2)>(reinterpret_cast<uint32_t*>(dst) + i, wr + i);
             }
         };
         // D_a = (I + L_aa)^{-1} of the chunk whose diagonal blocks are in sLd:
@@ -732,25 +734,30 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // The consumers carry the serial state chain.  In segment 2 it is the
     // longest path, so the SIMD arbiter is told to prefer them there over the
     // producers they share a SIMD with; in segment 1 they have slack and take
-    // the lowest priority.
+    // the lowest priority.  Consumer cj holds NT 16-column tiles of the state;
+    // with NT = 2 (DVT 64) the tiles share every fragment read and their
+    // independent chains interleave.
     // The state, U and Pm*S stay in registers: the operand orders set out at
     // kct_row let each product take them as they are.
-    const int cj = w;                        // consumer column tile
-    const int colw = jt * DVT + cj * 16;     // first value column of this wave
-    const int col = colw + ln;               // this lane's value column
+    const int cj = w;                                // consumer
+    const int colw = jt * DVT + cj * 16 * NT;        // first value column of this wave
+    const int col = colw + ln;                       // this lane's value column in tile 0
     bf16_t* __restrict__ go = static_cast<bf16_t*>(p.o);
     const size_t sbase = ((size_t)wi.seq * H + h) * DK * DV;
 
-    f32x4 S[NCT], Y[4], OI[4];  // state slice, beta-scaled X, (Qr (Pm S0))^T
-    Mf::F16 UP[4];              // U of the last solved chunk, packed (B operand layout)
+    f32x4 S[NT][NCT], Y[NT][4], OI[NT][4];  // state, beta-scaled X, (Qr (Pm S0))^T
+    Mf::F16 UP[NT][4];                      // U of the last solved chunk (B operand layout)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        S[ct] = zero4();
-        if (p.s0) {
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[ct][e] = p.s0[sbase + (size_t)state_ch(ct, lg, e) * DV + col];
+        for (int ct = 0; ct < NCT; ++ct) {
+            S[j][ct] = zero4();
+            if (p.s0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[j][ct][e] = p.s0[sbase + (size_t)state_ch(ct, lg, e) * DV + col + 16 * j];
+            }
         }
-    }
     // O_a = scale (OI_a + sum_{b<=a} M_ab U_b) of chunk ch, one 16-token block
     // of U per step; run in the consumers' first segment of chunk ch + 1 (M and
     // OI of chunk ch are still in place there) or after the last chunk.  The
@@ -765,21 +772,32 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         const uint32_t ob = (uint32_t)ln * rsv + (uint32_t)lg * 8;  // token ln, column colw + 4lg
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            f32x4 co = OI[a];
+            f32x4 co[NT];
 #pragma unroll
-            for (int b = 0; b <= a; ++b)
-                co = Mf::k16(UP[b], Mf::ld16(m_b + (a * (a + 1) / 2 + b) * BLK + ln * LDB + lg * 4), co);
-            const u32x2 ow = {pack2(p.scale * co[0], p.scale * co[1]), pack2(p.scale * co[2], p.scale * co[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(ow, ro, ob + (uint32_t)(a * 16) * rsv, 0, 0);
+            for (int j = 0; j < NT; ++j) co[j] = OI[j][a];
+#pragma unroll
+            for (int b = 0; b <= a; ++b) {
+                const auto fm = Mf::ld16(m_b + (a * (a + 1) / 2 + b) * BLK + ln * LDB + lg * 4);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) co[j] = Mf::k16(UP[j][b], fm, co[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const u32x2 ow = {pack2(p.scale * co[j][0], p.scale * co[j][1]),
+                                  pack2(p.scale * co[j][2], p.scale * co[j][3])};
+                __builtin_amdgcn_raw_buffer_store_b64(ow, ro, ob + (uint32_t)(a * 16) * rsv + 32 * j, 0, 0);
+            }
         }
     };
-    // the pair of state tiles 2s, 2s+1 times Pm, as one 32-deep B operand
-    auto sp_frag = [&](const float* pm, int s) {
+    // the pair of state tiles 2s, 2s+1 of column tile j times Pm, as one
+    // 32-deep B operand
+    auto sp_frag = [&](const float* pm, int j, int s) {
         const int g = (int)opaque((uint32_t)l) >> 4;
         const float4 m0 = ld4(pm + s * 32 + g * 8), m1 = ld4(pm + s * 32 + g * 8 + 4);
-        const f32x4 a = {m0.x * S[2 * s][0], m0.y * S[2 * s][1], m0.z * S[2 * s][2], m0.w * S[2 * s][3]};
-        const f32x4 b = {m1.x * S[2 * s + 1][0], m1.y * S[2 * s + 1][1], m1.z * S[2 * s + 1][2],
-                         m1.w * S[2 * s + 1][3]};
+        const f32x4 a = {m0.x * S[j][2 * s][0], m0.y * S[j][2 * s][1], m0.z * S[j][2 * s][2],
+                         m0.w * S[j][2 * s][3]};
+        const f32x4 b = {m1.x * S[j][2 * s + 1][0], m1.y * S[j][2 * s + 1][1], m1.z * S[j][2 * s + 1][2],
+                         m1.w * S[j][2 * s + 1][3]};
         return Mf::F32{__builtin_shufflevector(Mf::pack16(a).v, Mf::pack16(b).v, 0, 1, 2, 3, 4, 5, 6, 7)};
     };
     __syncthreads();
@@ -797,27 +815,38 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const float* beta = reinterpret_cast<const float*>(buf(par, L::bBeta));
             const float* vec = reinterpret_cast<const float*>(buf(par, L::bVec));
             const bf16_t* vt_b = reinterpret_cast<const bf16_t*>(buf(par, L::bVT));
-            Mf::F32 fs[DK / 32];
+            Mf::F32 fs[NT][DK / 32];
 #pragma unroll
-            for (int s = 0; s < DK / 32; ++s) fs[s] = sp_frag(vec, s);
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s) fs[j][s] = sp_frag(vec, j, s);
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                f32x4 cx = zero4(), co = zero4();
+                f32x4 cx[NT], co[NT];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) cx[j] = co[j] = zero4();
 #pragma unroll
                 for (int s = 0; s < DK / 32; ++s) {
                     const auto fk = Mf::ld32(kr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
                     const auto fq = Mf::ld32(qr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
-                    cx = Mf::k32(fk, fs[s], cx);
-                    co = Mf::k32(fs[s], fq, co);  // transposed, as c_out takes it
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        cx[j] = Mf::k32(fk, fs[j][s], cx[j]);
+                        co[j] = Mf::k32(fs[j][s], fq, co[j]);  // transposed, as c_out takes it
+                    }
                 }
                 const float4 b4 = ld4(beta + a * 16 + lg * 4);
-                const uint2 v4 = *reinterpret_cast<const uint2*>(vt_b + (cj * 16 + ln) * L::LDV + a * 16 + lg * 4);
-                // beta_r (v_r - (Kr Pm S0)_r); rows past the end have v = beta = 0
-                Y[a][0] = b4.x * (lo_f(v4.x) - cx[0]);
-                Y[a][1] = b4.y * (hi_f(v4.x) - cx[1]);
-                Y[a][2] = b4.z * (lo_f(v4.y) - cx[2]);
-                Y[a][3] = b4.w * (hi_f(v4.y) - cx[3]);
-                OI[a] = co;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const uint2 v4 = *reinterpret_cast<const uint2*>(
+                        vt_b + ((cj * NT + j) * 16 + ln) * L::LDV + a * 16 + lg * 4);
+                    // beta_r (v_r - (Kr Pm S0)_r); rows past the end have v = beta = 0
+                    Y[j][a][0] = b4.x * (lo_f(v4.x) - cx[j][0]);
+                    Y[j][a][1] = b4.y * (hi_f(v4.x) - cx[j][1]);
+                    Y[j][a][2] = b4.z * (lo_f(v4.y) - cx[j][2]);
+                    Y[j][a][3] = b4.w * (hi_f(v4.y) - cx[j][3]);
+                    OI[j][a] = co[j];
+                }
             }
         }
         __syncthreads();
@@ -829,39 +858,52 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const bf16_t* lo_b = reinterpret_cast<const bf16_t*>(buf(par, L::bLo));
             const float* vec = reinterpret_cast<const float*>(buf(par, L::bVec));
             // U_a = D_a (Y_a - sum_{b<a} L_ab U_b); lo_b holds -L_ab.  All
-            // fragments are read before the chain starts, so no step of the
+            // fragments are read before the chains start, so no step of a
             // chain waits for LDS.
             Mf::F16 fl[6], fd[4];
 #pragma unroll
-            for (int j = 0; j < 6; ++j) fl[j] = Mf::ld16(lo_b + j * BLK + ln * LDB + lg * 4);
+            for (int i = 0; i < 6; ++i) fl[i] = Mf::ld16(lo_b + i * BLK + ln * LDB + lg * 4);
 #pragma unroll
             for (int a = 0; a < 4; ++a) fd[a] = Mf::ld16(sD + a * BLK + ln * LDB + lg * 4);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                f32x4 acc = Y[a];
 #pragma unroll
-                for (int b = 0; b < a; ++b) acc = Mf::k16(fl[a * (a - 1) / 2 + b], UP[b], acc);
-                UP[a] = Mf::pack16(Mf::k16(fd[a], Mf::pack16(acc), zero4()));
+                for (int j = 0; j < NT; ++j) {
+                    f32x4 acc = Y[j][a];
+#pragma unroll
+                    for (int b = 0; b < a; ++b) acc = Mf::k16(fl[a * (a - 1) / 2 + b], UP[j][b], acc);
+                    UP[j][a] = Mf::pack16(Mf::k16(fd[a], Mf::pack16(acc), zero4()));
+                }
             }
             // S <- Pn*S0 + (Pn/Pm) (Kc^T U); blocks 2s, 2s+1 of U form k-step s
-            Mf::F32 fu[2];
+            Mf::F32 fu[NT][2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                fu[s].v = __builtin_shufflevector(UP[2 * s].v, UP[2 * s + 1].v, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 acc = zero4();
+            for (int j = 0; j < NT; ++j)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    acc = Mf::k32(Mf::ld32(sKcT + (ct * 16 + ln) * LDC + s * 32 + lg * 8), fu[s], acc);
+                    fu[j][s].v = __builtin_shufflevector(UP[j][2 * s].v, UP[j][2 * s + 1].v, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 acc[NT];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[j] = zero4();
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const auto fkt = Mf::ld32(sKcT + (ct * 16 + ln) * LDC + s * 32 + lg * 8);
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) acc[j] = Mf::k32(fkt, fu[j][s], acc[j]);
+                }
                 const int c0 = state_ch(ct, lg, 0);
                 const float4 pn = ld4(vec + DK + c0);
                 const float4 pnm = ld4(vec + 2 * DK + c0);
-                S[ct][0] = pn.x * S[ct][0] + pnm.x * acc[0];
-                S[ct][1] = pn.y * S[ct][1] + pnm.y * acc[1];
-                S[ct][2] = pn.z * S[ct][2] + pnm.z * acc[2];
-                S[ct][3] = pn.w * S[ct][3] + pnm.w * acc[3];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    S[j][ct][0] = pn.x * S[j][ct][0] + pnm.x * acc[j][0];
+                    S[j][ct][1] = pn.y * S[j][ct][1] + pnm.y * acc[j][1];
+                    S[j][ct][2] = pn.z * S[j][ct][2] + pnm.z * acc[j][2];
+                    S[j][ct][3] = pn.w * S[j][ct][3] + pnm.w * acc[j][3];
+                }
             }
         }
         __syncthreads();
@@ -870,10 +912,12 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     if (nch > 0) c_out(nch - 1);
     if (p.sT) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                p.sT[sbase + (size_t)state_ch(ct, lg, e) * DV + col] = S[ct][e];
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p.sT[sbase + (size_t)state_ch(ct, lg, e) * DV + col + 16 * j] = S[j][ct][e];
     }
 }
 
@@ -891,11 +935,14 @@ static hipError_t launch_t(const KParams& p, hipStream_t stream) {
 }
 
 // value-column tile widths this kernel supports
-bool chunk_bf16_supports(int dvt) { return dvt == 16 || dvt == 32; }
+bool chunk_bf16_supports(int dvt) { return dvt == 16 || dvt == 32 || dvt == 64; }
 
 hipError_t launch_chunk_bf16(const KParams& p, int dk, int dvt, hipStream_t stream) {
-    if (dk == 128) return dvt == 16 ? launch_t<128, 16>(p, stream) : launch_t<128, 32>(p, stream);
-    return dvt == 16 ? launch_t<64, 16>(p, stream) : launch_t<64, 32>(p, stream);
+    if (dk == 128)
+        return dvt == 16 ? launch_t<128, 16>(p, stream)
+             : dvt == 32 ? launch_t<128, 32>(p, stream) : launch_t<128, 64>(p, stream);
+    return dvt == 16 ? launch_t<64, 16>(p, stream)
+         : dvt == 32 ? launch_t<64, 32>(p, stream) : launch_t<64, 64>(p, stream);
 }
 
 }  // namespace kda
