@@ -13,13 +13,20 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
-           "kda_status_string", "kda_version", "KDAError", "LIB_PATH", "load_library"]
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_step",
+           "kda_recurrent_step_gated", "kda_chunk_fwd_workspace_size", "kda_status_string",
+           "kda_version", "KDAError", "LIB_PATH", "load_library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
+# forget-gate granularity (kda_gate): alpha per key channel (KDA), one alpha
+# per token and head (Gated DeltaNet), or none (DeltaNet, alpha = 1)
+KDA_GATE_CHANNEL = 0
+KDA_GATE_HEAD = 1
+KDA_GATE_NONE = 2
+_GATES = {"channel": KDA_GATE_CHANNEL, "head": KDA_GATE_HEAD, "none": KDA_GATE_NONE}
 _STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
            3: "KDA_ERROR_MISALIGNED", 4: "KDA_ERROR_INSUFFICIENT_WORKSPACE", 5: "KDA_ERROR_HIP"}
 
@@ -46,8 +53,14 @@ def load_library():
         lib.kda_chunk_fwd.restype = i
         lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
                                       vp, ip, i, f, i, vp, sz, vp]
+        lib.kda_chunk_fwd_gated.restype = i
+        lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, i,
+                                            vp, ip, i, f, i, vp, sz, vp]
         lib.kda_recurrent_step.restype = i
         lib.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, vp]
+        lib.kda_recurrent_step_gated.restype = i
+        lib.kda_recurrent_step_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i,
+                                                 f, vp]
         lib.kda_chunk_fwd_workspace_size.restype = sz
         lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -102,6 +115,25 @@ def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype=torch.bfloat16
     return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, code))
 
 
+def _gate_code(gate):
+    if isinstance(gate, str):
+        if gate not in _GATES:
+            raise ValueError("gate must be one of %s, got %r" % (sorted(_GATES), gate))
+        return _GATES[gate]
+    return int(gate)
+
+
+def _check_alpha(alpha, gate, lead, dk, dev):
+    """alpha for a gate code: [*lead, dk] per channel, [*lead] per head, None."""
+    if gate == KDA_GATE_NONE:
+        if alpha is not None:
+            raise ValueError("alpha must be None without a forget gate")
+    elif gate == KDA_GATE_HEAD:
+        _check(alpha, "alpha", torch.float32, dev, tuple(lead))
+    else:
+        _check(alpha, "alpha", torch.float32, dev, tuple(lead) + (dk,))
+
+
 def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
                   cu_seqlens_host=None, scale=None, output_final_state=True,
                   final_state=None, o=None, chunk_size=64, workspace=None):
@@ -118,6 +150,23 @@ def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
     kda_chunk_fwd_workspace_size() bytes (else one is allocated per call).
     Returns (o, final_state or None).
     """
+    return _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
+                      output_final_state, final_state, o, chunk_size, workspace, None)
+
+
+def kda_chunk_fwd_gated(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
+                        cu_seqlens_host=None, scale=None, output_final_state=True,
+                        final_state=None, o=None, chunk_size=64, workspace=None,
+                        gate="channel"):
+    """kda_chunk_fwd with the forget gate's granularity chosen by ``gate``:
+    "channel" (alpha [B, T, H, dk], KDA), "head" (alpha [B, T, H], Gated
+    DeltaNet) or "none" (alpha None, DeltaNet)."""
+    return _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
+                      output_final_state, final_state, o, chunk_size, workspace, _gate_code(gate))
+
+
+def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
+               output_final_state, final_state, o, chunk_size, workspace, gate):
     lib = load_library()
     dev = q.device
     dt = q.dtype
@@ -127,7 +176,7 @@ def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
     _check(q, "q", dt, dev)
     _check(k, "k", dt, dev, (B, T, H, dk))
     _check(v, "v", dt, dev, (B, T, H, dv))
-    _check(alpha, "alpha", torch.float32, dev, (B, T, H, dk))
+    _check_alpha(alpha, KDA_GATE_CHANNEL if gate is None else gate, (B, T, H), dk, dev)
     _check(beta, "beta", torch.float32, dev, (B, T, H))
     num_seqs = 0
     cu_dev = None
@@ -164,13 +213,20 @@ def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
         ws_bytes = workspace.numel()
     else:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                           _ptr(initial_state), _ptr(o), _ptr(final_state),
-                           B, T, H, dk, dv, code, _ptr(cu_dev), cu_host_arr, num_seqs,
-                           float(scale) if scale is not None else 0.0, int(chunk_size),
-                           _ptr(ws), ws_bytes, _stream(dev))
+    common = (float(scale) if scale is not None else 0.0, int(chunk_size), _ptr(ws), ws_bytes,
+              _stream(dev))
+    if gate is None:
+        st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(initial_state), _ptr(o), _ptr(final_state),
+                               B, T, H, dk, dv, code, _ptr(cu_dev), cu_host_arr, num_seqs,
+                               *common)
+    else:
+        st = lib.kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                     B, T, H, dk, dv, code, gate, _ptr(cu_dev), cu_host_arr,
+                                     num_seqs, *common)
     if st != 0:
-        raise KDAError(st, "kda_chunk_fwd")
+        raise KDAError(st, "kda_chunk_fwd" if gate is None else "kda_chunk_fwd_gated")
     return o, final_state
 
 
@@ -178,6 +234,16 @@ def kda_recurrent_step(q, k, v, alpha, beta, state, scale=None, o=None):
     """One decode step; ``state`` [N, H, dk, dv] fp32 is updated in place.
     q, k: [N, H, dk]; v: [N, H, dv]; alpha: [N, H, dk] fp32; beta: [N, H] fp32.
     Returns o [N, H, dv]."""
+    return _recurrent_step(q, k, v, alpha, beta, state, scale, o, None)
+
+
+def kda_recurrent_step_gated(q, k, v, alpha, beta, state, scale=None, o=None, gate="channel"):
+    """kda_recurrent_step with the forget gate's granularity chosen by ``gate``:
+    "channel" (alpha [N, H, dk]), "head" (alpha [N, H]) or "none" (alpha None)."""
+    return _recurrent_step(q, k, v, alpha, beta, state, scale, o, _gate_code(gate))
+
+
+def _recurrent_step(q, k, v, alpha, beta, state, scale, o, gate):
     lib = load_library()
     dev = q.device
     dt = q.dtype
@@ -187,16 +253,21 @@ def kda_recurrent_step(q, k, v, alpha, beta, state, scale=None, o=None):
     _check(q, "q", dt, dev)
     _check(k, "k", dt, dev, (N, H, dk))
     _check(v, "v", dt, dev, (N, H, dv))
-    _check(alpha, "alpha", torch.float32, dev, (N, H, dk))
+    _check_alpha(alpha, KDA_GATE_CHANNEL if gate is None else gate, (N, H), dk, dev)
     _check(beta, "beta", torch.float32, dev, (N, H))
     _check(state, "state", torch.float32, dev, (N, H, dk, dv))
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _check(o, "o", dt, dev, (N, H, dv))
-    st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
-                                _ptr(o), N, H, dk, dv, code,
-                                float(scale) if scale is not None else 0.0, _stream(dev))
+    sc = float(scale) if scale is not None else 0.0
+    if gate is None:
+        st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(state), _ptr(o), N, H, dk, dv, code, sc, _stream(dev))
+    else:
+        st = lib.kda_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                          _ptr(state), _ptr(o), N, H, dk, dv, code, gate, sc,
+                                          _stream(dev))
     if st != 0:
-        raise KDAError(st, "kda_recurrent_step")
+        raise KDAError(st, "kda_recurrent_step" if gate is None else "kda_recurrent_step_gated")
     return o

@@ -19,6 +19,7 @@ struct KParams {
     const int *cu_seqlens;
     const int *order;
     int B, T, H, dv, units, njt_all;
+    int gate;  // 0: alpha per key channel, 1: per head (Gated DeltaNet), 2: none (alpha = 1)
     float scale;
 };
 

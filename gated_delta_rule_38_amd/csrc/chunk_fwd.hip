@@ -111,6 +111,7 @@ template <> struct RawRow<bf16_t, 2> {
 template <> struct RawRow<float, 1> {
     typedef float T;
     static __device__ __forceinline__ T ld(const float* p) { return *p; }
+    static __device__ __forceinline__ T splat(float a) { return a; }
     static __device__ __forceinline__ void unpack(T w, float* x) { x[0] = w; }
 };
 template <> struct RawRow<float, 2> {
@@ -118,6 +119,7 @@ template <> struct RawRow<float, 2> {
     static __device__ __forceinline__ T ld(const float* p) {
         return *reinterpret_cast<const float2*>(p);
     }
+    static __device__ __forceinline__ T splat(float a) { return make_float2(a, a); }
     static __device__ __forceinline__ void unpack(T w, float* x) { x[0] = w.x; x[1] = w.y; }
 };
 
@@ -176,6 +178,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
     const Tin* __restrict__ gv = static_cast<const Tin*>(p.v);
     const float* __restrict__ ga = p.alpha;
     const float* __restrict__ gb = p.beta;
+    const int gate = p.gate;
     Tin* __restrict__ go = static_cast<Tin*>(p.o);
 
     const int tid = threadIdx.x;
@@ -225,7 +228,11 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
             const size_t off = ((size_t)(t0 + t) * H + h) * DK + c0;
             pq[r] = RQ::ld(gq + off);
             pk[r] = RQ::ld(gk + off);
-            pa[r] = RA::ld(ga + off);
+            if (gate == 0) {
+                pa[r] = RA::ld(ga + off);
+            } else {  // one decay for every channel of the token, or none
+                pa[r] = RA::splat(gate == 1 ? ga[(size_t)(t0 + t) * H + h] : 1.f);
+            }
         }
         if (w == 0) pbeta = gb[(size_t)(t0 + min(ch * CH + l, len - 1)) * H + h];
     };
@@ -575,6 +582,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const int* order, hipStream
     p.B = a.B; p.T = a.T; p.H = a.H; p.dv = a.dv;
     p.units = nseq * a.H;
     p.njt_all = a.dv / DVT;
+    p.gate = a.gate;
     p.scale = a.scale;
     const int groups = (p.units + 7) / 8;
     const long grid = 8L * p.njt_all * groups;
@@ -634,6 +642,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
         p.B = a.B; p.T = a.T; p.H = a.H; p.dv = a.dv;
         p.units = units;
         p.njt_all = a.dv / dvt;
+        p.gate = a.gate;
         p.scale = a.scale;
         return launch_chunk_bf16(p, a.dk, dvt, stream);
     }

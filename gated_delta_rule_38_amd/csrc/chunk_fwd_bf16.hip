@@ -124,6 +124,7 @@ __device__ __forceinline__ float row_shr(float x, float old) {
 #define KDA_ARGS4(x) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])
 #define KDA_SEQ8(OP) OP(0) OP(1) OP(2) OP(3) OP(4) OP(5) OP(6) OP(7)
 #define KDA_SEQ4(OP) OP(0) OP(1) OP(2) OP(3)
+#define KDA_SEQ1(OP) OP(0)
 // x[i] *= x[i] of lane l - 4 (row_shr) or l - 4 mod 16 (row_ror) inside the
 // lane's 16-lane row; with row_shr the first lanes of a row, which have no
 // source, keep x[i]
@@ -133,6 +134,9 @@ __device__ __forceinline__ float row_shr(float x, float old) {
     }                                                                                           \
     __device__ __forceinline__ void NAME(float (&x)[4]) {                                       \
         asm volatile("s_nop 1\n\t" KDA_SEQ4(KDA_MUL_DPP_I_##NAME) : KDA_ARGS4(x));              \
+    }                                                                                           \
+    __device__ __forceinline__ void NAME(float (&x)[1]) {                                       \
+        asm volatile("s_nop 1\n\t" KDA_SEQ1(KDA_MUL_DPP_I_##NAME) : "+v"(x[0]));                \
     }
 #define KDA_MUL_DPP_I_mul_row_shr4(i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
 #define KDA_MUL_DPP_I_mul_row_shr8(i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
@@ -163,6 +167,12 @@ __device__ __forceinline__ void ror4_mul_into(float (&z)[4], const float (&x)[4]
                  : "=&v"(z[0]), "=&v"(z[1]), "=&v"(z[2]), "=&v"(z[3])
                  : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
 }
+__device__ __forceinline__ void ror4_mul_into(float (&z)[1], const float (&x)[1]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_mul_f32_dpp %0, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf"
+                 : "=&v"(z[0])
+                 : "v"(x[0]));
+}
 // f[i] *= w[i] of lane l - 4 inside the row; the first four lanes of a row
 // keep f[i]
 __device__ __forceinline__ void mul_shr4_from(float (&f)[8], const float (&w)[8]) {
@@ -186,6 +196,12 @@ __device__ __forceinline__ void mul_shr4_from(float (&f)[4], const float (&w)[4]
                  "v_mul_f32_dpp %3, %7, %3 row_shr:4 row_mask:0xf bank_mask:0xf"
                  : KDA_ARGS4(f)
                  : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
+}
+__device__ __forceinline__ void mul_shr4_from(float (&f)[1], const float (&w)[1]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_mul_f32_dpp %0, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf"
+                 : "+v"(f[0])
+                 : "v"(w[0]));
 }
 // exchange between 16-lane rows: (a, b) -> ([a0 b0 a2 b2], [a1 b1 a3 b3]) by
 // rows, for each pair (a[i], b[i]); the trailing s_nop keeps the results two
@@ -212,12 +228,19 @@ __device__ __forceinline__ void swap_rows16(float (&a)[4], float (&b)[4]) {
                  "s_nop 1"
                  : KDA_ARGS4(a), KDA_ARGS4(b));
 }
+__device__ __forceinline__ void swap_rows16(float (&a)[1], float (&b)[1]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_permlane16_swap_b32 %0, %1\n\t"
+                 "s_nop 1"
+                 : "+v"(a[0]), "+v"(b[0]));
+}
 #undef KDA_MUL_DPP
 #undef KDA_MUL_DPP_I_mul_row_shr4
 #undef KDA_MUL_DPP_I_mul_row_shr8
 #undef KDA_MUL_DPP_I_mul_row_ror8
 #undef KDA_SEQ8
 #undef KDA_SEQ4
+#undef KDA_SEQ1
 #undef KDA_ARGS8
 #undef KDA_ARGS4
 // y in the 16-lane rows selected by ROWS (bit r = lanes 16r..16r+15), x elsewhere
@@ -261,7 +284,9 @@ struct Lay6 {
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int DVT>
+// GATE: 0 = alpha per key channel (KDA), 1 = one alpha per token and head
+// (Gated DeltaNet), 2 = no gate (DeltaNet, alpha = 1)
+template <int DK, int DVT, int GATE>
 __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel(KParams p) {
     using L = Lay6<DK, DVT>;
     using Mf = Mma<bf16_t>;
@@ -370,16 +395,18 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         // one channel group spread over rows would cost one access per lane);
         // 16-lane row r then holds tokens 16r..16r+15.
         const int pw = w - NJT;
+        // decays per lane and row: one per channel, or one for the token
+        constexpr int NA = GATE == 0 ? CPL : 1;
         // registers carried across chunks: two sets of raw q, k, alpha rows
         // (chunks of even and odd index, loaded three chunks ahead) and the
         // Kc^T pairs of the chunk whose operands were built last
-        struct Raw { uint32_t q[2 * CPL], k[2 * CPL], a[4 * CPL]; };
+        struct Raw { uint32_t q[2 * CPL], k[2 * CPL], a[4 * NA]; };
         Raw R0, R1;
         uint32_t RT[2 * CPL];
 #pragma unroll
         for (int i = 0; i < 2 * CPL; ++i) { R0.q[i] = R0.k[i] = R1.q[i] = R1.k[i] = 0u; RT[i] = 0u; }
 #pragma unroll
-        for (int i = 0; i < 4 * CPL; ++i) R0.a[i] = R1.a[i] = 0u;
+        for (int i = 0; i < 4 * NA; ++i) R0.a[i] = R1.a[i] = 0u;
 
         // descriptors and lane offsets of the raw q, k, alpha rows of chunk ch
         struct Src { Rsrc rq, rk, ra; uint32_t qo, ao; };
@@ -395,9 +422,14 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             Src sr;
             sr.rq = make_rsrc(gq + e0, (uint32_t)nr * rsq);
             sr.rk = make_rsrc(gk + e0, (uint32_t)nr * rsq);
-            sr.ra = make_rsrc(ga + e0, (uint32_t)nr * rsa);
             sr.qo = (uint32_t)pr0 * rsq + (uint32_t)pc0 * 2;
-            sr.ao = (uint32_t)pr0 * rsa + (uint32_t)pc0 * 4;
+            if constexpr (GATE == 0) {
+                sr.ra = make_rsrc(ga + e0, (uint32_t)nr * rsa);
+                sr.ao = (uint32_t)pr0 * rsa + (uint32_t)pc0 * 4;
+            } else {  // alpha [token][head]; unused without a gate
+                sr.ra = make_rsrc(GATE == 1 ? ga + e0 / DK : ga, GATE == 1 ? (uint32_t)nr * rsb : 0u);
+                sr.ao = (uint32_t)pr0 * rsb;
+            }
             return sr;
         };
         auto ld_qk = [&](const Src& sr, Raw& R, int rr) {  // q and k of the lane's row rr
@@ -414,11 +446,15 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             }
         };
         auto ld_a = [&](const Src& sr, Raw& R, int rr) {  // alpha of the lane's row rr
+            if constexpr (GATE == 0) {
 #pragma unroll
-            for (int j = 0; j < CPL / 4; ++j) {
-                const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr.ra, sr.ao + rr * rsa + 16 * j, 0, 0);
+                for (int j = 0; j < CPL / 4; ++j) {
+                    const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr.ra, sr.ao + rr * rsa + 16 * j, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) R.a[CPL * rr + 4 * j + i] = a4[i];
+                    for (int i = 0; i < 4; ++i) R.a[CPL * rr + 4 * j + i] = a4[i];
+                }
+            } else if constexpr (GATE == 1) {
+                R.a[rr] = __builtin_amdgcn_raw_buffer_load_b32(sr.ra, sr.ao + rr * rsb, 0, 0);
             }
         };
         auto p_load = [&](int ch, Raw& R) {  // raw q, k, alpha rows of chunk ch
@@ -448,79 +484,106 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const int pc0 = pw * (DK / 4) + (lx & 3) * CPL, pr0 = rg * 4;
             const int par = ch & 1;
             const int nval = len - ch * CH;
-            if (nval < CH) {  // alpha of rows past the end of the sequence is 1
+            bf16_t* kr_b = reinterpret_cast<bf16_t*>(buf(par, L::bKr));
+            bf16_t* qr_b = reinterpret_cast<bf16_t*>(buf(par, L::bQr));
+            // decays: f (P through row pr0 - 1, over Pm), g (Pm / P through row
+            // pr0 + 3), the running products pr over the lane's rows, and u (Pm
+            // in 16-lane row 0, Pn / Pm in row 3); index ai(c) for channel c
+            auto ai = [](int c) { return GATE == 0 ? c : 0; };
+            float pr[4][NA], f[NA], g[NA], u[NA];
+            if constexpr (GATE == 2) {
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    if (pr0 + rr >= nval)
+                for (int c = 0; c < NA; ++c) {
+                    f[c] = g[c] = u[c] = 1.f;
 #pragma unroll
-                        for (int c = 0; c < CPL; ++c) RA[CPL * rr + c] = __float_as_uint(1.f);
+                    for (int rr = 0; rr < 4; ++rr) pr[rr][c] = 1.f;
+                }
+            } else {
+                if (nval < CH) {  // alpha of rows past the end of the sequence is 1
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        if (pr0 + rr >= nval)
+#pragma unroll
+                            for (int c = 0; c < NA; ++c) RA[NA * rr + c] = __float_as_uint(1.f);
+                }
+                float inc[NA];
+#pragma unroll
+                for (int c = 0; c < NA; ++c) {
+                    float run = ra_f(c);
+                    pr[0][c] = run;
+#pragma unroll
+                    for (int rr = 1; rr < 4; ++rr) { run *= ra_f(NA * rr + c); pr[rr][c] = run; }
+                    inc[c] = run;
+                }
+                ld_a(sr, R, 0);  // alpha of row 0 is used up
+                __builtin_amdgcn_sched_barrier(0);  // keep each batch of loads where it is issued
+                // Products over the chunk's tokens, per channel.  w: over the
+                // lane's 16-lane row through its last token (tokens 16r..pr0+3);
+                // z: over the whole row (tokens 16r..16r+15), in every lane.
+                float w[NA], z[NA];
+#pragma unroll
+                for (int c = 0; c < NA; ++c) w[c] = inc[c];
+                mul_row_shr4(w);
+                mul_row_shr8(w);
+                ror4_mul_into(z, inc);
+                mul_row_ror8(z);
+                // With row totals z0..z3, Pm = z0 z1 and P_t / Pm = w_t F where F
+                // is 1/(z0 z1), 1/z1, 1 and z2 in rows 0..3.  The row exchange
+                // gives a = (z0, z0, z2, z2) and b = (z1, z1, z3, z3) by row; with
+                // t = (z0, 1, 1, z2), u = t b is Pm in row 0 and Pn / Pm in row 3.
+                float a[NA];
+#pragma unroll
+                for (int c = 0; c < NA; ++c) a[c] = z[c];
+                swap_rows16(a, z);  // z now holds b
+#pragma unroll
+                for (int c = 0; c < NA; ++c) {
+                    const float t = rows_sel<0x6>(a[c], 1.f);
+                    u[c] = t * z[c];
+                    f[c] = rows_sel<0xC>(fast_rcp(u[c]), t);  // F
+                    g[c] = fast_rcp(w[c] * f[c]);            // Pm / P through row pr0 + 3
+                }
+                mul_shr4_from(f, w);  // P through row pr0 - 1, over Pm
             }
-            float pr[4][CPL];  // running product over the lane's rows
-            float inc[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                float run = ra_f(c);
-                pr[0][c] = run;
-#pragma unroll
-                for (int rr = 1; rr < 4; ++rr) { run *= ra_f(CPL * rr + c); pr[rr][c] = run; }
-                inc[c] = run;
-            }
-            ld_a(sr, R, 0);  // alpha of row 0 is used up
-            __builtin_amdgcn_sched_barrier(0);  // keep each batch of loads where it is issued
-            // Products over the chunk's tokens, per channel.  w: over the
-            // lane's 16-lane row through its last token (tokens 16r..pr0+3);
-            // z: over the whole row (tokens 16r..16r+15), in every lane.
-            float w[CPL], z[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) w[c] = inc[c];
-            mul_row_shr4(w);
-            mul_row_shr8(w);
-            ror4_mul_into(z, inc);
-            mul_row_ror8(z);
-            // With row totals z0..z3, Pm = z0 z1 and P_t / Pm = w_t F where F
-            // is 1/(z0 z1), 1/z1, 1 and z2 in rows 0..3.  The row exchange
-            // gives a = (z0, z0, z2, z2) and b = (z1, z1, z3, z3) by row; with
-            // t = (z0, 1, 1, z2), u = t b is Pm in row 0 and Pn / Pm in row 3.
-            float a[CPL], u[CPL], f[CPL], g[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) a[c] = z[c];
-            swap_rows16(a, z);  // z now holds b
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const float t = rows_sel<0x6>(a[c], 1.f);
-                u[c] = t * z[c];
-                f[c] = rows_sel<0xC>(fast_rcp(u[c]), t);  // F
-                g[c] = fast_rcp(w[c] * f[c]);            // Pm / P through row pr0 + 3
-            }
-            mul_shr4_from(f, w);  // P through row pr0 - 1, over Pm
             // Pm from the first lanes of row 0, Pn / Pm from the first lanes of
             // row 3; the helper forms Pn from the two
             if (rg == 0 || rg == 12) {
                 float* vec = reinterpret_cast<float*>(buf(par, L::bVec)) + (rg == 0 ? 0 : 2 * DK);
 #pragma unroll
                 for (int c = 0; c < CPL; c += 4)
-                    *reinterpret_cast<float4*>(vec + pc0 + c) = make_float4(u[c], u[c + 1], u[c + 2], u[c + 3]);
+                    *reinterpret_cast<float4*>(vec + pc0 + c) =
+                        make_float4(u[ai(c)], u[ai(c + 1)], u[ai(c + 2)], u[ai(c + 3)]);
             }
-            bf16_t* kr_b = reinterpret_cast<bf16_t*>(buf(par, L::bKr));
-            bf16_t* qr_b = reinterpret_cast<bf16_t*>(buf(par, L::bQr));
             // rows from the last to the first: g_r = Pm / P_r = g_{r+1} * alpha_{r+1}
             uint32_t kcp[CPL / 2];  // Kc of row rr + 1 (the odd row of the current pair)
 #pragma unroll
             for (int rr = 3; rr >= 0; --rr) {
                 uint32_t kr[CPL / 2], qr[CPL / 2], kc[CPL / 2];
+                if constexpr (GATE == 1) {
+                    if (rr < 3) g[0] *= ra_f(rr + 1);
+                }
+                const float rrow = pr[rr][0] * f[0];  // P_r / Pm of a token-wide decay
 #pragma unroll
                 for (int i = 0; i < CPL / 2; ++i) {
                     const uint32_t kw = RK[(CPL / 2) * rr + i], qw = RQ[(CPL / 2) * rr + i];
                     const int c0 = 2 * i, c1 = 2 * i + 1;
-                    if (rr < 3) {
-                        g[c0] *= ra_f(CPL * (rr + 1) + c0);
-                        g[c1] *= ra_f(CPL * (rr + 1) + c1);
+                    if constexpr (GATE == 2) {  // no decay: the stored values as they are
+                        kr[i] = kw;
+                        qr[i] = qw;
+                        kc[i] = kw;
+                    } else {
+                        if constexpr (GATE == 0) {
+                            if (rr < 3) {
+                                g[c0] *= ra_f(CPL * (rr + 1) + c0);
+                                g[c1] *= ra_f(CPL * (rr + 1) + c1);
+                            }
+                        }
+                        const float r0 = GATE == 0 ? pr[rr][c0] * f[c0] : rrow;
+                        const float r1 = GATE == 0 ? pr[rr][c1] * f[c1] : rrow;
+                        const float k0 = lo_f(kw), k1 = hi_f(kw);
+                        kr[i] = pack2(k0 * r0, k1 * r1);
+                        qr[i] = pack2(lo_f(qw) * r0, hi_f(qw) * r1);
+                        kc[i] = pack2(k0 * g[ai(c0)], k1 * g[ai(c1)]);
                     }
-                    const float r0 = pr[rr][c0] * f[c0], r1 = pr[rr][c1] * f[c1];
-                    const float k0 = lo_f(kw), k1 = hi_f(kw);
-                    kr[i] = pack2(k0 * r0, k1 * r1);
-                    qr[i] = pack2(lo_f(qw) * r0, hi_f(qw) * r1);
-                    kc[i] = pack2(k0 * g[c0], k1 * g[c1]);
                     if (rr & 1) {
                         kcp[i] = kc[i];
                     } else {  // Kc^T pairs of channels c0, c1: rows (rr, rr + 1)
@@ -700,11 +763,18 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const uint32_t row = (uint32_t)(jt * (CH / njt) + lx / njt), sub = (uint32_t)(lx % njt);
             const Rsrc rq = make_rsrc(gq + tok * DK, (uint32_t)nr * rsq);
             const Rsrc rk = make_rsrc(gk + tok * DK, (uint32_t)nr * rsq);
-            const Rsrc ra = make_rsrc(ga + tok * DK, (uint32_t)nr * rsa);
             const Rsrc rv = make_rsrc(gv + tok * DV, (uint32_t)nr * rsv);
             r[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, row * rsq + (sub & 1) * 128, 0, 0);
             r[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, row * rsq + (sub & 1) * 128, 0, 0);
-            r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsa + (sub & 3) * 128, 0, 0);
+            if constexpr (GATE == 0) {
+                const Rsrc ra = make_rsrc(ga + tok * DK, (uint32_t)nr * rsa);
+                r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsa + (sub & 3) * 128, 0, 0);
+            } else if constexpr (GATE == 1) {
+                const Rsrc ra = make_rsrc(ga + tok, (uint32_t)nr * rsb);
+                r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsb, 0, 0);
+            } else {
+                r[2] = 0u;
+            }
             r[3] = __builtin_amdgcn_raw_buffer_load_b32(rv, row * rsv + (sub & 1) * 128, 0, 0);
         };
         __syncthreads();
@@ -921,17 +991,23 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     }
 }
 
-template <int DK, int DVT>
-static hipError_t launch_t(const KParams& p, hipStream_t stream) {
+template <int DK, int DVT, int GATE>
+static hipError_t launch_g(const KParams& p, hipStream_t stream) {
     using Lay = Lay6<DK, DVT>;
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)chunk_fwd_bf16_kernel<DK, DVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)Lay::bytes);
+        (const void*)chunk_fwd_bf16_kernel<DK, DVT, GATE>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
     const long grid = 8L * p.njt_all * ((p.units + 7) / 8);
-    hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVT>), dim3((unsigned)grid), dim3(Lay::NTH),
-                       Lay::bytes, stream, p);
+    hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVT, GATE>), dim3((unsigned)grid),
+                       dim3(Lay::NTH), Lay::bytes, stream, p);
     return hipGetLastError();
+}
+
+template <int DK, int DVT>
+static hipError_t launch_t(const KParams& p, hipStream_t stream) {
+    return p.gate == 0 ? launch_g<DK, DVT, 0>(p, stream)
+         : p.gate == 1 ? launch_g<DK, DVT, 1>(p, stream) : launch_g<DK, DVT, 2>(p, stream);
 }
 
 // value-column tile widths this kernel supports

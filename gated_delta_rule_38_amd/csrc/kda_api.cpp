@@ -53,6 +53,15 @@ float default_scale(float scale, int dk) {
     return 1.0f / sqrtf((float)dk);
 }
 
+bool valid_gate(int gate) {
+    return gate == KDA_GATE_CHANNEL || gate == KDA_GATE_HEAD || gate == KDA_GATE_NONE;
+}
+
+// alpha values per token and head for a gate
+size_t gate_width(int gate, int dk) {
+    return gate == KDA_GATE_CHANNEL ? (size_t)dk : gate == KDA_GATE_HEAD ? 1 : 0;
+}
+
 bool env_generic() {
     const char* s = getenv("KDA_CHUNK_GENERIC");
     return s && s[0] == '1';
@@ -64,6 +73,18 @@ int env_dvt() {
     int v = atoi(s);
     return (v == 16 || v == 32 || v == 64) ? v : 0;
 }
+
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
+                          const float* beta, const float* initial_state, void* o,
+                          float* final_state, int B, int T, int H, int dk, int dv,
+                          kda_dtype dtype, int gate, const int* cu_seqlens_dev,
+                          const int* cu_seqlens_host, int num_seqs, float scale,
+                          int chunk_size, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, float* state, void* o, int N, int H, int dk,
+                               int dv, kda_dtype dtype, int gate, float scale,
+                               hipStream_t stream);
 
 }  // namespace
 
@@ -99,8 +120,53 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          const int* cu_seqlens_host, int num_seqs, float scale,
                          int chunk_size, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, alpha, beta, initial_state, o, final_state, B, T, H, dk, dv,
+                          dtype, KDA_GATE_CHANNEL, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                          scale, chunk_size, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* initial_state, void* o,
+                               float* final_state, int B, int T, int H, int dk, int dv,
+                               kda_dtype dtype, kda_gate gate, const int* cu_seqlens_dev,
+                               const int* cu_seqlens_host, int num_seqs, float scale,
+                               int chunk_size, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, alpha, beta, initial_state, o, final_state, B, T, H, dk, dv,
+                          dtype, (int)gate, cu_seqlens_dev, cu_seqlens_host, num_seqs, scale,
+                          chunk_size, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, float* state, void* o, int N, int H, int dk,
+                              int dv, kda_dtype dtype, float scale, hipStream_t stream) {
+    return recurrent_step_impl(q, k, v, alpha, beta, state, o, N, H, dk, dv, dtype,
+                               KDA_GATE_CHANNEL, scale, stream);
+}
+
+kda_status kda_recurrent_step_gated(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, float* state,
+                                    void* o, int N, int H, int dk, int dv, kda_dtype dtype,
+                                    kda_gate gate, float scale, hipStream_t stream) {
+    return recurrent_step_impl(q, k, v, alpha, beta, state, o, N, H, dk, dv, dtype, (int)gate,
+                               scale, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
+                          const float* beta, const float* initial_state, void* o,
+                          float* final_state, int B, int T, int H, int dk, int dv,
+                          kda_dtype dtype, int gate, const int* cu_seqlens_dev,
+                          const int* cu_seqlens_host, int num_seqs, float scale,
+                          int chunk_size, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
     try {
         if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
+        if (!valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
+        if (gate == KDA_GATE_NONE && alpha) return KDA_ERROR_INVALID_VALUE;
         if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return KDA_ERROR_INVALID_VALUE;
         if (chunk_size != kChunk) return KDA_ERROR_NOT_SUPPORTED;
         if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
@@ -120,7 +186,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
         }
         size_t b_qk, b_v, b_a, b_b, b_s;
         if (!bytes_of(B, T, H, dk, es, &b_qk) || !bytes_of(B, T, H, dv, es, &b_v) ||
-            !bytes_of(B, T, H, dk, 4, &b_a) || !bytes_of(B, T, H, 1, 4, &b_b) ||
+            !bytes_of(B, T, H, gate_width(gate, dk), 4, &b_a) || !bytes_of(B, T, H, 1, 4, &b_b) ||
             !bytes_of(nstates, H, dk, dv, 4, &b_s))
             return KDA_ERROR_INVALID_VALUE;
         // grid and index limits of the kernels
@@ -129,12 +195,13 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
         const size_t tokens = (size_t)B * T * H;
         const size_t units = (size_t)nstates * H;
-        if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !o))
+        if (tokens > 0 && (!q || !k || !v || !beta || !o || (gate != KDA_GATE_NONE && !alpha)))
             return KDA_ERROR_INVALID_VALUE;
-        // q, k, alpha are read in pairs; the rest element by element
-        const void* pairs[] = {q, k, alpha};
+        // q, k and a per-channel alpha are read in pairs; the rest element by element
+        const void* pairs[] = {q, k, gate == KDA_GATE_CHANNEL ? alpha : nullptr};
         for (const void* ptr : pairs)
             if (!aligned(ptr, 8)) return KDA_ERROR_MISALIGNED;
+        if (!aligned(alpha, 4)) return KDA_ERROR_MISALIGNED;
         if (!aligned(v, es) || !aligned(o, es)) return KDA_ERROR_MISALIGNED;
         const void* words[] = {beta, initial_state, final_state, workspace};
         for (const void* ptr : words)
@@ -170,6 +237,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
         a.s0 = initial_state; a.o = o; a.sT = final_state;
         a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
         a.bf16 = dtype == KDA_DTYPE_BF16;
+        a.gate = gate;
         a.cu_seqlens = varlen ? cu_seqlens_dev : nullptr;
         a.num_seqs = varlen ? num_seqs : 0;
         a.order = (varlen && num_seqs <= 65536) ? static_cast<int*>(workspace) : nullptr;
@@ -182,17 +250,21 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     }
 }
 
-kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
-                              const float* beta, float* state, void* o, int N, int H, int dk,
-                              int dv, kda_dtype dtype, float scale, hipStream_t stream) {
+kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, float* state, void* o, int N, int H, int dk,
+                               int dv, kda_dtype dtype, int gate, float scale,
+                               hipStream_t stream) {
     try {
         if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
+        if (!valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
+        if (gate == KDA_GATE_NONE && alpha) return KDA_ERROR_INVALID_VALUE;
         if (N < 0 || H < 0) return KDA_ERROR_INVALID_VALUE;
         if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
         if ((long long)N * H > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
         const size_t units = (size_t)N * H;
         if (units == 0) return KDA_SUCCESS;
-        if (!q || !k || !v || !alpha || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+        if (!q || !k || !v || !beta || !state || !o || (gate != KDA_GATE_NONE && !alpha))
+            return KDA_ERROR_INVALID_VALUE;
         const size_t es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
         // the state is streamed as float4; everything else element by element
         if (!aligned(state, 16)) return KDA_ERROR_MISALIGNED;
@@ -202,7 +274,8 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
         const Range r_s = range_of(state, units * dk * dv * 4);
         const Range r_o = range_of(o, units * dv * es);
         const Range ins[] = {range_of(q, units * dk * es), range_of(k, units * dk * es),
-                             range_of(v, units * dv * es), range_of(alpha, units * dk * 4),
+                             range_of(v, units * dv * es),
+                             range_of(alpha, units * gate_width(gate, dk) * 4),
                              range_of(beta, units * 4)};
         for (const Range& r : ins)
             if (overlap(r_s, r) || overlap(r_o, r)) return KDA_ERROR_INVALID_VALUE;
@@ -212,6 +285,7 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
         a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.o = o;
         a.N = N; a.H = H; a.dk = dk; a.dv = dv;
         a.bf16 = dtype == KDA_DTYPE_BF16;
+        a.gate = gate;
         a.scale = default_scale(scale, dk);
         return kda::launch_recurrent_step(a, stream) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
     } catch (...) {
@@ -219,4 +293,4 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     }
 }
 
-}  // extern "C"
+}  // namespace

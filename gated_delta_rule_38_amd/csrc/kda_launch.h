@@ -15,6 +15,7 @@ struct StepArgs {
     void *o;
     int N, H, dk, dv;
     bool bf16;
+    int gate;  // kda_gate: 0 per channel, 1 per head, 2 none
     float scale;
 };
 
@@ -28,6 +29,7 @@ struct ChunkArgs {
     float *sT;
     int B, T, H, dk, dv;
     bool bf16;
+    int gate;               // kda_gate: 0 per channel, 1 per head, 2 none
     const int *cu_seqlens;  // device, NULL in dense mode
     int num_seqs;           // 0 in dense mode
     int *order;             // device workspace for the longest-first order (varlen), or NULL

@@ -29,7 +29,7 @@ template <typename Tin, int DK, int DV>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ state,
-    Tin* __restrict__ o, float scale) {
+    Tin* __restrict__ o, float scale, int gate) {
     constexpr int NCG = DV / 4;      // float4 column groups
     constexpr int NRG = 256 / NCG;   // row groups
     constexpr int RPG = DK / NRG;    // rows per thread
@@ -51,10 +51,12 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     for (int r = 0; r < RPG; ++r)
         s[r] = *reinterpret_cast<const float4*>(S + (size_t)(row0 + r) * DV + cg * 4);
 
+    // the forget gate: per key channel, one per (sequence, head), or none
     float a[RPG], kk[RPG], qq[RPG];
+    const float ah = gate == 1 ? alpha[unit] : 1.f;
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
-        a[r] = alpha[(size_t)unit * DK + row0 + r];
+        a[r] = gate == 0 ? alpha[(size_t)unit * DK + row0 + r] : ah;
         kk[r] = to_f32(k[(size_t)unit * DK + row0 + r]);
         qq[r] = to_f32(q[(size_t)unit * DK + row0 + r]);
     }
@@ -121,7 +123,7 @@ static hipError_t launch_step_t(const StepArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((recurrent_step_kernel<Tin, DK, DV>), dim3(units), dim3(256), 0, stream,
                        static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                        static_cast<const Tin*>(a.v), a.alpha, a.beta, a.state,
-                       static_cast<Tin*>(a.o), a.scale);
+                       static_cast<Tin*>(a.o), a.scale, a.gate);
     return hipGetLastError();
 }
 

@@ -65,6 +65,24 @@ typedef enum {
 } kda_dtype;
 
 /*
+ * Granularity of the forget gate alpha (the *_gated entry points).
+ * KDA_GATE_CHANNEL: one decay per token, head and key channel, Diag(alpha_t)
+ *   ("Kimi Delta Attention", section "一、Diag(α_t)：通道级遗忘").
+ * KDA_GATE_HEAD: one decay per token and head, alpha_t S_{t-1} for the whole
+ *   state: Gated DeltaNet (bugfactory.tech news 3610, third paragraph; the
+ *   per-head scalar rows of the table in the same section of "Kimi Delta
+ *   Attention").  Equal to KDA_GATE_CHANNEL with alpha_t repeated over the
+ *   dk channels.
+ * KDA_GATE_NONE: no forget gate, alpha = 1: DeltaNet (bugfactory.tech news
+ *   3610, second paragraph).  alpha must be NULL.
+ */
+typedef enum {
+    KDA_GATE_CHANNEL = 0, /* alpha [.., H, dk] float32 */
+    KDA_GATE_HEAD = 1,    /* alpha [.., H] float32 */
+    KDA_GATE_NONE = 2     /* alpha == NULL */
+} kda_gate;
+
+/*
  * Device workspace (bytes) that kda_chunk_fwd needs.  Dense calls
  * (num_seqs == 0) need none; packed variable-length calls need 4 bytes per
  * sequence (rounded up to 256), used to order sequences longest first.
@@ -109,6 +127,23 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          hipStream_t stream);
 
 /*
+ * kda_chunk_fwd with the forget gate's granularity chosen by `gate`: alpha is
+ * [B, T, H, dk] (KDA_GATE_CHANNEL, the same call as kda_chunk_fwd),
+ * [B, T, H] (KDA_GATE_HEAD) or NULL (KDA_GATE_NONE); a per-head alpha needs
+ * 4-byte alignment.  Every other argument, the layouts, the aliasing rules
+ * and the errors are those of kda_chunk_fwd; a gate outside the enum, or an
+ * alpha that is NULL where one is needed (or not NULL for KDA_GATE_NONE),
+ * returns KDA_ERROR_INVALID_VALUE.
+ */
+kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *alpha,
+                               const float *beta, const float *initial_state, void *o,
+                               float *final_state, int B, int T, int H, int dk, int dv,
+                               kda_dtype dtype, kda_gate gate, const int *cu_seqlens_dev,
+                               const int *cu_seqlens_host, int num_seqs, float scale,
+                               int chunk_size, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * One decode step, state updated in place.
  * Source: the fused recurrent mode of bugfactory.tech news 3610, fifth
  * paragraph (the sequence is processed token by token, state tiles updated
@@ -123,6 +158,18 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
 kda_status kda_recurrent_step(const void *q, const void *k, const void *v, const float *alpha,
                               const float *beta, float *state, void *o, int N, int H, int dk,
                               int dv, kda_dtype dtype, float scale, hipStream_t stream);
+
+/*
+ * kda_recurrent_step with the forget gate's granularity chosen by `gate`:
+ * alpha is [N, H, dk] (KDA_GATE_CHANNEL, the same call as
+ * kda_recurrent_step), [N, H] (KDA_GATE_HEAD) or NULL (KDA_GATE_NONE).
+ * Errors as for kda_recurrent_step, plus KDA_ERROR_INVALID_VALUE for a gate
+ * outside the enum or an alpha that does not match it.
+ */
+kda_status kda_recurrent_step_gated(const void *q, const void *k, const void *v,
+                                    const float *alpha, const float *beta, float *state,
+                                    void *o, int N, int H, int dk, int dv, kda_dtype dtype,
+                                    kda_gate gate, float scale, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *kda_status_string(kda_status status);

@@ -71,6 +71,27 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def channel_gate(alpha, gate, dk, lead=None):
+    """The per-channel decays a forget gate stands for, as float64 [..., dk].
+
+    gate "channel": alpha already holds one decay per key channel (KDA,
+    "Kimi Delta Attention", section "一、Diag(α_t)：通道级遗忘").
+    gate "head": one decay per token and head scales the whole state,
+    alpha_t S = Diag(alpha_t 1) S (Gated DeltaNet, bugfactory.tech news 3610,
+    third paragraph): the value is repeated over the dk channels.
+    gate "none": no forget gate (DeltaNet, the same page's second paragraph):
+    every decay is 1; ``lead`` gives the leading shape.
+    """
+    if gate == "channel":
+        return _f64(alpha)
+    if gate == "head":
+        a = _f64(alpha)
+        return np.ascontiguousarray(np.repeat(a[..., None], dk, axis=-1))
+    if gate == "none":
+        return np.ones(tuple(lead) + (dk,), np.float64)
+    raise ValueError("unknown gate %r" % (gate,))
+
+
 def forward_units(q, k, v, alpha, beta, initial_state=None, scale=None, threads=0,
                   want_o=True):
     """Token loop over independent units.

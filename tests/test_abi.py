@@ -31,8 +31,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["kda_chunk_fwd", "kda_recurrent_step", "kda_chunk_fwd_workspace_size",
-              "kda_status_string", "kda_version"]:
+    for n in ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_step",
+              "kda_recurrent_step_gated", "kda_chunk_fwd_workspace_size", "kda_status_string",
+              "kda_version"]:
         assert n in names, names
 
 
@@ -71,6 +72,20 @@ def chunk_call(lib, **kw):
                              a["sT"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"],
                              a["cu_dev"], a["cu_host"], a["num_seqs"], a["scale"], a["chunk"],
                              a["ws"], a["ws_bytes"], a["stream"])
+
+
+GATE_CHANNEL, GATE_HEAD, GATE_NONE = range(3)
+
+
+def chunk_gated_call(lib, gate, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), s0=fake(5), o=fake(6),
+             sT=fake(7), B=2, T=100, H=4, dk=128, dv=128, dt=1, cu_dev=None, cu_host=None,
+             num_seqs=0, scale=0.0, chunk=64, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"],
+                                   a["o"], a["sT"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                   a["dt"], gate, a["cu_dev"], a["cu_host"], a["num_seqs"],
+                                   a["scale"], a["chunk"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def step_call(lib, **kw):
@@ -164,6 +179,54 @@ def test_step_empty_is_a_noop(lib):
     assert step_call(lib, N=0) == SUCCESS
 
 
+def step_gated_call(lib, gate, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), state=fake(5),
+             o=fake(6), N=8, H=4, dk=128, dv=128, dt=1, scale=0.0, stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_step_gated(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                        a["state"], a["o"], a["N"], a["H"], a["dk"], a["dv"],
+                                        a["dt"], gate, a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("gate,kw,code", [
+    (3, {}, INVALID),                                   # not a gate
+    (-1, {}, INVALID),
+    (GATE_NONE, {}, INVALID),                           # alpha given without a gate
+    (GATE_HEAD, dict(alpha=None), INVALID),             # gate without alpha
+    (GATE_CHANNEL, dict(alpha=None), INVALID),
+    (GATE_HEAD, dict(alpha=fake(3, 2)), MISALIGNED),    # per-head alpha: 4-byte words
+    (GATE_CHANNEL, dict(alpha=fake(3, 4)), MISALIGNED),  # per-channel alpha: pairs
+    # a 4-byte aligned per-head alpha passes the alignment checks and the call
+    # then fails on the overlap below it
+    (GATE_HEAD, dict(alpha=fake(3, 4), sT=fake(6, 512)), INVALID),
+    (GATE_HEAD, dict(sT=fake(3, 256)), INVALID),        # final state inside alpha
+    (GATE_NONE, dict(alpha=None, dk=96), NOT_SUPPORTED),
+    (GATE_NONE, dict(alpha=None, o=None), INVALID),
+])
+def test_chunk_gated_rejects_before_any_hip_call(lib, gate, kw, code):
+    assert chunk_gated_call(lib, gate, **kw) == code
+
+
+def test_gated_empty_is_a_noop(lib):
+    for gate in (GATE_CHANNEL, GATE_HEAD):
+        assert chunk_gated_call(lib, gate, B=0) == SUCCESS
+        assert step_gated_call(lib, gate, N=0) == SUCCESS
+    assert chunk_gated_call(lib, GATE_NONE, alpha=None, H=0) == SUCCESS
+    assert step_gated_call(lib, GATE_NONE, alpha=None, N=0) == SUCCESS
+
+
+@pytest.mark.parametrize("gate,kw,code", [
+    (3, {}, INVALID),
+    (GATE_NONE, {}, INVALID),
+    (GATE_HEAD, dict(alpha=None), INVALID),
+    (GATE_HEAD, dict(alpha=fake(3, 2)), MISALIGNED),
+    (GATE_HEAD, dict(state=fake(3, 0)), INVALID),       # state aliasing alpha
+    (GATE_NONE, dict(alpha=None, state=fake(5, 8)), MISALIGNED),
+])
+def test_step_gated_rejects_before_any_hip_call(lib, gate, kw, code):
+    assert step_gated_call(lib, gate, **kw) == code
+
+
 def test_python_binding_checks_arguments():
     import torch
     import gated_delta_rule_38_amd as kda
@@ -172,3 +235,13 @@ def test_python_binding_checks_arguments():
         kda.kda_chunk_fwd(q.to(torch.float16), q, q, q, q[..., 0])
     with pytest.raises(ValueError):
         kda.kda_chunk_fwd(q, q[:, :2], q, q, q[..., 0])
+    b = q[..., 0].contiguous()
+    with pytest.raises(ValueError):  # a per-head alpha has no channel axis
+        kda.kda_chunk_fwd_gated(q, q, q, q, b, gate="head")
+    with pytest.raises(ValueError):  # no alpha without a gate
+        kda.kda_chunk_fwd_gated(q, q, q, b, b, gate="none")
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd_gated(q, q, q, b, b, gate="scalar")
+    s = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        kda.kda_recurrent_step_gated(q[0], q[0], q[0], q[0], b[0], s, gate="head")

@@ -276,3 +276,31 @@ def test_layouts_and_varlen_match_units():
     o1, st1 = oracle.step(q[:, 0], k[:, 0], v[:, 0], a[:, 0], b[:, 0], s0)
     of, sf = oracle.forward(q[:, :1], k[:, :1], v[:, :1], a[:, :1], b[:, :1], s0)
     assert np.array_equal(o1, of[:, 0]) and np.array_equal(st1, sf)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_head_and_no_gate_through_the_token_layout(seed):
+    """oracle.channel_gate in the library's [B, T, H] layout: a per-head gate
+    gives Gated DeltaNet and no gate gives DeltaNet, unit by unit, against the
+    matrix forms written separately in brute.py (bugfactory.tech news 3610,
+    second and third paragraphs)."""
+    rng = np.random.default_rng(10 + seed)
+    B, T, H, dk, dv = 2, 7, 3, 5, 4
+    q = unit(rng.standard_normal((B, T, H, dk)))
+    k = unit(rng.standard_normal((B, T, H, dk)))
+    v = rng.standard_normal((B, T, H, dv))
+    g = 1.0 / (1.0 + np.exp(-rng.normal(1.0, 1.0, (B, T, H))))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    s0 = 0.3 * rng.standard_normal((B, H, dk, dv))
+    o_g, s_g = oracle.forward(q, k, v, oracle.channel_gate(g, "head", dk), beta, s0, scale=0.6)
+    o_n, s_n = oracle.forward(q, k, v, oracle.channel_gate(None, "none", dk, (B, T, H)), beta,
+                              s0, scale=0.6)
+    for b in range(B):
+        for h in range(H):
+            args = (q[b, :, h], k[b, :, h], v[b, :, h], beta[b, :, h], s0[b, h], 0.6)
+            o_r, s_r = brute.deltanet_matrix_form(*args, gate=g[b, :, h])
+            assert rel(o_g[b, :, h], o_r) < TOL and rel(s_g[b, h], s_r) < TOL
+            o_r, s_r = brute.deltanet_matrix_form(*args)
+            assert rel(o_n[b, :, h], o_r) < TOL and rel(s_n[b, h], s_r) < TOL
+    with pytest.raises(ValueError):
+        oracle.channel_gate(g, "scalar", dk)

@@ -22,13 +22,25 @@ def _unit(x):
     return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
 
 
+def _alpha(lead, dk, gate, g, device, mu, sigma=1.0):
+    """Forget gates sigmoid(N(mu, sigma)): [*lead, dk] per channel, [*lead]
+    per head, None without a gate (nothing drawn)."""
+    if gate == "none":
+        return None
+    shape = tuple(lead) + ((dk,) if gate == "channel" else ())
+    if gate not in ("channel", "head"):
+        raise ValueError("unknown gate %r" % (gate,))
+    return torch.sigmoid(_normal(shape, g, device, mu, sigma)).to(torch.float32).contiguous()
+
+
 def draw_chunk(B, T, H, dk, dv, dtype="bf16", alpha_mu=4.0, alpha_sigma=1.0, s0_std=None,
-               num_states=None, seed=0, device="cpu", lengths=None):
+               num_states=None, seed=0, device="cpu", lengths=None, gate="channel"):
     """Draw one chunked-forward input set.
 
     Returns a dict with q, k [B,T,H,dk] and v [B,T,H,dv] in the storage dtype,
-    alpha [B,T,H,dk] and beta [B,T,H] in float32, initial_state
-    [num_states or B, H, dk, dv] float32 (or None), on ``device``.
+    alpha [B,T,H,dk] (gate "channel"), [B,T,H] ("head") or None ("none") and
+    beta [B,T,H] in float32, initial_state [num_states or B, H, dk, dv]
+    float32 (or None), on ``device``.
     """
     g = _gen(device, seed)
     dt = _DT[dtype]
@@ -36,13 +48,13 @@ def draw_chunk(B, T, H, dk, dv, dtype="bf16", alpha_mu=4.0, alpha_sigma=1.0, s0_
     k = _unit(_normal((B, T, H, dk), g, device)).to(dt)
     v = _normal((B, T, H, dv), g, device).to(dt)
     beta = torch.sigmoid(_normal((B, T, H), g, device)).to(torch.float32)
-    alpha = torch.sigmoid(_normal((B, T, H, dk), g, device, alpha_mu, alpha_sigma)).to(torch.float32)
+    alpha = _alpha((B, T, H), dk, gate, g, device, alpha_mu, alpha_sigma)
     ns = B if num_states is None else num_states
     s0 = None
     if s0_std is not None:
         s0 = _normal((ns, H, dk, dv), g, device, 0.0, s0_std).to(torch.float32)
-    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), alpha=alpha.contiguous(),
-                beta=beta.contiguous(), initial_state=s0)
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), alpha=alpha,
+                beta=beta.contiguous(), initial_state=s0, gate=gate)
 
 
 def varlen_lengths(num_seqs, lo, hi, seed):
@@ -51,9 +63,10 @@ def varlen_lengths(num_seqs, lo, hi, seed):
     return [int(x) for x in torch.randint(lo, hi + 1, (num_seqs,), generator=g)]
 
 
-def chunk_inputs(cfg, device="cpu", T=None, B=None, H=None, seed=None):
+def chunk_inputs(cfg, device="cpu", T=None, B=None, H=None, seed=None, gate="channel"):
     """Inputs of a chunked-forward workload; T/B/H override the sizes for
-    reduced versions.  Varlen workloads also get cu_seqlens (host list and an
+    reduced versions and ``gate`` the forget gate's granularity (the same
+    draws otherwise).  Varlen workloads also get cu_seqlens (host list and an
     int32 tensor on ``device``)."""
     seed = cfg.seed if seed is None else seed
     H = cfg.H if H is None else H
@@ -66,21 +79,22 @@ def chunk_inputs(cfg, device="cpu", T=None, B=None, H=None, seed=None):
         for l in lens:
             cu.append(cu[-1] + l)
         d = draw_chunk(1, cu[-1], H, cfg.dk, cfg.dv, cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std,
-                       num_states=len(lens), seed=seed, device=device)
+                       num_states=len(lens), seed=seed, device=device, gate=gate)
         d["cu_seqlens_host"] = cu
         d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=device)
         return d
     d = draw_chunk(cfg.B if B is None else B, cfg.T if T is None else T, H, cfg.dk, cfg.dv,
-                   cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std, seed=seed, device=device)
+                   cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std, seed=seed, device=device, gate=gate)
     d["cu_seqlens_host"] = None
     d["cu_seqlens"] = None
     return d
 
 
-def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None):
+def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None, gate="channel"):
     """Decode workload: initial state [N,H,dk,dv] float32 and per-step inputs
     stacked on a leading step axis: q, k [S,N,H,dk], v [S,N,H,dv] (storage
-    dtype), alpha [S,N,H,dk], beta [S,N,H] float32."""
+    dtype), alpha [S,N,H,dk] (gate "channel"), [S,N,H] ("head") or None
+    ("none"), beta [S,N,H] float32."""
     seed = cfg.seed if seed is None else seed
     N = cfg.B if N is None else N
     H = cfg.H if H is None else H
@@ -92,6 +106,6 @@ def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None):
     k = _unit(_normal((steps, N, H, cfg.dk), g, device)).to(dt)
     v = _normal((steps, N, H, cfg.dv), g, device).to(dt)
     beta = torch.sigmoid(_normal((steps, N, H), g, device)).to(torch.float32)
-    alpha = torch.sigmoid(_normal((steps, N, H, cfg.dk), g, device, cfg.alpha_mu)).to(torch.float32)
+    alpha = _alpha((steps, N, H), cfg.dk, gate, g, device, cfg.alpha_mu)
     return dict(state=state.contiguous(), q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
-                alpha=alpha.contiguous(), beta=beta.contiguous())
+                alpha=alpha, beta=beta.contiguous(), gate=gate)
