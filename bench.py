@@ -6,8 +6,13 @@ resident in HBM.  value = tokens per second (B*T tokens per step).  The same
 line also carries the decode workload (256 sequences x 32 heads, d=128, fp32
 state in place, 100 consecutive steps) as GB/s against the HBM roofline.
 
+With --gate head (one decay per token and head: Gated DeltaNet) or --gate
+none (no forget gate: DeltaNet) the same workloads run through the *_gated
+entry points with alpha drawn per head (or absent); the default is the
+per-channel gate of KDA.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--calib-copy] [--skip-decode]
+                       [--calib-copy] [--skip-decode] [--gate channel|head|none]
 """
 import argparse
 import hashlib
@@ -39,8 +44,10 @@ def _code_only(text):
 
 
 def source_hash(kernel):
+    """Hash of the sources of a kernel; "name[gate=...]" names an instantiation
+    of the same sources."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES[kernel]:
+    for name in KERNEL_SOURCES[kernel.split("[")[0]]:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -59,18 +66,25 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
-def chunk_bytes(B, T, H, dk, dv, es=2, nstates=None):
+# alpha values per token and head for each forget gate
+GATE_WIDTH = {"channel": lambda dk: dk, "head": lambda dk: 1, "none": lambda dk: 0}
+GATE_NAME = {"channel": "KDA", "head": "Gated DeltaNet", "none": "DeltaNet"}
+
+
+def chunk_bytes(B, T, H, dk, dv, es=2, nstates=None, gate="channel"):
     """Algorithmic HBM bytes of one chunk-wise forward: every input read once,
     every output written once."""
     ns = B if nstates is None else nstates
     tok = B * T * H
-    return (tok * (2 * dk * es + dv * es + dk * 4 + 4 + dv * es)  # q, k, v, alpha, beta, o
+    aw = GATE_WIDTH[gate](dk)
+    return (tok * (2 * dk * es + dv * es + aw * 4 + 4 + dv * es)  # q, k, v, alpha, beta, o
             + 2 * ns * H * dk * dv * 4)                            # initial + final state
 
 
-def decode_bytes(N, H, dk, dv, es=2):
+def decode_bytes(N, H, dk, dv, es=2, gate="channel"):
     """Algorithmic HBM bytes of one decode step."""
-    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + dk * 4 + 4 + dv * es)
+    aw = GATE_WIDTH[gate](dk)
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + aw * 4 + 4 + dv * es)
 
 
 def main():
@@ -85,7 +99,11 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--gate", choices=sorted(GATE_WIDTH), default="channel",
+                    help="forget gate: per key channel (KDA, the default), per head (Gated "
+                         "DeltaNet) or none (DeltaNet)")
     args = ap.parse_args()
+    gate = args.gate
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the workload shards by (batch, head) with no exchange; see DESIGN.md). "
@@ -99,14 +117,18 @@ def main():
     dev = torch.device("cuda:0")
     kda.load_library()
     cfg = CONFIGS[1]
-    d = gen.chunk_inputs(cfg, device=dev)
+    d = gen.chunk_inputs(cfg, device=dev, gate=gate)
     B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     fs = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
 
     def step():
-        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
-                          o=o, final_state=fs)
+        if gate == "channel":
+            kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
+                              o=o, final_state=fs)
+        else:
+            kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                    d["initial_state"], o=o, final_state=fs, gate=gate)
 
     for _ in range(args.warmup):
         step()
@@ -125,12 +147,16 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     tokens = B * T
     value = tokens * args.steps / (ms * args.steps / 1e3)
-    alg = chunk_bytes(B, T, H, dk, dv)
+    alg = chunk_bytes(B, T, H, dk, dv, gate=gate)
     achieved = alg / (ms / 1e3) / 1e9
-    traffic = measured_traffic("chunk_fwd_bf16_kernel")
+    traffic = measured_traffic("chunk_fwd_bf16_kernel" + ("" if gate == "channel" else
+                                                          "[gate=%s]" % gate))
+    gname = GATE_NAME[gate]
+    wl = {"channel": "kda_chunk_fwd", "head": "kda_chunk_fwd_gated (per-head alpha)",
+          "none": "kda_chunk_fwd_gated (no gate)"}[gate]
 
     out = {
-        "metric": "KDA chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline",
+        "metric": "%s chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline" % gname,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -142,7 +168,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "kda_chunk_fwd bf16 B4 H16 T4096 dk128 dv128 chunk64, "
+        "config": {"workload": wl + " bf16 B4 H16 T4096 dk128 dv128 chunk64, "
                                "initial state N(0,0.02)",
                    "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": 64,
                    "parallelism": "single GPU"},
@@ -155,32 +181,41 @@ def main():
 
     if not args.skip_decode:
         dc = CONFIGS[3]
-        dd = gen.decode_inputs(dc, device=dev)
+        dd = gen.decode_inputs(dc, device=dev, gate=gate)
         state = dd["state"].clone()
         od = torch.empty((dc.B, dc.H, dc.dv), dtype=torch.bfloat16, device=dev)
-        sargs = [[dd[n][t] for n in ("q", "k", "v", "alpha", "beta")] for t in range(dc.steps)]
+        sargs = [[None if dd[n] is None else dd[n][t] for n in ("q", "k", "v", "alpha", "beta")]
+                 for t in range(dc.steps)]
+
+        def dstep(t, st):
+            if gate == "channel":
+                kda.kda_recurrent_step(*sargs[t], st, o=od)
+            else:
+                kda.kda_recurrent_step_gated(*sargs[t], st, o=od, gate=gate)
         warm = state.clone()
         for t in range(3):
-            kda.kda_recurrent_step(*sargs[t], warm, o=od)
+            dstep(t, warm)
         torch.cuda.synchronize()
         del warm
         f0 = torch.cuda.Event(enable_timing=True)
         f1 = torch.cuda.Event(enable_timing=True)
         f0.record(stream)
         for t in range(dc.steps):
-            kda.kda_recurrent_step(*sargs[t], state, o=od)
+            dstep(t, state)
         f1.record(stream)
         torch.cuda.synchronize()
         us = f0.elapsed_time(f1) * 1e3 / dc.steps
-        dbytes = decode_bytes(dc.B, dc.H, dc.dk, dc.dv)
+        dbytes = decode_bytes(dc.B, dc.H, dc.dk, dc.dv, gate=gate)
         gbs = dbytes / (us / 1e6) / 1e9
         out["decode"] = {
-            "workload": "kda_recurrent_step bf16 N256 H32 dk128 dv128, fp32 state in place, "
-                        "100 consecutive steps",
+            "workload": "%s bf16 N256 H32 dk128 dv128, fp32 state in place, "
+                        "100 consecutive steps" % ("kda_recurrent_step" if gate == "channel" else
+                                                   "kda_recurrent_step_gated (gate %s)" % gate),
             "us_per_step": us, "tokens_per_s": dc.B / (us / 1e6),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("recurrent_step_kernel"),
+                         "traffic": measured_traffic("recurrent_step_kernel") if gate == "channel"
+                         else None,
                          "kernel": "recurrent_step_kernel",
                          "algorithmic_bytes_per_launch": dbytes},
         }
@@ -200,11 +235,13 @@ def main():
         def units(x):
             x = x.cpu()
             return x.transpose(1, 2).reshape((B * H, T) + tuple(x.shape[3:])).contiguous()
-        host = {n: units(d[n]) for n in ("q", "k", "v", "alpha", "beta")}
+        host = {n: units(d[n]) for n in ("q", "k", "v", "beta")}
         s0 = d["initial_state"].cpu().reshape(B * H, dk, dv)
         cores = min(len(os.sched_getaffinity(0)), B * H)
         c0 = time.perf_counter()
-        oracle.forward_units(host["q"], host["k"], host["v"], host["alpha"], host["beta"], s0,
+        alpha = oracle.channel_gate(None if d["alpha"] is None else units(d["alpha"]), gate, dk,
+                                    (B * H, T))
+        oracle.forward_units(host["q"], host["k"], host["v"], alpha, host["beta"], s0,
                              threads=cores)
         cw = time.perf_counter() - c0
         out["cpu_baseline"] = {"value": tokens / cw, "unit": "tokens/s", "cores": cores,

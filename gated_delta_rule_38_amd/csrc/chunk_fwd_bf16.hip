@@ -747,10 +747,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 
     if (w == NJT + NP + 1) {
         // ====================================================== prefetch wave
-        // Pulls the q, k, alpha and V lines of chunk c + 3 into L2 while chunk c
-        // runs, so that the producers' loads of them (issued during chunk c + 1)
-        // and the helper's (chunk c + 2) hit L2 instead of waiting out HBM
-        // latency with some 500 lines in flight per compute unit.  Value tile jt of a unit takes
+        // Pulls the q, k, alpha and V lines of chunk c + 3 into L2 at the start of
+        // chunk c, so that the producers' loads of them (spread over the operand
+        // build later in the same segment) and the helper's (chunk c + 1) find
+        // them in L2 or in flight instead of waiting out HBM latency with some
+        // 500 lines in flight per compute unit.  Value tile jt of a unit takes
         // rows jt*64/njt.. of the chunk, one line per lane and tensor; the
         // four tiles together touch every line once.  Three register sets
         // rotate, so a wait for a set's loads comes three chunks after them.
