@@ -804,8 +804,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // ============================================================ consumers
     // The consumers carry the serial state chain.  In segment 2 it is the
     // longest path, so the SIMD arbiter is told to prefer them there over the
-    // producers they share a SIMD with; in segment 1 they have slack and take
-    // the lowest priority.  Consumer cj holds NT 16-column tiles of the state;
+    // producers they share a SIMD with; in segment 1 they take the lowest
+    // priority unless they hold two tiles.  Consumer cj holds NT 16-column tiles of the state;
     // with NT = 2 (DVT 64) the tiles share every fragment read and their
     // independent chains interleave.
     // The state, U and Pm*S stay in registers: the operand orders set out at
@@ -876,7 +876,9 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     for (int ch = 0; ch < nch; ++ch) {
         const int par = ch & 1;
         // ======================= segment 1 =======================
-        __builtin_amdgcn_s_setprio(0);
+        // with two tiles per consumer (DVT 64) the consumers' segment-1 work is
+        // as long as the producers', and they share the raised priority
+        __builtin_amdgcn_s_setprio(NT > 1 ? 2 : 0);
         {
             const int lx = (int)opaque((uint32_t)l);  // addresses recomputed per chunk
             const int ln = lx & 15, lg = lx >> 4;
