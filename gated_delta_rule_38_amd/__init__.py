@@ -13,9 +13,9 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_step",
-           "kda_recurrent_step_gated", "kda_chunk_fwd_workspace_size", "kda_status_string",
-           "kda_version", "KDAError", "LIB_PATH", "load_library"]
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused", "kda_recurrent_step",
+           "kda_recurrent_step_gated", "kda_recurrent_step_fused", "kda_chunk_fwd_workspace_size",
+           "kda_status_string", "kda_version", "KDAError", "LIB_PATH", "load_library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -27,6 +27,10 @@ KDA_GATE_CHANNEL = 0
 KDA_GATE_HEAD = 1
 KDA_GATE_NONE = 2
 _GATES = {"channel": KDA_GATE_CHANNEL, "head": KDA_GATE_HEAD, "none": KDA_GATE_NONE}
+# in-kernel input preparation (kda_fuse_flag)
+KDA_FUSE_GATE_LOGITS = 1
+KDA_FUSE_BETA_LOGITS = 2
+KDA_FUSE_QK_L2NORM = 4
 _STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
            3: "KDA_ERROR_MISALIGNED", 4: "KDA_ERROR_INSUFFICIENT_WORKSPACE", 5: "KDA_ERROR_HIP"}
 
@@ -61,6 +65,13 @@ def load_library():
         lib.kda_recurrent_step_gated.restype = i
         lib.kda_recurrent_step_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i,
                                                  f, vp]
+        u = ctypes.c_uint
+        lib.kda_chunk_fwd_fused.restype = i
+        lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i,
+                                            u, vp, ip, i, f, i, vp, sz, vp]
+        lib.kda_recurrent_step_fused.restype = i
+        lib.kda_recurrent_step_fused.argtypes = [vp, vp, vp, vp, fp, fp, vp, i, i, i, i, i, i,
+                                                 u, f, vp]
         lib.kda_chunk_fwd_workspace_size.restype = sz
         lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -123,15 +134,21 @@ def _gate_code(gate):
     return int(gate)
 
 
-def _check_alpha(alpha, gate, lead, dk, dev):
+def _check_alpha(alpha, gate, lead, dk, dev, dtype=torch.float32):
     """alpha for a gate code: [*lead, dk] per channel, [*lead] per head, None."""
     if gate == KDA_GATE_NONE:
         if alpha is not None:
             raise ValueError("alpha must be None without a forget gate")
     elif gate == KDA_GATE_HEAD:
-        _check(alpha, "alpha", torch.float32, dev, tuple(lead))
+        _check(alpha, "alpha", dtype, dev, tuple(lead))
     else:
-        _check(alpha, "alpha", torch.float32, dev, tuple(lead) + (dk,))
+        _check(alpha, "alpha", dtype, dev, tuple(lead) + (dk,))
+
+
+def _fuse_flags(gate_logits, beta_logits, qk_l2norm):
+    return ((KDA_FUSE_GATE_LOGITS if gate_logits else 0) |
+            (KDA_FUSE_BETA_LOGITS if beta_logits else 0) |
+            (KDA_FUSE_QK_L2NORM if qk_l2norm else 0))
 
 
 def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
@@ -165,8 +182,22 @@ def kda_chunk_fwd_gated(q, k, v, alpha, beta, initial_state=None, cu_seqlens=Non
                       output_final_state, final_state, o, chunk_size, workspace, _gate_code(gate))
 
 
+def kda_chunk_fwd_fused(q, k, v, gate, beta, initial_state=None, cu_seqlens=None,
+                        cu_seqlens_host=None, scale=None, output_final_state=True,
+                        final_state=None, o=None, chunk_size=64, workspace=None,
+                        gate_kind="channel", gate_logits=True, beta_logits=True,
+                        qk_l2norm=True):
+    """kda_chunk_fwd_gated with the inputs prepared in the kernel: ``gate``
+    holds logits (dtype of q, alpha = sigmoid) when gate_logits, else float32
+    alpha; ``beta`` holds logits (beta = sigmoid) when beta_logits; q and k
+    are L2-normalised per token and head when qk_l2norm."""
+    return _chunk_fwd(q, k, v, gate, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
+                      output_final_state, final_state, o, chunk_size, workspace,
+                      _gate_code(gate_kind), _fuse_flags(gate_logits, beta_logits, qk_l2norm))
+
+
 def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
-               output_final_state, final_state, o, chunk_size, workspace, gate):
+               output_final_state, final_state, o, chunk_size, workspace, gate, flags=None):
     lib = load_library()
     dev = q.device
     dt = q.dtype
@@ -176,7 +207,8 @@ def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
     _check(q, "q", dt, dev)
     _check(k, "k", dt, dev, (B, T, H, dk))
     _check(v, "v", dt, dev, (B, T, H, dv))
-    _check_alpha(alpha, KDA_GATE_CHANNEL if gate is None else gate, (B, T, H), dk, dev)
+    _check_alpha(alpha, KDA_GATE_CHANNEL if gate is None else gate, (B, T, H), dk, dev,
+                 dt if (flags or 0) & KDA_FUSE_GATE_LOGITS else torch.float32)
     _check(beta, "beta", torch.float32, dev, (B, T, H))
     num_seqs = 0
     cu_dev = None
@@ -215,7 +247,12 @@ def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     common = (float(scale) if scale is not None else 0.0, int(chunk_size), _ptr(ws), ws_bytes,
               _stream(dev))
-    if gate is None:
+    if flags is not None:
+        st = lib.kda_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                     B, T, H, dk, dv, code, gate, flags, _ptr(cu_dev),
+                                     cu_host_arr, num_seqs, *common)
+    elif gate is None:
         st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(initial_state), _ptr(o), _ptr(final_state),
                                B, T, H, dk, dv, code, _ptr(cu_dev), cu_host_arr, num_seqs,
@@ -226,7 +263,8 @@ def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
                                      B, T, H, dk, dv, code, gate, _ptr(cu_dev), cu_host_arr,
                                      num_seqs, *common)
     if st != 0:
-        raise KDAError(st, "kda_chunk_fwd" if gate is None else "kda_chunk_fwd_gated")
+        raise KDAError(st, "kda_chunk_fwd_fused" if flags is not None else
+                       "kda_chunk_fwd" if gate is None else "kda_chunk_fwd_gated")
     return o, final_state
 
 
@@ -243,7 +281,15 @@ def kda_recurrent_step_gated(q, k, v, alpha, beta, state, scale=None, o=None, ga
     return _recurrent_step(q, k, v, alpha, beta, state, scale, o, _gate_code(gate))
 
 
-def _recurrent_step(q, k, v, alpha, beta, state, scale, o, gate):
+def kda_recurrent_step_fused(q, k, v, gate, beta, state, scale=None, o=None, gate_kind="channel",
+                             gate_logits=True, beta_logits=True, qk_l2norm=True):
+    """kda_recurrent_step_gated with the inputs prepared in the kernel (flags as
+    for kda_chunk_fwd_fused)."""
+    return _recurrent_step(q, k, v, gate, beta, state, scale, o, _gate_code(gate_kind),
+                           _fuse_flags(gate_logits, beta_logits, qk_l2norm))
+
+
+def _recurrent_step(q, k, v, alpha, beta, state, scale, o, gate, flags=None):
     lib = load_library()
     dev = q.device
     dt = q.dtype
@@ -253,7 +299,8 @@ def _recurrent_step(q, k, v, alpha, beta, state, scale, o, gate):
     _check(q, "q", dt, dev)
     _check(k, "k", dt, dev, (N, H, dk))
     _check(v, "v", dt, dev, (N, H, dv))
-    _check_alpha(alpha, KDA_GATE_CHANNEL if gate is None else gate, (N, H), dk, dev)
+    _check_alpha(alpha, KDA_GATE_CHANNEL if gate is None else gate, (N, H), dk, dev,
+                 dt if (flags or 0) & KDA_FUSE_GATE_LOGITS else torch.float32)
     _check(beta, "beta", torch.float32, dev, (N, H))
     _check(state, "state", torch.float32, dev, (N, H, dk, dv))
     if o is None:
@@ -261,7 +308,11 @@ def _recurrent_step(q, k, v, alpha, beta, state, scale, o, gate):
     else:
         _check(o, "o", dt, dev, (N, H, dv))
     sc = float(scale) if scale is not None else 0.0
-    if gate is None:
+    if flags is not None:
+        st = lib.kda_recurrent_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                          _ptr(state), _ptr(o), N, H, dk, dv, code, gate, flags,
+                                          sc, _stream(dev))
+    elif gate is None:
         st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                     _ptr(state), _ptr(o), N, H, dk, dv, code, sc, _stream(dev))
     else:
@@ -269,5 +320,6 @@ def _recurrent_step(q, k, v, alpha, beta, state, scale, o, gate):
                                           _ptr(state), _ptr(o), N, H, dk, dv, code, gate, sc,
                                           _stream(dev))
     if st != 0:
-        raise KDAError(st, "kda_recurrent_step" if gate is None else "kda_recurrent_step_gated")
+        raise KDAError(st, "kda_recurrent_step_fused" if flags is not None else
+                       "kda_recurrent_step" if gate is None else "kda_recurrent_step_gated")
     return o

@@ -13,13 +13,15 @@ constexpr int CH = 64;  // chunk length
 
 struct KParams {
     const void *q, *k, *v;
-    const float *alpha, *beta, *s0;
+    const void *alpha;  // float32 decays, or logits in the dtype of q (FUSE_GATE_LOGITS)
+    const float *beta, *s0;
     void *o;
     float *sT;
     const int *cu_seqlens;
     const int *order;
     int B, T, H, dv, units, njt_all;
     int gate;  // 0: alpha per key channel, 1: per head (Gated DeltaNet), 2: none (alpha = 1)
+    int fuse;  // kda_fuse_flag bits (FUSE_*)
     float scale;
 };
 

@@ -112,6 +112,7 @@ template <> struct RawRow<float, 1> {
     typedef float T;
     static __device__ __forceinline__ T ld(const float* p) { return *p; }
     static __device__ __forceinline__ T splat(float a) { return a; }
+    static __device__ __forceinline__ T pack(const float* x) { return x[0]; }
     static __device__ __forceinline__ void unpack(T w, float* x) { x[0] = w; }
 };
 template <> struct RawRow<float, 2> {
@@ -120,6 +121,7 @@ template <> struct RawRow<float, 2> {
         return *reinterpret_cast<const float2*>(p);
     }
     static __device__ __forceinline__ T splat(float a) { return make_float2(a, a); }
+    static __device__ __forceinline__ T pack(const float* x) { return make_float2(x[0], x[1]); }
     static __device__ __forceinline__ void unpack(T w, float* x) { x[0] = w.x; x[1] = w.y; }
 };
 
@@ -176,9 +178,11 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
     const Tin* __restrict__ gq = static_cast<const Tin*>(p.q);
     const Tin* __restrict__ gk = static_cast<const Tin*>(p.k);
     const Tin* __restrict__ gv = static_cast<const Tin*>(p.v);
-    const float* __restrict__ ga = p.alpha;
+    const float* __restrict__ ga = static_cast<const float*>(p.alpha);
+    const Tin* __restrict__ gg = static_cast<const Tin*>(p.alpha);  // gate logits
     const float* __restrict__ gb = p.beta;
     const int gate = p.gate;
+    const bool gl = p.fuse & FUSE_GATE_LOGITS, qn = p.fuse & FUSE_QK_L2NORM;
     Tin* __restrict__ go = static_cast<Tin*>(p.o);
 
     const int tid = threadIdx.x;
@@ -229,9 +233,18 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
             pq[r] = RQ::ld(gq + off);
             pk[r] = RQ::ld(gk + off);
             if (gate == 0) {
-                pa[r] = RA::ld(ga + off);
+                if (!gl) {
+                    pa[r] = RA::ld(ga + off);
+                } else if constexpr (sizeof(Tin) == 4) {  // float32 logits, same layout
+                    pa[r] = RA::ld(reinterpret_cast<const float*>(gg) + off);
+                } else {  // bf16 logits, widened here
+                    float x[CPT];
+                    RQ::unpack(RQ::ld(gg + off), x);
+                    pa[r] = RA::pack(x);
+                }
             } else {  // one decay for every channel of the token, or none
-                pa[r] = RA::splat(gate == 1 ? ga[(size_t)(t0 + t) * H + h] : 1.f);
+                const size_t oh = (size_t)(t0 + t) * H + h;
+                pa[r] = RA::splat(gate == 1 ? (gl ? to_f32(gg[oh]) : ga[oh]) : 1.f);
             }
         }
         if (w == 0) pbeta = gb[(size_t)(t0 + min(ch * CH + l, len - 1)) * H + h];
@@ -263,6 +276,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
             for (int r = 0; r < 16; ++r) {
                 float a[CPT];
                 RA::unpack(pa[r], a);
+                if (gl) {
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) a[c] = sigmoid_f(a[c]);
+                }
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
                     run[c] *= (r < nvalid) ? a[c] : 1.f;
@@ -291,6 +308,19 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
                 float kx[CPT], qx[CPT];
                 RQ::unpack(pk[r], kx);
                 RQ::unpack(pq[r], qx);
+                if (qn) {  // L2 norms of the row's k and q over the 64 lanes
+                    float sk = 0.f, sq = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) { sk += kx[c] * kx[c]; sq += qx[c] * qx[c]; }
+#pragma unroll
+                    for (int off = 1; off < 64; off *= 2) {
+                        sk += __shfl_xor(sk, off, 64);
+                        sq += __shfl_xor(sq, off, 64);
+                    }
+                    const float ik = inv_norm(sk), iq = inv_norm(sq);
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) { kx[c] *= ik; qx[c] *= iq; }
+                }
                 Top kr[CPT], qr[CPT], kc[CPT];
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
@@ -308,7 +338,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
             }
 #pragma unroll
             for (int c = 0; c < CPT; ++c) store_run<Top, 16>(sKcT + (c0 + c) * LDC + w * 16, kct[c]);
-            if (w == 0) sBeta[l] = (ch * CH + l < len) ? pbeta : 0.f;
+            if (w == 0)
+                sBeta[l] = (ch * CH + l < len)
+                               ? ((p.fuse & FUSE_BETA_LOGITS) ? sigmoid_f(pbeta) : pbeta) : 0.f;
             // state operand SP = (Pm * S0)^T and the per-row decays kept for phase 4
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
@@ -583,6 +615,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const int* order, hipStream
     p.units = nseq * a.H;
     p.njt_all = a.dv / DVT;
     p.gate = a.gate;
+    p.fuse = a.fuse;
     p.scale = a.scale;
     const int groups = (p.units + 7) / 8;
     const long grid = 8L * p.njt_all * groups;
@@ -643,6 +676,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
         p.units = units;
         p.njt_all = a.dv / dvt;
         p.gate = a.gate;
+        p.fuse = a.fuse;
         p.scale = a.scale;
         return launch_chunk_bf16(p, a.dk, dvt, stream);
     }

@@ -249,7 +249,7 @@ __device__ __forceinline__ float rows_sel(float x, float y) {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(y), 0xE4, ROWS, 0xf, false));
 }
 
-template <int DK, int DVT>
+template <int DK, int DVT, bool QN = false>
 struct Lay6 {
     static constexpr int NJT = DVT >= 32 ? 2 : 1;  // consumer waves
     static constexpr int NT = DVT / 16 / NJT;      // 16-column state tiles per consumer
@@ -280,15 +280,23 @@ struct Lay6 {
     static constexpr size_t oKc = oKcT + (size_t)DK * LDC * 2;  // [64][LDK]
     static constexpr size_t oLd = oKc + szTok;                  // fp32 [4][16 rows][LDL]
     static constexpr size_t oD = oLd + (size_t)4 * 16 * LDL * 4;  // D_a, 4 blocks row-major
-    static constexpr size_t bytes = oD + (size_t)4 * BLK * 2;
+    // with in-kernel q/k normalisation: fp32 partial sums of squares
+    // [parity][q, k][64 rows][4 producers]
+    static constexpr size_t oPart = oD + (size_t)4 * BLK * 2;
+    static constexpr size_t bytes = oPart + (QN ? (size_t)2 * 2 * CH * 4 * 4 : 0);
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
 // GATE: 0 = alpha per key channel (KDA), 1 = one alpha per token and head
-// (Gated DeltaNet), 2 = no gate (DeltaNet, alpha = 1)
-template <int DK, int DVT, int GATE>
+// (Gated DeltaNet), 2 = no gate (DeltaNet, alpha = 1).
+// FE: in-kernel input preparation, FUSE_GATE_LOGITS (bf16 logits z in place
+// of alpha, alpha = sigmoid(z)) and FUSE_QK_L2NORM (q, k normalised per
+// token); beta logits (FUSE_BETA_LOGITS) are a run-time flag.
+template <int DK, int DVT, int GATE, int FE>
 __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel(KParams p) {
-    using L = Lay6<DK, DVT>;
+    constexpr bool GL = (FE & FUSE_GATE_LOGITS) != 0, QN = (FE & FUSE_QK_L2NORM) != 0;
+    static_assert(!(GL && GATE == 2), "gate logits need a gate");
+    using L = Lay6<DK, DVT, QN>;
     using Mf = Mma<bf16_t>;
     constexpr int LDK = L::LDK, LDC = L::LDC, LDB = L::LDB, LDL = L::LDL, BLK = L::BLK;
     constexpr int NJT = L::NJT, NT = L::NT, NP = L::NP, CPL = L::CPL, RPV = L::RPV;
@@ -300,6 +308,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     bf16_t* sKc = reinterpret_cast<bf16_t*>(smem + L::oKc);
     float* sLd = reinterpret_cast<float*>(smem + L::oLd);
     bf16_t* sD = reinterpret_cast<bf16_t*>(smem + L::oD);
+    float* sPart = reinterpret_cast<float*>(smem + L::oPart);
 
     const WorkItem wi = decode_work(p);
     if (!wi.valid) return;
@@ -314,13 +323,14 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     const int ln = l & 15, lg = l >> 4;
 
     // byte strides of one token row
-    const uint32_t rsq = (uint32_t)H * DK * 2, rsa = (uint32_t)H * DK * 4;
+    const uint32_t rsq = (uint32_t)H * DK * 2, rsa = (uint32_t)H * DK * (GL ? 2 : 4);
     const uint32_t rsb = (uint32_t)H * 4, rsv = (uint32_t)H * DV * 2;
 
     const bf16_t* __restrict__ gq = static_cast<const bf16_t*>(p.q);
     const bf16_t* __restrict__ gk = static_cast<const bf16_t*>(p.k);
     const bf16_t* __restrict__ gv = static_cast<const bf16_t*>(p.v);
-    const float* __restrict__ ga = p.alpha;
+    const float* __restrict__ ga = static_cast<const float*>(p.alpha);
+    const bf16_t* __restrict__ gg = static_cast<const bf16_t*>(p.alpha);  // gate logits
     const float* __restrict__ gb = p.beta;
 
     // ---------------------------------------------------------- Gram blocks
@@ -397,16 +407,20 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         const int pw = w - NJT;
         // decays per lane and row: one per channel, or one for the token
         constexpr int NA = GATE == 0 ? CPL : 1;
+        // 32-bit words of raw alpha per lane and row (bf16 logits come in pairs)
+        constexpr int NAW = GATE == 0 ? (GL ? CPL / 2 : CPL) : 1;
+        // bytes per token of a per-head alpha
+        const uint32_t rsh = (uint32_t)H * (GL ? 2 : 4);
         // registers carried across chunks: two sets of raw q, k, alpha rows
         // (chunks of even and odd index, loaded three chunks ahead) and the
         // Kc^T pairs of the chunk whose operands were built last
-        struct Raw { uint32_t q[2 * CPL], k[2 * CPL], a[4 * NA]; };
+        struct Raw { uint32_t q[2 * CPL], k[2 * CPL], a[4 * NAW]; };
         Raw R0, R1;
         uint32_t RT[2 * CPL];
 #pragma unroll
         for (int i = 0; i < 2 * CPL; ++i) { R0.q[i] = R0.k[i] = R1.q[i] = R1.k[i] = 0u; RT[i] = 0u; }
 #pragma unroll
-        for (int i = 0; i < 4 * NA; ++i) R0.a[i] = R1.a[i] = 0u;
+        for (int i = 0; i < 4 * NAW; ++i) R0.a[i] = R1.a[i] = 0u;
 
         // descriptors and lane offsets of the raw q, k, alpha rows of chunk ch
         struct Src { Rsrc rq, rk, ra; uint32_t qo, ao; };
@@ -424,11 +438,12 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             sr.rk = make_rsrc(gk + e0, (uint32_t)nr * rsq);
             sr.qo = (uint32_t)pr0 * rsq + (uint32_t)pc0 * 2;
             if constexpr (GATE == 0) {
-                sr.ra = make_rsrc(ga + e0, (uint32_t)nr * rsa);
-                sr.ao = (uint32_t)pr0 * rsa + (uint32_t)pc0 * 4;
+                sr.ra = make_rsrc(GL ? (const void*)(gg + e0) : (const void*)(ga + e0), (uint32_t)nr * rsa);
+                sr.ao = (uint32_t)pr0 * rsa + (uint32_t)pc0 * (GL ? 2 : 4);
             } else {  // alpha [token][head]; unused without a gate
-                sr.ra = make_rsrc(GATE == 1 ? ga + e0 / DK : ga, GATE == 1 ? (uint32_t)nr * rsb : 0u);
-                sr.ao = (uint32_t)pr0 * rsb;
+                const void* hb = GL ? (const void*)(gg + e0 / DK) : (const void*)(ga + e0 / DK);
+                sr.ra = make_rsrc(GATE == 1 ? hb : p.alpha, GATE == 1 ? (uint32_t)nr * rsh : 0u);
+                sr.ao = (uint32_t)pr0 * rsh;
             }
             return sr;
         };
@@ -446,21 +461,68 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             }
         };
         auto ld_a = [&](const Src& sr, Raw& R, int rr) {  // alpha of the lane's row rr
-            if constexpr (GATE == 0) {
+            if constexpr (GATE == 0 && !GL) {
 #pragma unroll
                 for (int j = 0; j < CPL / 4; ++j) {
                     const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr.ra, sr.ao + rr * rsa + 16 * j, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) R.a[CPL * rr + 4 * j + i] = a4[i];
                 }
-            } else if constexpr (GATE == 1) {
-                R.a[rr] = __builtin_amdgcn_raw_buffer_load_b32(sr.ra, sr.ao + rr * rsb, 0, 0);
+            } else if constexpr (GATE == 0 && CPL == 8) {  // 8 bf16 logits
+                const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr.ra, sr.ao + rr * rsa, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) R.a[4 * rr + i] = a4[i];
+            } else if constexpr (GATE == 0) {  // 4 bf16 logits
+                const u32x2 a2 = __builtin_amdgcn_raw_buffer_load_b64(sr.ra, sr.ao + rr * rsa, 0, 0);
+                R.a[2 * rr] = a2[0]; R.a[2 * rr + 1] = a2[1];
+            } else if constexpr (GATE == 1 && !GL) {
+                R.a[rr] = __builtin_amdgcn_raw_buffer_load_b32(sr.ra, sr.ao + rr * rsh, 0, 0);
+            } else if constexpr (GATE == 1) {  // one bf16 logit, in the low half
+                R.a[rr] = __builtin_amdgcn_raw_buffer_load_b16(sr.ra, sr.ao + rr * rsh, 0, 0);
             }
         };
         auto p_load = [&](int ch, Raw& R) {  // raw q, k, alpha rows of chunk ch
             const Src sr = p_src(ch);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) { ld_qk(sr, R, rr); ld_a(sr, R, rr); }
+        };
+        // Partial sums of squares of the raw q and k rows of chunk ch held in R,
+        // over this producer's channels, into sPart (parity ch & 1): a quad's
+        // four lanes hold one token's channels of the producer, so two DPP
+        // steps finish the producer's sum and the first lane stores it.
+        auto p_norms = [&](const Raw& R, int ch) {
+            const int lx = (int)opaque((uint32_t)l);
+            const int pr0 = (lx >> 2) * 4;
+            float ss[2][4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int i = 0; i < CPL / 2; ++i) {
+                    const bf16x2v qw = __builtin_bit_cast(bf16x2v, R.q[(CPL / 2) * rr + i]);
+                    const bf16x2v kw = __builtin_bit_cast(bf16x2v, R.k[(CPL / 2) * rr + i]);
+                    sq = __builtin_amdgcn_fdot2_f32_bf16(qw, qw, sq, false);
+                    sk = __builtin_amdgcn_fdot2_f32_bf16(kw, kw, sk, false);
+                }
+                ss[0][rr] = sq;
+                ss[1][rr] = sk;
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    float x = ss[t][rr];
+                    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
+                    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
+                    ss[t][rr] = x;
+                }
+            if ((lx & 3) == 0) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        sPart[(((ch & 1) * 2 + t) * CH + pr0 + rr) * 4 + pw] = ss[t][rr];
+            }
         };
         auto p_write_kct = [&]() {
             const int lx = (int)opaque((uint32_t)l);
@@ -490,6 +552,34 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             // pr0 + 3), the running products pr over the lane's rows, and u (Pm
             // in 16-lane row 0, Pn / Pm in row 3); index ai(c) for channel c
             auto ai = [](int c) { return GATE == 0 ? c : 0; };
+            // the decays of the lane's rows: stored alpha, or sigmoid of the
+            // stored logits, formed once here (rows past the end decay by 1)
+            float al[GL ? 4 : 1][GL ? NA : 1];
+            if constexpr (GL) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                    for (int c = 0; c < NA; ++c) {
+                        const uint32_t wd = RA[NAW * rr + c / 2];
+                        al[rr][c] = (pr0 + rr < nval) ? sigmoid_f((c & 1) ? hi_f(wd) : lo_f(wd)) : 1.f;
+                    }
+            }
+            auto alv = [&](int rr, int c) {
+                if constexpr (GL) return al[rr][c];
+                else return ra_f(NA * rr + c);
+            };
+            // 1 / |k| and 1 / |q| of the lane's rows from the producers' partial sums
+            float ik[4], iq[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                ik[rr] = iq[rr] = 1.f;
+                if constexpr (QN) {
+                    const float4 sq = ld4(sPart + (((ch & 1) * 2 + 0) * CH + pr0 + rr) * 4);
+                    const float4 sk = ld4(sPart + (((ch & 1) * 2 + 1) * CH + pr0 + rr) * 4);
+                    iq[rr] = inv_norm((sq.x + sq.y) + (sq.z + sq.w));
+                    ik[rr] = inv_norm((sk.x + sk.y) + (sk.z + sk.w));
+                }
+            }
             float pr[4][NA], f[NA], g[NA], u[NA];
             if constexpr (GATE == 2) {
 #pragma unroll
@@ -499,7 +589,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                     for (int rr = 0; rr < 4; ++rr) pr[rr][c] = 1.f;
                 }
             } else {
-                if (nval < CH) {  // alpha of rows past the end of the sequence is 1
+                if (!GL && nval < CH) {  // alpha of rows past the end of the sequence is 1
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
                         if (pr0 + rr >= nval)
@@ -509,10 +599,10 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                 float inc[NA];
 #pragma unroll
                 for (int c = 0; c < NA; ++c) {
-                    float run = ra_f(c);
+                    float run = alv(0, c);
                     pr[0][c] = run;
 #pragma unroll
-                    for (int rr = 1; rr < 4; ++rr) { run *= ra_f(NA * rr + c); pr[rr][c] = run; }
+                    for (int rr = 1; rr < 4; ++rr) { run *= alv(rr, c); pr[rr][c] = run; }
                     inc[c] = run;
                 }
                 ld_a(sr, R, 0);  // alpha of row 0 is used up
@@ -559,30 +649,44 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             for (int rr = 3; rr >= 0; --rr) {
                 uint32_t kr[CPL / 2], qr[CPL / 2], kc[CPL / 2];
                 if constexpr (GATE == 1) {
-                    if (rr < 3) g[0] *= ra_f(rr + 1);
+                    if (rr < 3) g[0] *= alv(rr + 1, 0);
                 }
                 const float rrow = pr[rr][0] * f[0];  // P_r / Pm of a token-wide decay
+                // row multipliers with the norms folded in (the norms are 1 without QN)
+                const float rrk = rrow * ik[rr], rrq = rrow * iq[rr], grk = g[0] * ik[rr];
 #pragma unroll
                 for (int i = 0; i < CPL / 2; ++i) {
                     const uint32_t kw = RK[(CPL / 2) * rr + i], qw = RQ[(CPL / 2) * rr + i];
                     const int c0 = 2 * i, c1 = 2 * i + 1;
-                    if constexpr (GATE == 2) {  // no decay: the stored values as they are
+                    if constexpr (GATE == 2 && !QN) {  // no decay: the stored values as they are
                         kr[i] = kw;
                         qr[i] = qw;
                         kc[i] = kw;
-                    } else {
-                        if constexpr (GATE == 0) {
-                            if (rr < 3) {
-                                g[c0] *= ra_f(CPL * (rr + 1) + c0);
-                                g[c1] *= ra_f(CPL * (rr + 1) + c1);
-                            }
+                    } else if constexpr (GATE == 2) {  // normalised, no decay
+                        kr[i] = pack2(lo_f(kw) * ik[rr], hi_f(kw) * ik[rr]);
+                        qr[i] = pack2(lo_f(qw) * iq[rr], hi_f(qw) * iq[rr]);
+                        kc[i] = kr[i];
+                    } else if constexpr (GATE == 0) {
+                        if (rr < 3) {
+                            g[c0] *= alv(rr + 1, c0);
+                            g[c1] *= alv(rr + 1, c1);
                         }
-                        const float r0 = GATE == 0 ? pr[rr][c0] * f[c0] : rrow;
-                        const float r1 = GATE == 0 ? pr[rr][c1] * f[c1] : rrow;
+                        const float r0 = pr[rr][c0] * f[c0], r1 = pr[rr][c1] * f[c1];
                         const float k0 = lo_f(kw), k1 = hi_f(kw);
-                        kr[i] = pack2(k0 * r0, k1 * r1);
-                        qr[i] = pack2(lo_f(qw) * r0, hi_f(qw) * r1);
-                        kc[i] = pack2(k0 * g[ai(c0)], k1 * g[ai(c1)]);
+                        if constexpr (QN) {
+                            kr[i] = pack2(k0 * (r0 * ik[rr]), k1 * (r1 * ik[rr]));
+                            qr[i] = pack2(lo_f(qw) * (r0 * iq[rr]), hi_f(qw) * (r1 * iq[rr]));
+                            kc[i] = pack2(k0 * (g[c0] * ik[rr]), k1 * (g[c1] * ik[rr]));
+                        } else {
+                            kr[i] = pack2(k0 * r0, k1 * r1);
+                            qr[i] = pack2(lo_f(qw) * r0, hi_f(qw) * r1);
+                            kc[i] = pack2(k0 * g[c0], k1 * g[c1]);
+                        }
+                    } else {  // one decay for the token
+                        const float k0 = lo_f(kw), k1 = hi_f(kw);
+                        kr[i] = pack2(k0 * rrk, k1 * rrk);
+                        qr[i] = pack2(lo_f(qw) * rrq, hi_f(qw) * rrq);
+                        kc[i] = pack2(k0 * grk, k1 * grk);
                     }
                     if (rr & 1) {
                         kcp[i] = kc[i];
@@ -614,10 +718,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         //   segment 1: Kc^T(c); operands of c+1 from its raw set, which
         //              meanwhile receives the rows of c+3
         //   segment 2: Gram blocks of c+1
-        auto step = [&](int ch, Raw& R) {
+        auto step = [&](int ch, Raw& R, const Raw& RO) {
             __builtin_amdgcn_s_setprio(2);
             p_write_kct();  // Kc^T of chunk ch (its Kc came with the operands one chunk ago)
             p_operands(ch + 1, R, ch + 3);
+            if constexpr (QN) p_norms(RO, ch + 2);  // RO holds the rows of chunk ch + 2
             __syncthreads();
             __builtin_amdgcn_s_setprio(0);
             gram_share(ch + 1, pw);
@@ -625,6 +730,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         };
         p_load(0, R0);
         p_load(1, R1);
+        if constexpr (QN) {
+            p_norms(R0, 0);
+            p_norms(R1, 1);
+            __syncthreads();
+        }
         p_operands(0, R0, 2);
         __syncthreads();
         gram_share(0, pw);
@@ -632,10 +742,10 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         // two chunks per trip so each raw set keeps fixed registers
         int ch = 0;
         for (; ch + 1 < nch; ch += 2) {
-            step(ch, R1);
-            step(ch + 1, R0);
+            step(ch, R1, R0);
+            step(ch + 1, R0, R1);
         }
-        if (ch < nch) step(ch, R1);
+        if (ch < nch) step(ch, R1, R0);
         return;
     }
 
@@ -673,7 +783,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             }
         };
         auto h_write_beta = [&](int ch) {
-            reinterpret_cast<float*>(buf(ch & 1, L::bBeta))[(int)opaque((uint32_t)l)] = __uint_as_float(HB);
+            const int lx = (int)opaque((uint32_t)l);
+            float bv = __uint_as_float(HB);
+            // beta logits: sigmoid for the rows of the chunk; rows past the end keep 0
+            if ((p.fuse & FUSE_BETA_LOGITS) && lx < len - ch * CH) bv = sigmoid_f(bv);
+            reinterpret_cast<float*>(buf(ch & 1, L::bBeta))[lx] = bv;
         };
         // V^T: for each of the lane's 8 columns, its RPV rows as one run
         auto h_write_vt = [&](int ch) {
@@ -726,6 +840,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         h_write_beta(0);
         h_write_vt(0);
         h_load(1);
+        if constexpr (QN) __syncthreads();
         __syncthreads();
         gram_share(0, NP);
         __syncthreads();
@@ -767,17 +882,23 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const Rsrc rv = make_rsrc(gv + tok * DV, (uint32_t)nr * rsv);
             r[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, row * rsq + (sub & 1) * 128, 0, 0);
             r[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, row * rsq + (sub & 1) * 128, 0, 0);
-            if constexpr (GATE == 0) {
-                const Rsrc ra = make_rsrc(ga + tok * DK, (uint32_t)nr * rsa);
-                r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsa + (sub & 3) * 128, 0, 0);
+            if constexpr (GATE == 0) {  // 512-byte rows (256 with bf16 logits)
+                const Rsrc ra = make_rsrc(GL ? (const void*)(gg + tok * DK) : (const void*)(ga + tok * DK),
+                                          (uint32_t)nr * rsa);
+                r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsa + (sub & (GL ? 1 : 3)) * 128, 0, 0);
             } else if constexpr (GATE == 1) {
-                const Rsrc ra = make_rsrc(ga + tok, (uint32_t)nr * rsb);
-                r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsb, 0, 0);
+                const uint32_t rsh = (uint32_t)H * (GL ? 2 : 4);
+                const Rsrc ra = make_rsrc(GL ? (const void*)(gg + tok) : (const void*)(ga + tok), (uint32_t)nr * rsh);
+                if constexpr (GL)  // bf16 logits: 2-byte elements
+                    r[2] = __builtin_amdgcn_raw_buffer_load_b16(ra, row * rsh, 0, 0);
+                else
+                    r[2] = __builtin_amdgcn_raw_buffer_load_b32(ra, row * rsh, 0, 0);
             } else {
                 r[2] = 0u;
             }
             r[3] = __builtin_amdgcn_raw_buffer_load_b32(rv, row * rsv + (sub & 1) * 128, 0, 0);
         };
+        if constexpr (QN) __syncthreads();
         __syncthreads();
         __syncthreads();
         int ch = 0;
@@ -871,6 +992,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                          m1.w * S[j][2 * s + 1][3]};
         return Mf::F32{__builtin_shufflevector(Mf::pack16(a).v, Mf::pack16(b).v, 0, 1, 2, 3, 4, 5, 6, 7)};
     };
+    if constexpr (QN) __syncthreads();
     __syncthreads();
     __syncthreads();
     for (int ch = 0; ch < nch; ++ch) {
@@ -994,23 +1116,38 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     }
 }
 
-template <int DK, int DVT, int GATE>
+template <int DK, int DVT, int GATE, int FE>
 static hipError_t launch_g(const KParams& p, hipStream_t stream) {
-    using Lay = Lay6<DK, DVT>;
+    using Lay = Lay6<DK, DVT, (FE & FUSE_QK_L2NORM) != 0>;
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)chunk_fwd_bf16_kernel<DK, DVT, GATE>,
+        (const void*)chunk_fwd_bf16_kernel<DK, DVT, GATE, FE>,
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
     const long grid = 8L * p.njt_all * ((p.units + 7) / 8);
-    hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVT, GATE>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVT, GATE, FE>), dim3((unsigned)grid),
                        dim3(Lay::NTH), Lay::bytes, stream, p);
     return hipGetLastError();
 }
 
+// the front-end instantiations: gate logits and q/k normalisation (beta
+// logits are a run-time flag)
+template <int DK, int DVT, int GATE>
+static hipError_t launch_fe(const KParams& p, hipStream_t stream) {
+    const bool gl = (p.fuse & FUSE_GATE_LOGITS) != 0, qn = (p.fuse & FUSE_QK_L2NORM) != 0;
+    if constexpr (GATE == 2) {
+        return qn ? launch_g<DK, DVT, 2, FUSE_QK_L2NORM>(p, stream) : launch_g<DK, DVT, 2, 0>(p, stream);
+    } else {
+        if (gl && qn) return launch_g<DK, DVT, GATE, FUSE_GATE_LOGITS | FUSE_QK_L2NORM>(p, stream);
+        if (gl) return launch_g<DK, DVT, GATE, FUSE_GATE_LOGITS>(p, stream);
+        if (qn) return launch_g<DK, DVT, GATE, FUSE_QK_L2NORM>(p, stream);
+        return launch_g<DK, DVT, GATE, 0>(p, stream);
+    }
+}
+
 template <int DK, int DVT>
 static hipError_t launch_t(const KParams& p, hipStream_t stream) {
-    return p.gate == 0 ? launch_g<DK, DVT, 0>(p, stream)
-         : p.gate == 1 ? launch_g<DK, DVT, 1>(p, stream) : launch_g<DK, DVT, 2>(p, stream);
+    return p.gate == 0 ? launch_fe<DK, DVT, 0>(p, stream)
+         : p.gate == 1 ? launch_fe<DK, DVT, 1>(p, stream) : launch_fe<DK, DVT, 2>(p, stream);
 }
 
 // value-column tile widths this kernel supports

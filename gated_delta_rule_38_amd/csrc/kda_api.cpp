@@ -57,6 +57,14 @@ bool valid_gate(int gate) {
     return gate == KDA_GATE_CHANNEL || gate == KDA_GATE_HEAD || gate == KDA_GATE_NONE;
 }
 
+constexpr unsigned kAllFuse = KDA_FUSE_GATE_LOGITS | KDA_FUSE_BETA_LOGITS | KDA_FUSE_QK_L2NORM;
+
+// flags that the gate kind admits
+bool valid_flags(int gate, unsigned flags) {
+    if (flags & ~kAllFuse) return false;
+    return !(gate == KDA_GATE_NONE && (flags & KDA_FUSE_GATE_LOGITS));
+}
+
 // alpha values per token and head for a gate
 size_t gate_width(int gate, int dk) {
     return gate == KDA_GATE_CHANNEL ? (size_t)dk : gate == KDA_GATE_HEAD ? 1 : 0;
@@ -74,16 +82,16 @@ int env_dvt() {
     return (v == 16 || v == 32 || v == 64) ? v : 0;
 }
 
-kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* alpha,
                           const float* beta, const float* initial_state, void* o,
                           float* final_state, int B, int T, int H, int dk, int dv,
-                          kda_dtype dtype, int gate, const int* cu_seqlens_dev,
+                          kda_dtype dtype, int gate, unsigned flags, const int* cu_seqlens_dev,
                           const int* cu_seqlens_host, int num_seqs, float scale,
                           int chunk_size, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
-kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const float* alpha,
+kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const void* alpha,
                                const float* beta, float* state, void* o, int N, int H, int dk,
-                               int dv, kda_dtype dtype, int gate, float scale,
+                               int dv, kda_dtype dtype, int gate, unsigned flags, float scale,
                                hipStream_t stream);
 
 }  // namespace
@@ -121,7 +129,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int chunk_size, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, alpha, beta, initial_state, o, final_state, B, T, H, dk, dv,
-                          dtype, KDA_GATE_CHANNEL, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                          dtype, KDA_GATE_CHANNEL, 0u, cu_seqlens_dev, cu_seqlens_host, num_seqs,
                           scale, chunk_size, workspace, workspace_bytes, stream);
 }
 
@@ -133,15 +141,27 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, cons
                                int chunk_size, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, alpha, beta, initial_state, o, final_state, B, T, H, dk, dv,
-                          dtype, (int)gate, cu_seqlens_dev, cu_seqlens_host, num_seqs, scale,
+                          dtype, (int)gate, 0u, cu_seqlens_dev, cu_seqlens_host, num_seqs, scale,
                           chunk_size, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* gate,
+                               const float* beta, const float* initial_state, void* o,
+                               float* final_state, int B, int T, int H, int dk, int dv,
+                               kda_dtype dtype, kda_gate gate_kind, unsigned flags,
+                               const int* cu_seqlens_dev, const int* cu_seqlens_host,
+                               int num_seqs, float scale, int chunk_size, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, gate, beta, initial_state, o, final_state, B, T, H, dk, dv,
+                          dtype, (int)gate_kind, flags, cu_seqlens_dev, cu_seqlens_host,
+                          num_seqs, scale, chunk_size, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, float* state, void* o, int N, int H, int dk,
                               int dv, kda_dtype dtype, float scale, hipStream_t stream) {
     return recurrent_step_impl(q, k, v, alpha, beta, state, o, N, H, dk, dv, dtype,
-                               KDA_GATE_CHANNEL, scale, stream);
+                               KDA_GATE_CHANNEL, 0u, scale, stream);
 }
 
 kda_status kda_recurrent_step_gated(const void* q, const void* k, const void* v,
@@ -149,23 +169,32 @@ kda_status kda_recurrent_step_gated(const void* q, const void* k, const void* v,
                                     void* o, int N, int H, int dk, int dv, kda_dtype dtype,
                                     kda_gate gate, float scale, hipStream_t stream) {
     return recurrent_step_impl(q, k, v, alpha, beta, state, o, N, H, dk, dv, dtype, (int)gate,
-                               scale, stream);
+                               0u, scale, stream);
+}
+
+kda_status kda_recurrent_step_fused(const void* q, const void* k, const void* v,
+                                    const void* gate, const float* beta, float* state, void* o,
+                                    int N, int H, int dk, int dv, kda_dtype dtype,
+                                    kda_gate gate_kind, unsigned flags, float scale,
+                                    hipStream_t stream) {
+    return recurrent_step_impl(q, k, v, gate, beta, state, o, N, H, dk, dv, dtype,
+                               (int)gate_kind, flags, scale, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha,
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* alpha,
                           const float* beta, const float* initial_state, void* o,
                           float* final_state, int B, int T, int H, int dk, int dv,
-                          kda_dtype dtype, int gate, const int* cu_seqlens_dev,
+                          kda_dtype dtype, int gate, unsigned flags, const int* cu_seqlens_dev,
                           const int* cu_seqlens_host, int num_seqs, float scale,
                           int chunk_size, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
     try {
         if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
-        if (!valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
+        if (!valid_gate(gate) || !valid_flags(gate, flags)) return KDA_ERROR_INVALID_VALUE;
         if (gate == KDA_GATE_NONE && alpha) return KDA_ERROR_INVALID_VALUE;
         if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return KDA_ERROR_INVALID_VALUE;
         if (chunk_size != kChunk) return KDA_ERROR_NOT_SUPPORTED;
@@ -173,6 +202,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         const bool varlen = num_seqs > 0;
         if (!varlen && (cu_seqlens_dev || cu_seqlens_host)) return KDA_ERROR_INVALID_VALUE;
         const size_t es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+        const size_t ges = (flags & KDA_FUSE_GATE_LOGITS) ? es : 4;  // gate element size
         int nstates = B;
         if (varlen) {
             if (!cu_seqlens_dev || !cu_seqlens_host || B != 1) return KDA_ERROR_INVALID_VALUE;
@@ -186,7 +216,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         }
         size_t b_qk, b_v, b_a, b_b, b_s;
         if (!bytes_of(B, T, H, dk, es, &b_qk) || !bytes_of(B, T, H, dv, es, &b_v) ||
-            !bytes_of(B, T, H, gate_width(gate, dk), 4, &b_a) || !bytes_of(B, T, H, 1, 4, &b_b) ||
+            !bytes_of(B, T, H, gate_width(gate, dk), ges, &b_a) || !bytes_of(B, T, H, 1, 4, &b_b) ||
             !bytes_of(nstates, H, dk, dv, 4, &b_s))
             return KDA_ERROR_INVALID_VALUE;
         // grid and index limits of the kernels
@@ -201,7 +231,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         const void* pairs[] = {q, k, gate == KDA_GATE_CHANNEL ? alpha : nullptr};
         for (const void* ptr : pairs)
             if (!aligned(ptr, 8)) return KDA_ERROR_MISALIGNED;
-        if (!aligned(alpha, 4)) return KDA_ERROR_MISALIGNED;
+        if (!aligned(alpha, ges)) return KDA_ERROR_MISALIGNED;
         if (!aligned(v, es) || !aligned(o, es)) return KDA_ERROR_MISALIGNED;
         const void* words[] = {beta, initial_state, final_state, workspace};
         for (const void* ptr : words)
@@ -238,6 +268,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
         a.bf16 = dtype == KDA_DTYPE_BF16;
         a.gate = gate;
+        a.fuse = (int)flags;
         a.cu_seqlens = varlen ? cu_seqlens_dev : nullptr;
         a.num_seqs = varlen ? num_seqs : 0;
         a.order = (varlen && num_seqs <= 65536) ? static_cast<int*>(workspace) : nullptr;
@@ -250,13 +281,13 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     }
 }
 
-kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const float* alpha,
+kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const void* alpha,
                                const float* beta, float* state, void* o, int N, int H, int dk,
-                               int dv, kda_dtype dtype, int gate, float scale,
+                               int dv, kda_dtype dtype, int gate, unsigned flags, float scale,
                                hipStream_t stream) {
     try {
         if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
-        if (!valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
+        if (!valid_gate(gate) || !valid_flags(gate, flags)) return KDA_ERROR_INVALID_VALUE;
         if (gate == KDA_GATE_NONE && alpha) return KDA_ERROR_INVALID_VALUE;
         if (N < 0 || H < 0) return KDA_ERROR_INVALID_VALUE;
         if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
@@ -268,14 +299,15 @@ kda_status recurrent_step_impl(const void* q, const void* k, const void* v, cons
         const size_t es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
         // the state is streamed as float4; everything else element by element
         if (!aligned(state, 16)) return KDA_ERROR_MISALIGNED;
+        const size_t ges = (flags & KDA_FUSE_GATE_LOGITS) ? es : 4;  // gate element size
         if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(o, es) ||
-            !aligned(alpha, 4) || !aligned(beta, 4))
+            !aligned(alpha, ges) || !aligned(beta, 4))
             return KDA_ERROR_MISALIGNED;
         const Range r_s = range_of(state, units * dk * dv * 4);
         const Range r_o = range_of(o, units * dv * es);
         const Range ins[] = {range_of(q, units * dk * es), range_of(k, units * dk * es),
                              range_of(v, units * dv * es),
-                             range_of(alpha, units * gate_width(gate, dk) * 4),
+                             range_of(alpha, units * gate_width(gate, dk) * ges),
                              range_of(beta, units * 4)};
         for (const Range& r : ins)
             if (overlap(r_s, r) || overlap(r_o, r)) return KDA_ERROR_INVALID_VALUE;
@@ -286,6 +318,7 @@ kda_status recurrent_step_impl(const void* q, const void* k, const void* v, cons
         a.N = N; a.H = H; a.dk = dk; a.dv = dv;
         a.bf16 = dtype == KDA_DTYPE_BF16;
         a.gate = gate;
+        a.fuse = (int)flags;
         a.scale = default_scale(scale, dk);
         return kda::launch_recurrent_step(a, stream) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
     } catch (...) {

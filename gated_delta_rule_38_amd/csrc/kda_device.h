@@ -20,6 +20,19 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
     return __uint_as_float(uint32_t(__builtin_bit_cast(uint16_t, x)) << 16);
 }
 
+// The logistic function 1 / (1 + e^-z), with e^-z = 2^(-z log2 e) taken by the
+// hardware base-2 exponential and the division by its reciprocal (about two
+// ulp); z -> -inf gives 0, z -> +inf gives 1.
+__device__ __forceinline__ float sigmoid_f(float z) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+// 1 / sqrt(ss + 1e-6): the scale that L2-normalises a vector with squared norm
+// ss (a zero vector stays zero)
+__device__ __forceinline__ float inv_norm(float ss) { return __builtin_amdgcn_rsqf(ss + 1e-6f); }
+
+// in-kernel input preparation (kda_fuse_flag bits)
+constexpr int FUSE_GATE_LOGITS = 1, FUSE_BETA_LOGITS = 2, FUSE_QK_L2NORM = 4;
+
 template <typename T>
 __device__ __forceinline__ T from_f32(float x);
 template <>

@@ -10,12 +10,14 @@ namespace kda {
 
 struct StepArgs {
     const void *q, *k, *v;
-    const float *alpha, *beta;
+    const void *alpha;  // float32 decays, or logits in the dtype of q (fuse & 1)
+    const float *beta;
     float *state;
     void *o;
     int N, H, dk, dv;
     bool bf16;
     int gate;  // kda_gate: 0 per channel, 1 per head, 2 none
+    int fuse;  // kda_fuse_flag bits: 1 gate logits, 2 beta logits, 4 q/k L2 norm
     float scale;
 };
 
@@ -23,13 +25,15 @@ hipError_t launch_recurrent_step(const StepArgs &a, hipStream_t stream);
 
 struct ChunkArgs {
     const void *q, *k, *v;
-    const float *alpha, *beta;
+    const void *alpha;  // float32 decays, or logits in the dtype of q (fuse & 1)
+    const float *beta;
     const float *s0;
     void *o;
     float *sT;
     int B, T, H, dk, dv;
     bool bf16;
     int gate;               // kda_gate: 0 per channel, 1 per head, 2 none
+    int fuse;               // kda_fuse_flag bits: 1 gate logits, 2 beta logits, 4 q/k L2 norm
     const int *cu_seqlens;  // device, NULL in dense mode
     int num_seqs;           // 0 in dense mode
     int *order;             // device workspace for the longest-first order (varlen), or NULL

@@ -25,15 +25,18 @@
 
 namespace kda {
 
-template <typename Tin, int DK, int DV>
+// QN: q and k are L2-normalised in-kernel (two more reductions, |k|^2 and
+// |q|^2, share the pass; every reduced quantity is linear in k or q, so the
+// norms are applied to the sums)
+template <typename Tin, int DK, int DV, bool QN>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ state,
-    Tin* __restrict__ o, float scale, int gate) {
+    const void* __restrict__ alpha_p, const float* __restrict__ beta, float* __restrict__ state,
+    Tin* __restrict__ o, float scale, int gate, int fuse) {
     constexpr int NCG = DV / 4;      // float4 column groups
     constexpr int NRG = 256 / NCG;   // row groups
     constexpr int RPG = DK / NRG;    // rows per thread
-    constexpr int NRED = 9;          // 4 x vh, 4 x p, k.q
+    constexpr int NRED = QN ? 11 : 9;  // 4 x vh, 4 x p, k.q (, |k|^2, |q|^2)
     static_assert(NCG <= 64 && 64 % NCG == 0 && RPG >= 1, "shape");
 
     __shared__ float red[4][NCG][NRED + 1];
@@ -51,19 +54,24 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     for (int r = 0; r < RPG; ++r)
         s[r] = *reinterpret_cast<const float4*>(S + (size_t)(row0 + r) * DV + cg * 4);
 
-    // the forget gate: per key channel, one per (sequence, head), or none
+    // the forget gate: per key channel, one per (sequence, head), or none;
+    // float32 decays, or logits in the dtype of q
+    const float* __restrict__ alpha = static_cast<const float*>(alpha_p);
+    const Tin* __restrict__ glog = static_cast<const Tin*>(alpha_p);
+    const bool gl = fuse & FUSE_GATE_LOGITS;
     float a[RPG], kk[RPG], qq[RPG];
-    const float ah = gate == 1 ? alpha[unit] : 1.f;
+    const float ah = gate == 1 ? (gl ? sigmoid_f(to_f32(glog[unit])) : alpha[unit]) : 1.f;
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
-        a[r] = gate == 0 ? alpha[(size_t)unit * DK + row0 + r] : ah;
+        const size_t ai = (size_t)unit * DK + row0 + r;
+        a[r] = gate == 0 ? (gl ? sigmoid_f(to_f32(glog[ai])) : alpha[ai]) : ah;
         kk[r] = to_f32(k[(size_t)unit * DK + row0 + r]);
         qq[r] = to_f32(q[(size_t)unit * DK + row0 + r]);
     }
     float vv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) vv[j] = to_f32(v[(size_t)unit * DV + cg * 4 + j]);
-    const float b = beta[unit];
+    const float b = (fuse & FUSE_BETA_LOGITS) ? sigmoid_f(beta[unit]) : beta[unit];
 
     // forget, then the partial reductions over this thread's rows
     float part[NRED];
@@ -77,6 +85,10 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
         part[4] += qq[r] * s[r].x; part[5] += qq[r] * s[r].y;
         part[6] += qq[r] * s[r].z; part[7] += qq[r] * s[r].w;
         part[8] += kk[r] * qq[r];
+        if constexpr (QN) {
+            part[9] += kk[r] * kk[r];
+            part[10] += qq[r] * qq[r];
+        }
     }
     // across the row groups that share a wavefront
 #pragma unroll
@@ -95,6 +107,14 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     for (int i = 0; i < NRED; ++i)
         tot[i] = red[0][cg][i] + red[1][cg][i] + red[2][cg][i] + red[3][cg][i];
 
+    if constexpr (QN) {  // the sums of the normalised k and q
+        const float ik = inv_norm(tot[9]), iq = inv_norm(tot[10]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { tot[j] *= ik; tot[4 + j] *= iq; }
+        tot[8] *= ik * iq;
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) kk[r] *= ik;
+    }
     // correct: e = beta (v - vh); read: o = scale (p + e (k.q))
     float e[4];
 #pragma unroll
@@ -120,10 +140,16 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 template <typename Tin, int DK, int DV>
 static hipError_t launch_step_t(const StepArgs& a, hipStream_t stream) {
     const int units = a.N * a.H;
-    hipLaunchKernelGGL((recurrent_step_kernel<Tin, DK, DV>), dim3(units), dim3(256), 0, stream,
-                       static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
-                       static_cast<const Tin*>(a.v), a.alpha, a.beta, a.state,
-                       static_cast<Tin*>(a.o), a.scale, a.gate);
+    if (a.fuse & FUSE_QK_L2NORM)
+        hipLaunchKernelGGL((recurrent_step_kernel<Tin, DK, DV, true>), dim3(units), dim3(256), 0,
+                           stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+                           static_cast<const Tin*>(a.v), a.alpha, a.beta, a.state,
+                           static_cast<Tin*>(a.o), a.scale, a.gate, a.fuse);
+    else
+        hipLaunchKernelGGL((recurrent_step_kernel<Tin, DK, DV, false>), dim3(units), dim3(256), 0,
+                           stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+                           static_cast<const Tin*>(a.v), a.alpha, a.beta, a.state,
+                           static_cast<Tin*>(a.o), a.scale, a.gate, a.fuse);
     return hipGetLastError();
 }
 

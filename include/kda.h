@@ -83,6 +83,31 @@ typedef enum {
 } kda_gate;
 
 /*
+ * In-kernel preparation of the inputs (flags of the *_fused entry points),
+ * so that the raw outputs of the projections that produce them need no
+ * separate pass over HBM:
+ * KDA_FUSE_GATE_LOGITS: `gate` holds logits z in the dtype of q (bf16 or
+ *   float32) and the decay is alpha = sigmoid(z) = 1 / (1 + exp(-z)),
+ *   evaluated in float32 as 1 / (1 + 2^(-z log2 e)), which keeps alpha in
+ *   (0, 1) as the per-channel decay of "Kimi Delta Attention", section
+ *   "一、Diag(α_t)：通道级遗忘" requires.  Without the flag `gate` holds
+ *   alpha itself in float32.
+ * KDA_FUSE_BETA_LOGITS: `beta` holds logits b (float32) and the write
+ *   strength is beta = sigmoid(b), in (0, 1) (the data-dependent update
+ *   strength listed under "在DeltaNet基础上的进一步演进" on the kongchang.com
+ *   page).
+ * KDA_FUSE_QK_L2NORM: q and k are divided by their L2 norm per token and
+ *   head, x / sqrt(sum x^2 + 1e-6), in float32 before any other use (with
+ *   unit keys, beta = 1 makes the write an exact overwrite: bugfactory.tech
+ *   news 3610, second paragraph).
+ */
+typedef enum {
+    KDA_FUSE_GATE_LOGITS = 1,
+    KDA_FUSE_BETA_LOGITS = 2,
+    KDA_FUSE_QK_L2NORM = 4
+} kda_fuse_flag;
+
+/*
  * Device workspace (bytes) that kda_chunk_fwd needs.  Dense calls
  * (num_seqs == 0) need none; packed variable-length calls need 4 bytes per
  * sequence (rounded up to 256), used to order sequences longest first.
@@ -144,6 +169,23 @@ kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, cons
                                hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_gated with in-kernel input preparation: `flags` is a bitwise
+ * OR of kda_fuse_flag values (0 gives kda_chunk_fwd_gated exactly).  With
+ * KDA_FUSE_GATE_LOGITS, `gate` has the shape of alpha for `gate_kind` and the
+ * dtype of q; without it, `gate` is the float32 alpha.  KDA_GATE_NONE takes
+ * gate == NULL and no KDA_FUSE_GATE_LOGITS.  Alignment: q, k and a
+ * per-channel gate 8 bytes, a per-head gate its element size.  Errors as
+ * for kda_chunk_fwd_gated, plus KDA_ERROR_INVALID_VALUE for unknown flags.
+ */
+kda_status kda_chunk_fwd_fused(const void *q, const void *k, const void *v, const void *gate,
+                               const float *beta, const float *initial_state, void *o,
+                               float *final_state, int B, int T, int H, int dk, int dv,
+                               kda_dtype dtype, kda_gate gate_kind, unsigned flags,
+                               const int *cu_seqlens_dev, const int *cu_seqlens_host,
+                               int num_seqs, float scale, int chunk_size, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step, state updated in place.
  * Source: the fused recurrent mode of bugfactory.tech news 3610, fifth
  * paragraph (the sequence is processed token by token, state tiles updated
@@ -170,6 +212,16 @@ kda_status kda_recurrent_step_gated(const void *q, const void *k, const void *v,
                                     const float *alpha, const float *beta, float *state,
                                     void *o, int N, int H, int dk, int dv, kda_dtype dtype,
                                     kda_gate gate, float scale, hipStream_t stream);
+
+/*
+ * kda_recurrent_step_gated with in-kernel input preparation: `flags` and
+ * `gate` as for kda_chunk_fwd_fused ([N, H, dk], [N, H] or NULL).
+ */
+kda_status kda_recurrent_step_fused(const void *q, const void *k, const void *v,
+                                    const void *gate, const float *beta, float *state, void *o,
+                                    int N, int H, int dk, int dv, kda_dtype dtype,
+                                    kda_gate gate_kind, unsigned flags, float scale,
+                                    hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *kda_status_string(kda_status status);

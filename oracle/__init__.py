@@ -92,6 +92,33 @@ def channel_gate(alpha, gate, dk, lead=None):
     raise ValueError("unknown gate %r" % (gate,))
 
 
+def prepare(q, k, alpha, beta, gate="channel", gate_logits=False, beta_logits=False,
+            qk_l2norm=False, lead=None):
+    """The inputs the recurrence takes, from the stored tensors of a call with
+    in-kernel input preparation, as float64 (q, k, per-channel alpha, beta).
+
+    gate_logits: alpha holds logits z and the decay is the logistic function
+    1 / (1 + exp(-z)), which maps any logit into (0, 1) as the per-channel
+    decay of "Kimi Delta Attention", section "一、Diag(α_t)：通道级遗忘"
+    requires; beta_logits: the same map for the write strength beta.
+    qk_l2norm: q and k divided by sqrt(sum of squares + 1e-6) per token and
+    head.  gate and lead as for channel_gate.
+    """
+    q, k = _f64(q), _f64(k)
+    dk = q.shape[-1]
+    if qk_l2norm:
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + 1e-6)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + 1e-6)
+    a = None if alpha is None else _f64(alpha)
+    if gate_logits:
+        a = 1.0 / (1.0 + np.exp(-a))
+    a = channel_gate(a, gate, dk, q.shape[:-1] if lead is None else lead)
+    b = _f64(beta)
+    if beta_logits:
+        b = 1.0 / (1.0 + np.exp(-b))
+    return q, k, a, b
+
+
 def forward_units(q, k, v, alpha, beta, initial_state=None, scale=None, threads=0,
                   want_o=True):
     """Token loop over independent units.

@@ -31,9 +31,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_step",
-              "kda_recurrent_step_gated", "kda_chunk_fwd_workspace_size", "kda_status_string",
-              "kda_version"]:
+    for n in ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused", "kda_recurrent_step",
+              "kda_recurrent_step_gated", "kda_recurrent_step_fused",
+              "kda_chunk_fwd_workspace_size", "kda_status_string", "kda_version"]:
         assert n in names, names
 
 
@@ -227,6 +227,65 @@ def test_step_gated_rejects_before_any_hip_call(lib, gate, kw, code):
     assert step_gated_call(lib, gate, **kw) == code
 
 
+GL, BL, QN = 1, 2, 4
+
+
+def chunk_fused_call(lib, gate, flags, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), s0=fake(5), o=fake(6),
+             sT=fake(7), B=2, T=100, H=4, dk=128, dv=128, dt=1, cu_dev=None, cu_host=None,
+             num_seqs=0, scale=0.0, chunk=64, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_fused(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"],
+                                   a["o"], a["sT"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                   a["dt"], gate, flags, a["cu_dev"], a["cu_host"],
+                                   a["num_seqs"], a["scale"], a["chunk"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
+
+
+def step_fused_call(lib, gate, flags, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), state=fake(5),
+             o=fake(6), N=8, H=4, dk=128, dv=128, dt=1, scale=0.0, stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_step_fused(a["q"], a["k"], a["v"], a["alpha"], a["beta"],
+                                        a["state"], a["o"], a["N"], a["H"], a["dk"], a["dv"],
+                                        a["dt"], gate, flags, a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("gate,flags,kw,code", [
+    (GATE_CHANNEL, 8, {}, INVALID),                                  # unknown flag bit
+    (GATE_CHANNEL, 0x80000000, {}, INVALID),
+    (GATE_NONE, GL, dict(alpha=None), INVALID),                      # logits without a gate
+    (GATE_HEAD, GL | QN, dict(alpha=None), INVALID),
+    (GATE_CHANNEL, GL, dict(alpha=fake(3, 4)), MISALIGNED),          # per-channel: 8 bytes
+    (GATE_HEAD, GL, dict(alpha=fake(3, 1)), MISALIGNED),             # bf16 per head: 2 bytes
+    (GATE_HEAD, 0, dict(alpha=fake(3, 2)), MISALIGNED),              # float32 per head: 4 bytes
+    # a 2-byte aligned bf16 per-head logit passes and the call fails on the overlap
+    (GATE_HEAD, GL, dict(alpha=fake(3, 2), sT=fake(6, 512)), INVALID),
+    # bf16 per-channel logits span B*T*H*dk*2 bytes: a final state 4 KB past
+    # their start overlaps them
+    (GATE_CHANNEL, GL | BL | QN, dict(sT=fake(3, 4096)), INVALID),
+    (GATE_CHANNEL, GL | BL | QN, dict(dk=96), NOT_SUPPORTED),
+    (GATE_NONE, QN | BL, dict(alpha=None, o=None), INVALID),
+])
+def test_chunk_fused_rejects_before_any_hip_call(lib, gate, flags, kw, code):
+    assert chunk_fused_call(lib, gate, flags, **kw) == code
+
+
+def test_fused_empty_is_a_noop(lib):
+    assert chunk_fused_call(lib, GATE_CHANNEL, GL | BL | QN, B=0) == SUCCESS
+    assert step_fused_call(lib, GATE_HEAD, GL | BL | QN, N=0) == SUCCESS
+
+
+@pytest.mark.parametrize("gate,flags,kw,code", [
+    (GATE_CHANNEL, 16, {}, INVALID),
+    (GATE_NONE, GL, dict(alpha=None), INVALID),
+    (GATE_HEAD, GL, dict(alpha=fake(3, 1)), MISALIGNED),
+    (GATE_CHANNEL, GL | QN, dict(state=fake(3, 0)), INVALID),        # state aliasing the logits
+])
+def test_step_fused_rejects_before_any_hip_call(lib, gate, flags, kw, code):
+    assert step_fused_call(lib, gate, flags, **kw) == code
+
+
 def test_python_binding_checks_arguments():
     import torch
     import gated_delta_rule_38_amd as kda
@@ -245,3 +304,6 @@ def test_python_binding_checks_arguments():
     s = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         kda.kda_recurrent_step_gated(q[0], q[0], q[0], q[0], b[0], s, gate="head")
+    with pytest.raises(TypeError):  # gate logits come in the dtype of q (bf16 here)
+        qb = q.to(torch.bfloat16)
+        kda.kda_chunk_fwd_fused(qb, qb, qb, q, b)

@@ -304,3 +304,57 @@ def test_head_and_no_gate_through_the_token_layout(seed):
             assert rel(o_n[b, :, h], o_r) < TOL and rel(s_n[b, h], s_r) < TOL
     with pytest.raises(ValueError):
         oracle.channel_gate(g, "scalar", dk)
+
+
+def test_prepare_logistic_and_norm_fixed_points():
+    """oracle.prepare: the logistic map at points where it is known exactly
+    (1/2 at 0, 3/4 at ln 3, 1/4 at -ln 3), and the L2 normalisation: unit rows
+    parallel to the stored ones, zero rows left zero."""
+    z = np.array([[0.0, np.log(3.0), -np.log(3.0)]])
+    q = np.array([[[3.0, 4.0, 0.0]], [[0.0, 0.0, 0.0]]])  # [2 tokens, 1 head, 3]
+    k = np.array([[[1.0, 2.0, 2.0]], [[0.0, 5.0, 0.0]]])
+    qn, kn, a, b = oracle.prepare(q, k, np.repeat(z, 2, 0)[:, None, :], z[:, :2].T,
+                                  gate_logits=True, beta_logits=True, qk_l2norm=True)
+    assert np.allclose(a[0, 0], [0.5, 0.75, 0.25], rtol=0, atol=1e-15)
+    assert np.allclose(b[:, 0], [0.5, 0.75], rtol=0, atol=1e-15)
+    e = 1e-6
+    assert np.allclose(qn[0, 0], np.array([3.0, 4.0, 0.0]) / np.sqrt(25 + e), rtol=1e-15)
+    assert np.array_equal(qn[1, 0], np.zeros(3))
+    assert np.allclose(kn[:, 0], [[1 / 3, 2 / 3, 2 / 3], [0, 1, 0]], atol=1e-7)
+    # per-head logits: one decay repeated over the channels
+    _, _, ah, _ = oracle.prepare(q, k, z[:, :2].T, z[:, :2].T, gate="head", gate_logits=True)
+    assert np.allclose(ah[:, 0], [[0.5] * 3, [0.75] * 3], atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prepared_forward_is_scale_invariant_in_q_and_k(seed):
+    """With in-kernel normalisation the result depends on q and k only through
+    their directions: positive per-token scalings of the stored q and k leave
+    the prepared forward unchanged (the 1e-6 inside the root aside)."""
+    rng = np.random.default_rng(20 + seed)
+    B, T, H, dk, dv = 1, 9, 2, 6, 4
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    z = rng.normal(3.0, 1.0, (B, T, H, dk))
+    bl = rng.standard_normal((B, T, H))
+    s0 = 0.1 * rng.standard_normal((B, H, dk, dv))
+    cq = rng.uniform(5.0, 50.0, (B, T, H, 1))
+    ck = rng.uniform(5.0, 50.0, (B, T, H, 1))
+    flags = dict(gate_logits=True, beta_logits=True, qk_l2norm=True)
+    o1, s1 = _fwd_kw(*_prep4(q, k, z, bl, flags), v, s0)
+    o2, s2 = _fwd_kw(*_prep4(cq * q, ck * k, z, bl, flags), v, s0)
+    assert rel(o2, o1) < 1e-6 and rel(s2, s1) < 1e-6
+    # and without the map, logits are not decays: a different result
+    o3, _ = _fwd_kw(*_prep4(q, k, np.clip(z, 0.0, 1.0), bl, dict(flags, gate_logits=False)),
+                    v, s0)
+    assert rel(o3, o1) > 1e-2
+
+
+def _prep4(q, k, z, bl, flags):
+    qn, kn, a, b = oracle.prepare(q, k, z, bl, **flags)
+    return qn, kn, a, b
+
+
+def _fwd_kw(qn, kn, a, b, v, s0):
+    return oracle.forward(qn, kn, v, a, b, s0)

@@ -22,39 +22,49 @@ def _unit(x):
     return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
 
 
-def _alpha(lead, dk, gate, g, device, mu, sigma=1.0):
+def _alpha(lead, dk, gate, g, device, mu, sigma=1.0, logits=False, dtype=torch.float32):
     """Forget gates sigmoid(N(mu, sigma)): [*lead, dk] per channel, [*lead]
-    per head, None without a gate (nothing drawn)."""
+    per head, None without a gate (nothing drawn).  logits=True stores the
+    N(mu, sigma) draws themselves in ``dtype``."""
     if gate == "none":
         return None
     shape = tuple(lead) + ((dk,) if gate == "channel" else ())
     if gate not in ("channel", "head"):
         raise ValueError("unknown gate %r" % (gate,))
-    return torch.sigmoid(_normal(shape, g, device, mu, sigma)).to(torch.float32).contiguous()
+    z = _normal(shape, g, device, mu, sigma)
+    if logits:
+        return z.to(dtype).contiguous()
+    return torch.sigmoid(z).to(torch.float32).contiguous()
 
 
 def draw_chunk(B, T, H, dk, dv, dtype="bf16", alpha_mu=4.0, alpha_sigma=1.0, s0_std=None,
-               num_states=None, seed=0, device="cpu", lengths=None, gate="channel"):
+               num_states=None, seed=0, device="cpu", lengths=None, gate="channel",
+               raw=False):
     """Draw one chunked-forward input set.
 
     Returns a dict with q, k [B,T,H,dk] and v [B,T,H,dv] in the storage dtype,
     alpha [B,T,H,dk] (gate "channel"), [B,T,H] ("head") or None ("none") and
     beta [B,T,H] in float32, initial_state [num_states or B, H, dk, dv]
-    float32 (or None), on ``device``.
+    float32 (or None), on ``device``.  raw=True draws the same values but
+    stores what in-kernel preparation takes: q and k not normalised, and
+    the logits of alpha (in the storage dtype) and of beta (float32).
     """
     g = _gen(device, seed)
     dt = _DT[dtype]
-    q = _unit(_normal((B, T, H, dk), g, device)).to(dt)
-    k = _unit(_normal((B, T, H, dk), g, device)).to(dt)
+    prep = (lambda x: x) if raw else _unit
+    q = prep(_normal((B, T, H, dk), g, device)).to(dt)
+    k = prep(_normal((B, T, H, dk), g, device)).to(dt)
     v = _normal((B, T, H, dv), g, device).to(dt)
-    beta = torch.sigmoid(_normal((B, T, H), g, device)).to(torch.float32)
-    alpha = _alpha((B, T, H), dk, gate, g, device, alpha_mu, alpha_sigma)
+    beta = _normal((B, T, H), g, device)
+    beta = (beta if raw else torch.sigmoid(beta)).to(torch.float32)
+    alpha = _alpha((B, T, H), dk, gate, g, device, alpha_mu, alpha_sigma, logits=raw,
+                   dtype=dt)
     ns = B if num_states is None else num_states
     s0 = None
     if s0_std is not None:
         s0 = _normal((ns, H, dk, dv), g, device, 0.0, s0_std).to(torch.float32)
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), alpha=alpha,
-                beta=beta.contiguous(), initial_state=s0, gate=gate)
+                beta=beta.contiguous(), initial_state=s0, gate=gate, raw=raw)
 
 
 def varlen_lengths(num_seqs, lo, hi, seed):
@@ -63,7 +73,8 @@ def varlen_lengths(num_seqs, lo, hi, seed):
     return [int(x) for x in torch.randint(lo, hi + 1, (num_seqs,), generator=g)]
 
 
-def chunk_inputs(cfg, device="cpu", T=None, B=None, H=None, seed=None, gate="channel"):
+def chunk_inputs(cfg, device="cpu", T=None, B=None, H=None, seed=None, gate="channel",
+                 raw=False):
     """Inputs of a chunked-forward workload; T/B/H override the sizes for
     reduced versions and ``gate`` the forget gate's granularity (the same
     draws otherwise).  Varlen workloads also get cu_seqlens (host list and an
@@ -79,18 +90,20 @@ def chunk_inputs(cfg, device="cpu", T=None, B=None, H=None, seed=None, gate="cha
         for l in lens:
             cu.append(cu[-1] + l)
         d = draw_chunk(1, cu[-1], H, cfg.dk, cfg.dv, cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std,
-                       num_states=len(lens), seed=seed, device=device, gate=gate)
+                       num_states=len(lens), seed=seed, device=device, gate=gate, raw=raw)
         d["cu_seqlens_host"] = cu
         d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=device)
         return d
     d = draw_chunk(cfg.B if B is None else B, cfg.T if T is None else T, H, cfg.dk, cfg.dv,
-                   cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std, seed=seed, device=device, gate=gate)
+                   cfg.dtype, cfg.alpha_mu, 1.0, cfg.s0_std, seed=seed, device=device, gate=gate,
+                   raw=raw)
     d["cu_seqlens_host"] = None
     d["cu_seqlens"] = None
     return d
 
 
-def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None, gate="channel"):
+def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None, gate="channel",
+                  raw=False):
     """Decode workload: initial state [N,H,dk,dv] float32 and per-step inputs
     stacked on a leading step axis: q, k [S,N,H,dk], v [S,N,H,dv] (storage
     dtype), alpha [S,N,H,dk] (gate "channel"), [S,N,H] ("head") or None
@@ -102,10 +115,12 @@ def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None, gate
     g = _gen(device, seed)
     dt = _DT[cfg.dtype]
     state = _normal((N, H, cfg.dk, cfg.dv), g, device, 0.0, cfg.s0_std).to(torch.float32)
-    q = _unit(_normal((steps, N, H, cfg.dk), g, device)).to(dt)
-    k = _unit(_normal((steps, N, H, cfg.dk), g, device)).to(dt)
+    prep = (lambda x: x) if raw else _unit
+    q = prep(_normal((steps, N, H, cfg.dk), g, device)).to(dt)
+    k = prep(_normal((steps, N, H, cfg.dk), g, device)).to(dt)
     v = _normal((steps, N, H, cfg.dv), g, device).to(dt)
-    beta = torch.sigmoid(_normal((steps, N, H), g, device)).to(torch.float32)
-    alpha = _alpha((steps, N, H), cfg.dk, gate, g, device, cfg.alpha_mu)
+    beta = _normal((steps, N, H), g, device)
+    beta = (beta if raw else torch.sigmoid(beta)).to(torch.float32)
+    alpha = _alpha((steps, N, H), cfg.dk, gate, g, device, cfg.alpha_mu, logits=raw, dtype=dt)
     return dict(state=state.contiguous(), q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
-                alpha=alpha, beta=beta.contiguous(), gate=gate)
+                alpha=alpha, beta=beta.contiguous(), gate=gate, raw=raw)
