@@ -9,10 +9,12 @@ state in place, 100 consecutive steps) as GB/s against the HBM roofline.
 With --gate head (one decay per token and head: Gated DeltaNet) or --gate
 none (no forget gate: DeltaNet) the same workloads run through the *_gated
 entry points with alpha drawn per head (or absent); the default is the
-per-channel gate of KDA.
+per-channel gate of KDA.  With --fused the inputs are stored raw (gate
+logits in bf16, beta logits, q and k not normalised) and the *_fused entry
+points prepare them in the kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--calib-copy] [--skip-decode] [--gate channel|head|none]
+                       [--calib-copy] [--skip-decode] [--gate channel|head|none] [--fused]
 """
 import argparse
 import hashlib
@@ -71,20 +73,21 @@ GATE_WIDTH = {"channel": lambda dk: dk, "head": lambda dk: 1, "none": lambda dk:
 GATE_NAME = {"channel": "KDA", "head": "Gated DeltaNet", "none": "DeltaNet"}
 
 
-def chunk_bytes(B, T, H, dk, dv, es=2, nstates=None, gate="channel"):
+def chunk_bytes(B, T, H, dk, dv, es=2, nstates=None, gate="channel", ges=4):
     """Algorithmic HBM bytes of one chunk-wise forward: every input read once,
-    every output written once."""
+    every output written once (ges: bytes per gate element, 4 for float32
+    alpha, es for logits in the storage dtype)."""
     ns = B if nstates is None else nstates
     tok = B * T * H
     aw = GATE_WIDTH[gate](dk)
-    return (tok * (2 * dk * es + dv * es + aw * 4 + 4 + dv * es)  # q, k, v, alpha, beta, o
-            + 2 * ns * H * dk * dv * 4)                            # initial + final state
+    return (tok * (2 * dk * es + dv * es + aw * ges + 4 + dv * es)  # q, k, v, alpha, beta, o
+            + 2 * ns * H * dk * dv * 4)                              # initial + final state
 
 
-def decode_bytes(N, H, dk, dv, es=2, gate="channel"):
+def decode_bytes(N, H, dk, dv, es=2, gate="channel", ges=4):
     """Algorithmic HBM bytes of one decode step."""
     aw = GATE_WIDTH[gate](dk)
-    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + aw * 4 + 4 + dv * es)
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + aw * ges + 4 + dv * es)
 
 
 def main():
@@ -102,8 +105,14 @@ def main():
     ap.add_argument("--gate", choices=sorted(GATE_WIDTH), default="channel",
                     help="forget gate: per key channel (KDA, the default), per head (Gated "
                          "DeltaNet) or none (DeltaNet)")
+    ap.add_argument("--fused", action="store_true",
+                    help="raw inputs (bf16 gate logits, beta logits, q and k not normalised) "
+                         "prepared in the kernel")
     args = ap.parse_args()
     gate = args.gate
+    fused = args.fused
+    fl = dict(gate_logits=gate != "none", beta_logits=True, qk_l2norm=True)
+    ges = 2 if fused else 4
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the workload shards by (batch, head) with no exchange; see DESIGN.md). "
@@ -117,13 +126,16 @@ def main():
     dev = torch.device("cuda:0")
     kda.load_library()
     cfg = CONFIGS[1]
-    d = gen.chunk_inputs(cfg, device=dev, gate=gate)
+    d = gen.chunk_inputs(cfg, device=dev, gate=gate, raw=fused)
     B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
     o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     fs = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
 
     def step():
-        if gate == "channel":
+        if fused:
+            kda.kda_chunk_fwd_fused(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                    d["initial_state"], o=o, final_state=fs, gate_kind=gate, **fl)
+        elif gate == "channel":
             kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
                               o=o, final_state=fs)
         else:
@@ -147,16 +159,21 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     tokens = B * T
     value = tokens * args.steps / (ms * args.steps / 1e3)
-    alg = chunk_bytes(B, T, H, dk, dv, gate=gate)
+    alg = chunk_bytes(B, T, H, dk, dv, gate=gate, ges=ges)
     achieved = alg / (ms / 1e3) / 1e9
-    traffic = measured_traffic("chunk_fwd_bf16_kernel" + ("" if gate == "channel" else
-                                                          "[gate=%s]" % gate))
+    variant = ([] if gate == "channel" else ["gate=%s" % gate]) + (["fused"] if fused else [])
+    traffic = measured_traffic("chunk_fwd_bf16_kernel" +
+                               ("[%s]" % ",".join(variant) if variant else ""))
     gname = GATE_NAME[gate]
     wl = {"channel": "kda_chunk_fwd", "head": "kda_chunk_fwd_gated (per-head alpha)",
           "none": "kda_chunk_fwd_gated (no gate)"}[gate]
+    if fused:
+        wl = ("kda_chunk_fwd_fused (%s gate, bf16 gate logits, beta logits, q/k L2 norm "
+              "in-kernel)" % gate)
 
     out = {
-        "metric": "%s chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline" % gname,
+        "metric": "%s%s chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline" % (
+            gname, " (fused input preparation)" if fused else ""),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -181,14 +198,16 @@ def main():
 
     if not args.skip_decode:
         dc = CONFIGS[3]
-        dd = gen.decode_inputs(dc, device=dev, gate=gate)
+        dd = gen.decode_inputs(dc, device=dev, gate=gate, raw=fused)
         state = dd["state"].clone()
         od = torch.empty((dc.B, dc.H, dc.dv), dtype=torch.bfloat16, device=dev)
         sargs = [[None if dd[n] is None else dd[n][t] for n in ("q", "k", "v", "alpha", "beta")]
                  for t in range(dc.steps)]
 
         def dstep(t, st):
-            if gate == "channel":
+            if fused:
+                kda.kda_recurrent_step_fused(*sargs[t], st, o=od, gate_kind=gate, **fl)
+            elif gate == "channel":
                 kda.kda_recurrent_step(*sargs[t], st, o=od)
             else:
                 kda.kda_recurrent_step_gated(*sargs[t], st, o=od, gate=gate)
@@ -205,17 +224,19 @@ def main():
         f1.record(stream)
         torch.cuda.synchronize()
         us = f0.elapsed_time(f1) * 1e3 / dc.steps
-        dbytes = decode_bytes(dc.B, dc.H, dc.dk, dc.dv, gate=gate)
+        dbytes = decode_bytes(dc.B, dc.H, dc.dk, dc.dv, gate=gate, ges=ges)
         gbs = dbytes / (us / 1e6) / 1e9
         out["decode"] = {
             "workload": "%s bf16 N256 H32 dk128 dv128, fp32 state in place, "
-                        "100 consecutive steps" % ("kda_recurrent_step" if gate == "channel" else
-                                                   "kda_recurrent_step_gated (gate %s)" % gate),
+                        "100 consecutive steps" % (
+                            "kda_recurrent_step_fused (gate %s)" % gate if fused else
+                            "kda_recurrent_step" if gate == "channel" else
+                            "kda_recurrent_step_gated (gate %s)" % gate),
             "us_per_step": us, "tokens_per_s": dc.B / (us / 1e6),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("recurrent_step_kernel") if gate == "channel"
-                         else None,
+                         "traffic": measured_traffic("recurrent_step_kernel")
+                         if gate == "channel" and not fused else None,
                          "kernel": "recurrent_step_kernel",
                          "algorithmic_bytes_per_launch": dbytes},
         }
@@ -239,10 +260,14 @@ def main():
         s0 = d["initial_state"].cpu().reshape(B * H, dk, dv)
         cores = min(len(os.sched_getaffinity(0)), B * H)
         c0 = time.perf_counter()
-        alpha = oracle.channel_gate(None if d["alpha"] is None else units(d["alpha"]), gate, dk,
-                                    (B * H, T))
-        oracle.forward_units(host["q"], host["k"], host["v"], alpha, host["beta"], s0,
-                             threads=cores)
+        a_units = None if d["alpha"] is None else units(d["alpha"])
+        if fused:
+            qh, kh, alpha, bh = oracle.prepare(host["q"], host["k"], a_units, host["beta"], gate,
+                                               lead=(B * H, T), **fl)
+        else:
+            qh, kh, bh = host["q"], host["k"], host["beta"]
+            alpha = oracle.channel_gate(a_units, gate, dk, (B * H, T))
+        oracle.forward_units(qh, kh, host["v"], alpha, bh, s0, threads=cores)
         cw = time.perf_counter() - c0
         out["cpu_baseline"] = {"value": tokens / cw, "unit": "tokens/s", "cores": cores,
                                "kind": "oracle",

@@ -552,8 +552,13 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             // pr0 + 3), the running products pr over the lane's rows, and u (Pm
             // in 16-lane row 0, Pn / Pm in row 3); index ai(c) for channel c
             auto ai = [](int c) { return GATE == 0 ? c : 0; };
-            // the decays of the lane's rows: stored alpha, or sigmoid of the
-            // stored logits, formed once here (rows past the end decay by 1)
+            // The decays of the lane's rows: stored alpha, or from the stored
+            // logits, formed once here (rows past the end decay by 1).  From
+            // per-channel logits the scan below runs on 1 / alpha = 1 + e^-z,
+            // which needs no reciprocal per element: every product it forms is
+            // then the inverse of the one it stands for, so P_r / Pm and
+            // Pm / P_r trade places and the vector entries are inverted.
+            constexpr bool INV = GL && GATE == 0;
             float al[GL ? 4 : 1][GL ? NA : 1];
             if constexpr (GL) {
 #pragma unroll
@@ -561,7 +566,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 #pragma unroll
                     for (int c = 0; c < NA; ++c) {
                         const uint32_t wd = RA[NAW * rr + c / 2];
-                        al[rr][c] = (pr0 + rr < nval) ? sigmoid_f((c & 1) ? hi_f(wd) : lo_f(wd)) : 1.f;
+                        const float z = (c & 1) ? hi_f(wd) : lo_f(wd);
+                        if constexpr (INV)
+                            al[rr][c] = (pr0 + rr < nval) ? 1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z) : 1.f;
+                        else
+                            al[rr][c] = (pr0 + rr < nval) ? sigmoid_f(z) : 1.f;
                     }
             }
             auto alv = [&](int rr, int c) {
@@ -639,9 +648,12 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             if (rg == 0 || rg == 12) {
                 float* vec = reinterpret_cast<float*>(buf(par, L::bVec)) + (rg == 0 ? 0 : 2 * DK);
 #pragma unroll
-                for (int c = 0; c < CPL; c += 4)
-                    *reinterpret_cast<float4*>(vec + pc0 + c) =
-                        make_float4(u[ai(c)], u[ai(c + 1)], u[ai(c + 2)], u[ai(c + 3)]);
+                for (int c = 0; c < CPL; c += 4) {
+                    float4 v4 = make_float4(u[ai(c)], u[ai(c + 1)], u[ai(c + 2)], u[ai(c + 3)]);
+                    if constexpr (INV)
+                        v4 = make_float4(fast_rcp(v4.x), fast_rcp(v4.y), fast_rcp(v4.z), fast_rcp(v4.w));
+                    *reinterpret_cast<float4*>(vec + pc0 + c) = v4;
+                }
             }
             // rows from the last to the first: g_r = Pm / P_r = g_{r+1} * alpha_{r+1}
             uint32_t kcp[CPL / 2];  // Kc of row rr + 1 (the odd row of the current pair)
@@ -671,17 +683,18 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                             g[c0] *= alv(rr + 1, c0);
                             g[c1] *= alv(rr + 1, c1);
                         }
-                        const float r0 = pr[rr][c0] * f[c0], r1 = pr[rr][c1] * f[c1];
-                        const float k0 = lo_f(kw), k1 = hi_f(kw);
+                        const float p0 = pr[rr][c0] * f[c0], p1 = pr[rr][c1] * f[c1];
+                        // P_r / Pm and Pm / P_r (swapped when the scan ran on 1 / alpha)
+                        const float r0 = INV ? g[c0] : p0, r1 = INV ? g[c1] : p1;
+                        const float h0 = INV ? p0 : g[c0], h1 = INV ? p1 : g[c1];
+                        float k0 = lo_f(kw), k1 = hi_f(kw), q0 = lo_f(qw), q1 = hi_f(qw);
                         if constexpr (QN) {
-                            kr[i] = pack2(k0 * (r0 * ik[rr]), k1 * (r1 * ik[rr]));
-                            qr[i] = pack2(lo_f(qw) * (r0 * iq[rr]), hi_f(qw) * (r1 * iq[rr]));
-                            kc[i] = pack2(k0 * (g[c0] * ik[rr]), k1 * (g[c1] * ik[rr]));
-                        } else {
-                            kr[i] = pack2(k0 * r0, k1 * r1);
-                            qr[i] = pack2(lo_f(qw) * r0, hi_f(qw) * r1);
-                            kc[i] = pack2(k0 * g[c0], k1 * g[c1]);
+                            k0 *= ik[rr]; k1 *= ik[rr];
+                            q0 *= iq[rr]; q1 *= iq[rr];
                         }
+                        kr[i] = pack2(k0 * r0, k1 * r1);
+                        qr[i] = pack2(q0 * r0, q1 * r1);
+                        kc[i] = pack2(k0 * h0, k1 * h1);
                     } else {  // one decay for the token
                         const float k0 = lo_f(kw), k1 = hi_f(kw);
                         kr[i] = pack2(k0 * rrk, k1 * rrk);
