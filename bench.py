@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="raw inputs (bf16 gate logits, beta logits, q and k not normalised) "
                          "prepared in the kernel")
+    ap.add_argument("--prep-baseline", action="store_true",
+                    help="with --fused: also time the same preparation done by torch "
+                         "elementwise kernels followed by the plain entry point")
     args = ap.parse_args()
     gate = args.gate
     fused = args.fused
@@ -195,6 +198,37 @@ def main():
                      "avg_launch_ms": ms},
         "timed_wall_s": wall,
     }
+
+    if fused and args.prep_baseline:
+        def prep():
+            qn = torch.nn.functional.normalize(d["q"].float(), dim=-1, eps=1e-3).to(d["q"].dtype)
+            kn = torch.nn.functional.normalize(d["k"].float(), dim=-1, eps=1e-3).to(d["k"].dtype)
+            a = None if d["alpha"] is None else torch.sigmoid(d["alpha"].float())
+            return qn, kn, a, torch.sigmoid(d["beta"])
+
+        def unfused():
+            qn, kn, a, b = prep()
+            kda.kda_chunk_fwd_gated(qn, kn, d["v"], a, b, d["initial_state"], o=o, final_state=fs,
+                                    gate=gate)
+
+        def time_fn(fn, n):
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for _ in range(n):
+                fn()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            return g0.elapsed_time(g1) / n
+        n = max(10, args.steps // 2)
+        out["prep_baseline"] = {
+            "what": "torch elementwise preparation (normalise q and k, sigmoid of the logits) "
+                    "then kda_chunk_fwd_gated, same inputs",
+            "prep_ms": time_fn(prep, n), "prep_plus_chunk_ms": time_fn(unfused, n),
+            "fused_ms": ms}
 
     if not args.skip_decode:
         dc = CONFIGS[3]
