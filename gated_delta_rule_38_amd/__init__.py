@@ -14,7 +14,8 @@ import os
 import torch
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused", "kda_recurrent_step",
-           "kda_recurrent_step_gated", "kda_recurrent_step_fused", "kda_chunk_fwd_workspace_size",
+           "kda_recurrent_step_gated", "kda_recurrent_step_fused", "kda_backward",
+           "kda_backward_workspace_size", "kda_chunk_fwd_workspace_size",
            "kda_status_string", "kda_version", "KDAError", "LIB_PATH", "load_library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -72,6 +73,11 @@ def load_library():
         lib.kda_recurrent_step_fused.restype = i
         lib.kda_recurrent_step_fused.argtypes = [vp, vp, vp, vp, fp, fp, vp, i, i, i, i, i, i,
                                                  u, f, vp]
+        lib.kda_backward.restype = i
+        lib.kda_backward.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                     i, i, i, i, i, i, vp, ip, i, f, vp, sz, vp]
+        lib.kda_backward_workspace_size.restype = sz
+        lib.kda_backward_workspace_size.argtypes = [i, i, i, i, i, i, i]
         lib.kda_chunk_fwd_workspace_size.restype = sz
         lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
         lib.kda_status_string.restype = ctypes.c_char_p
@@ -266,6 +272,68 @@ def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
         raise KDAError(st, "kda_chunk_fwd_fused" if flags is not None else
                        "kda_chunk_fwd" if gate is None else "kda_chunk_fwd_gated")
     return o, final_state
+
+
+def kda_backward_workspace_size(B, T, H, dk, dv, num_seqs, dtype=torch.bfloat16):
+    code = KDA_DTYPE_BF16 if dtype == torch.bfloat16 else KDA_DTYPE_F32
+    return int(load_library().kda_backward_workspace_size(B, T, H, dk, dv, num_seqs, code))
+
+
+def kda_backward(q, k, v, alpha, beta, initial_state, dout, dfinal_state=None,
+                 cu_seqlens=None, cu_seqlens_host=None, scale=None, workspace=None):
+    """Gradients of kda_chunk_fwd (per-channel gate): dout [B, T, H, dv] in the
+    dtype of q, dfinal_state [B or N, H, dk, dv] float32 or None.  Returns
+    float32 (dq, dk, dv, dalpha, dbeta, dinitial_state)."""
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(q, "q", dt, dev)
+    _check(k, "k", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    _check(alpha, "alpha", torch.float32, dev, (B, T, H, dk))
+    _check(beta, "beta", torch.float32, dev, (B, T, H))
+    _check(dout, "dout", dt, dev, (B, T, H, dv))
+    num_seqs, cu_dev, cu_host_arr = 0, None, None
+    if cu_seqlens is not None or cu_seqlens_host is not None:
+        if cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.to("cpu")
+        host = [int(x) for x in (cu_seqlens_host.tolist() if isinstance(cu_seqlens_host, torch.Tensor)
+                                 else cu_seqlens_host)]
+        if cu_seqlens is None:
+            cu_seqlens = torch.tensor(host, dtype=torch.int32, device=dev)
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (len(host),))
+        num_seqs = len(host) - 1
+        cu_dev = cu_seqlens
+        cu_host_arr = (ctypes.c_int * len(host))(*host)
+    nstates = num_seqs if num_seqs > 0 else B
+    sshape = (nstates, H, dk, dv)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.float32, dev, sshape)
+    if dfinal_state is not None:
+        _check(dfinal_state, "dfinal_state", torch.float32, dev, sshape)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = (torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32),
+         torch.empty((B, T, H, dv), **f32), torch.empty((B, T, H, dk), **f32),
+         torch.empty((B, T, H), **f32), torch.empty(sshape, **f32))
+    ws_bytes = int(lib.kda_backward_workspace_size(B, T, H, dk, dv, num_seqs, code))
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < ws_bytes:
+            raise ValueError("workspace holds %d bytes, the call needs %d" % (workspace.numel(), ws_bytes))
+        ws, ws_bytes = workspace, workspace.numel()
+    else:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+                          _ptr(dout), _ptr(dfinal_state), *[_ptr(x) for x in g],
+                          B, T, H, dk, dv, code, _ptr(cu_dev), cu_host_arr, num_seqs,
+                          float(scale) if scale is not None else 0.0, _ptr(ws), ws_bytes,
+                          _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_backward")
+    return g
 
 
 def kda_recurrent_step(q, k, v, alpha, beta, state, scale=None, o=None):

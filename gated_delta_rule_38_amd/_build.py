@@ -8,7 +8,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "chunk_fwd.hip", "chunk_fwd_bf16.hip", "recurrent_step.hip"]
+SOURCES = ["kda_api.cpp", "chunk_fwd.hip", "chunk_fwd_bf16.hip", "recurrent_step.hip",
+           "backward.hip"]
 ARCH = "gfx950"
 
 

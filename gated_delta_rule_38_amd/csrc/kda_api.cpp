@@ -181,6 +181,105 @@ kda_status kda_recurrent_step_fused(const void* q, const void* k, const void* v,
                                (int)gate_kind, flags, scale, stream);
 }
 
+size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                   kda_dtype dtype) {
+    if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return 0;
+    if (!supported_dim(dk) || !supported_dim(dv)) return 0;
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return 0;
+    const long tokens = num_seqs > 0 ? (long)T : (long)B * T;
+    const int nseq = num_seqs > 0 ? num_seqs : B;
+    if (nseq == 0 || H == 0) return 0;
+    return kda::backward_workspace_bytes(tokens, nseq, H, dk, dv);
+}
+
+kda_status kda_backward(const void* q, const void* k, const void* v, const float* alpha,
+                        const float* beta, const float* initial_state, const void* dout,
+                        const float* dfinal_state, float* dq, float* dk, float* dv,
+                        float* dalpha, float* dbeta, float* dinitial_state, int B, int T, int H,
+                        int dk_dim, int dv_dim, kda_dtype dtype, const int* cu_seqlens_dev,
+                        const int* cu_seqlens_host, int num_seqs, float scale, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    try {
+        if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
+        if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return KDA_ERROR_INVALID_VALUE;
+        if (!supported_dim(dk_dim) || !supported_dim(dv_dim)) return KDA_ERROR_NOT_SUPPORTED;
+        const bool varlen = num_seqs > 0;
+        if (!varlen && (cu_seqlens_dev || cu_seqlens_host)) return KDA_ERROR_INVALID_VALUE;
+        int nstates = B;
+        if (varlen) {
+            if (!cu_seqlens_dev || !cu_seqlens_host || B != 1) return KDA_ERROR_INVALID_VALUE;
+            if (cu_seqlens_host[0] != 0 || cu_seqlens_host[num_seqs] != T)
+                return KDA_ERROR_INVALID_VALUE;
+            for (int n = 0; n < num_seqs; ++n)
+                if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERROR_INVALID_VALUE;
+            if ((reinterpret_cast<uintptr_t>(cu_seqlens_dev) & 3u) != 0)
+                return KDA_ERROR_MISALIGNED;
+            nstates = num_seqs;
+        }
+        const size_t es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+        size_t b_qk, b_v, b_qk4, b_v4, b_b, b_s;
+        if (!bytes_of(B, T, H, dk_dim, es, &b_qk) || !bytes_of(B, T, H, dv_dim, es, &b_v) ||
+            !bytes_of(B, T, H, dk_dim, 4, &b_qk4) || !bytes_of(B, T, H, dv_dim, 4, &b_v4) ||
+            !bytes_of(B, T, H, 1, 4, &b_b) || !bytes_of(nstates, H, dk_dim, dv_dim, 4, &b_s))
+            return KDA_ERROR_INVALID_VALUE;
+        if ((long long)nstates * H > (1LL << 30)) return KDA_ERROR_NOT_SUPPORTED;
+        if ((long long)B * T > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
+        const size_t tokens = (size_t)B * T * H;
+        const size_t units = (size_t)nstates * H;
+        if (tokens > 0 && (!q || !k || !v || !alpha || !beta || !dout || !dq || !dk || !dv ||
+                           !dalpha || !dbeta))
+            return KDA_ERROR_INVALID_VALUE;
+        if (units > 0 && !dinitial_state) return KDA_ERROR_INVALID_VALUE;
+        const void* elems[] = {q, k, v, dout};
+        for (const void* ptr : elems)
+            if (!aligned(ptr, es)) return KDA_ERROR_MISALIGNED;
+        const void* words[] = {alpha, beta, dq, dk, dv, dalpha, dbeta};
+        for (const void* ptr : words)
+            if (!aligned(ptr, 4)) return KDA_ERROR_MISALIGNED;
+        const void* quads[] = {initial_state, dfinal_state, dinitial_state};
+        for (const void* ptr : quads)
+            if (!aligned(ptr, 16)) return KDA_ERROR_MISALIGNED;
+        if (!aligned(workspace, 256)) return KDA_ERROR_MISALIGNED;
+        const size_t need_ws =
+            kda_backward_workspace_size(B, T, H, dk_dim, dv_dim, num_seqs, dtype);
+        if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+            return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+        // outputs against inputs and against each other
+        const Range outs[] = {range_of(dq, tokens ? b_qk4 : 0), range_of(dk, tokens ? b_qk4 : 0),
+                              range_of(dv, tokens ? b_v4 : 0), range_of(dalpha, tokens ? b_qk4 : 0),
+                              range_of(dbeta, tokens ? b_b : 0),
+                              range_of(dinitial_state, units ? b_s : 0),
+                              range_of(workspace, need_ws)};
+        const Range ins[] = {range_of(q, b_qk), range_of(k, b_qk), range_of(v, b_v),
+                             range_of(alpha, b_qk4), range_of(beta, b_b), range_of(dout, b_v),
+                             range_of(initial_state, units ? b_s : 0),
+                             range_of(dfinal_state, units ? b_s : 0),
+                             range_of(cu_seqlens_dev, varlen ? (size_t)(num_seqs + 1) * 4 : 0)};
+        for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+            for (const Range& r : ins)
+                if (overlap(outs[i], r)) return KDA_ERROR_INVALID_VALUE;
+            for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+                if (overlap(outs[i], outs[j])) return KDA_ERROR_INVALID_VALUE;
+        }
+        if (units == 0) return KDA_SUCCESS;
+
+        kda::BwdArgs a;
+        a.q = q; a.k = k; a.v = v; a.dout = dout;
+        a.alpha = alpha; a.beta = beta; a.s0 = initial_state; a.dsT = dfinal_state;
+        a.g_q = dq; a.g_k = dk; a.g_v = dv; a.g_alpha = dalpha; a.g_beta = dbeta;
+        a.g_s0 = dinitial_state;
+        a.B = B; a.T = T; a.H = H; a.dk = dk_dim; a.dv = dv_dim;
+        a.bf16 = dtype == KDA_DTYPE_BF16;
+        a.cu_seqlens = varlen ? cu_seqlens_dev : nullptr;
+        a.num_seqs = varlen ? num_seqs : 0;
+        a.scale = default_scale(scale, dk_dim);
+        a.workspace = workspace;
+        return kda::launch_backward(a, stream) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+    } catch (...) {
+        return KDA_ERROR_HIP;
+    }
+}
+
 }  // extern "C"
 
 namespace {

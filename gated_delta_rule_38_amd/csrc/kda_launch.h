@@ -47,4 +47,20 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
 // value-column tile the planner picks for a given number of units
 int plan_chunk_dvt(int units, int dv, bool bf16);
 
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *alpha, *beta, *s0, *dsT;
+    float *g_q, *g_k, *g_v, *g_alpha, *g_beta, *g_s0;  // gradients
+    int B, T, H, dk, dv;
+    bool bf16;
+    const int *cu_seqlens;  // device, NULL in dense mode
+    int num_seqs;
+    float scale;
+    void *workspace;
+};
+
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
+// workspace of launch_backward: block checkpoints and one block of states per unit
+size_t backward_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv);
+
 }  // namespace kda

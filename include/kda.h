@@ -223,6 +223,46 @@ kda_status kda_recurrent_step_fused(const void *q, const void *k, const void *v,
                                     kda_gate gate_kind, unsigned flags, float scale,
                                     hipStream_t stream);
 
+/*
+ * Device workspace (bytes) that kda_backward needs: a checkpoint of the
+ * state every 16 tokens and one 16-token block of states per (sequence,
+ * head), about (tokens/16 + sequences + 1) * H * dk * dv * 4 bytes plus
+ * sequences * H * 16 * dk * dv * 4.  Returns 0 for arguments kda_backward
+ * would reject.
+ */
+size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                   kda_dtype dtype);
+
+/*
+ * Gradients of kda_chunk_fwd (per-channel gate, no input preparation): given
+ * dout = dL/do and dfinal_state = dL/dS_T, returns dL/dq, dL/dk, dL/dv,
+ * dL/dalpha, dL/dbeta and dL/dS_0.
+ * Source: the chain rule through the four steps of the update ("Kimi Delta
+ * Attention", section "KDA 的更新式"; bugfactory.tech news 3610, second to
+ * fourth paragraphs) taken token by token in reverse order; the fifth
+ * paragraph there names training as the use of the chunk-wise mode.
+ *   q, k, v, alpha, beta, initial_state, B, T, H, dk, dv, dtype, cu_seqlens_*,
+ *   num_seqs, scale: as for kda_chunk_fwd (the forward being differentiated)
+ *   dout          [B, T, H, dv]  dtype
+ *   dfinal_state  [Ns, H, dk, dv] float32, or NULL (zero)
+ *   dq, dk        [B, T, H, dk]  float32 (written)
+ *   dv            [B, T, H, dv]  float32 (written)
+ *   dalpha        [B, T, H, dk]  float32 (written)
+ *   dbeta         [B, T, H]      float32 (written)
+ *   dinitial_state [Ns, H, dk, dv] float32 (written; required)
+ * The states and their gradients need 16-byte alignment.  workspace: device
+ * memory of at least kda_backward_workspace_size() bytes, 256-byte aligned.
+ * Outputs must not overlap inputs, each other or the workspace.  Errors as
+ * for kda_chunk_fwd.
+ */
+kda_status kda_backward(const void *q, const void *k, const void *v, const float *alpha,
+                        const float *beta, const float *initial_state, const void *dout,
+                        const float *dfinal_state, float *dq, float *dk, float *dv,
+                        float *dalpha, float *dbeta, float *dinitial_state, int B, int T, int H,
+                        int dk_dim, int dv_dim, kda_dtype dtype, const int *cu_seqlens_dev,
+                        const int *cu_seqlens_host, int num_seqs, float scale, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *kda_status_string(kda_status status);
 

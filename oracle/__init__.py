@@ -185,6 +185,89 @@ def forward(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, scale=Non
     return o_all, s_all
 
 
+def backward_units(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, scale=None):
+    """Gradients of the token loop, float64, by the chain rule through its four
+    steps in reverse order (forget, predict, correct and write, read; the
+    update equation of "Kimi Delta Attention", section "KDA 的更新式", with
+    the order of bugfactory.tech news 3610, second to fourth paragraphs).
+
+    q, k, alpha: [U, T, dk]; v: [U, T, dv]; beta: [U, T]; initial_state
+    [U, dk, dv] or None; do: [U, T, dv] (gradient of o); dfinal_state
+    [U, dk, dv] or None (gradient of the final state).
+    Returns dq, dk, dv, dalpha, dbeta, dinitial_state (same shapes as the
+    inputs).  The forward states are kept for the reverse sweep, so this is
+    for small cases only.
+    """
+    q, k, v, alpha, beta, do = (_f64(x) for x in (q, k, v, alpha, beta, do))
+    U, T, dk = q.shape
+    dv = v.shape[2]
+    if scale is None:
+        scale = dk ** -0.5
+    S = np.zeros((U, dk, dv)) if initial_state is None else _f64(initial_state).copy()
+    s_prev = np.empty((T, U, dk, dv))
+    resid = np.empty((T, U, dv))  # v_t - vhat_t
+    for t in range(T):
+        s_prev[t] = S
+        st = alpha[:, t, :, None] * S                                 # forget
+        vhat = np.einsum("uij,ui->uj", st, k[:, t])                   # predict
+        resid[t] = v[:, t] - vhat
+        S = st + beta[:, t, None, None] * k[:, t, :, None] * resid[t][:, None, :]  # write
+    dS = np.zeros((U, dk, dv)) if dfinal_state is None else _f64(dfinal_state).copy()
+    g_q, g_k, g_v = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    g_a, g_b = np.zeros_like(alpha), np.zeros_like(beta)
+    for t in reversed(range(T)):
+        st = alpha[:, t, :, None] * s_prev[t]
+        e = beta[:, t, None] * resid[t]
+        s_t = st + k[:, t, :, None] * e[:, None, :]
+        # read: o_t = scale S_t^T q_t
+        g_q[:, t] = scale * np.einsum("uij,uj->ui", s_t, do[:, t])
+        dS = dS + scale * q[:, t, :, None] * do[:, t, None, :]
+        # write: S_t = S~ + k_t e^T
+        g_k[:, t] = np.einsum("uij,uj->ui", dS, e)
+        de = np.einsum("uij,ui->uj", dS, k[:, t])
+        # correct: e = beta_t (v_t - vhat)
+        g_b[:, t] = np.sum(de * resid[t], axis=-1)
+        g_v[:, t] = beta[:, t, None] * de
+        dvhat = -beta[:, t, None] * de
+        # predict: vhat = S~^T k_t
+        dst = dS + k[:, t, :, None] * dvhat[:, None, :]
+        g_k[:, t] += np.einsum("uij,uj->ui", st, dvhat)
+        # forget: S~ = Diag(alpha_t) S_{t-1}
+        g_a[:, t] = np.sum(dst * s_prev[t], axis=-1)
+        dS = alpha[:, t, :, None] * dst
+    return g_q, g_k, g_v, g_a, g_b, dS
+
+
+def backward(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, cu_seqlens=None,
+             scale=None):
+    """backward_units in the library's token layout (dense [B, T, H, d], or
+    B == 1 with cu_seqlens); returns dq, dk, dv, dalpha, dbeta, dinitial_state
+    ([B or N, H, dk, dv])."""
+    q, k, v, alpha, beta, do = (_f64(x) for x in (q, k, v, alpha, beta, do))
+    s0 = _f64(initial_state)
+    ds = _f64(dfinal_state)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if cu_seqlens is None:
+        starts = [(b, 0, T) for b in range(B)]
+    else:
+        cu = [int(c) for c in cu_seqlens]
+        starts = [(0, cu[n], cu[n + 1] - cu[n]) for n in range(len(cu) - 1)]
+    outs = [np.zeros_like(x) for x in (q, k, v, alpha, beta)]
+    g_s0 = np.zeros((len(starts), H, dk, dv))
+    for n, (b, t0, L) in enumerate(starts):
+        def units(x):  # [L, H, d] -> [H, L, d]
+            return np.moveaxis(x[b, t0:t0 + L], 1, 0)
+        res = backward_units(units(q), units(k), units(v), units(alpha),
+                             beta[b, t0:t0 + L].T, None if s0 is None else s0[n],
+                             units(do), None if ds is None else ds[n], scale=scale)
+        for i in range(4):
+            outs[i][b, t0:t0 + L] = np.moveaxis(res[i], 0, 1)
+        outs[4][b, t0:t0 + L] = res[4].T
+        g_s0[n] = res[5]
+    return tuple(outs) + (g_s0,)
+
+
 def step(q, k, v, alpha, beta, state, scale=None, threads=0):
     """One decode step.  q, k, alpha [N, H, dk]; v [N, H, dv]; beta [N, H];
     state [N, H, dk, dv].  Returns (o [N, H, dv], new_state), float64; the

@@ -32,8 +32,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused", "kda_recurrent_step",
-              "kda_recurrent_step_gated", "kda_recurrent_step_fused",
-              "kda_chunk_fwd_workspace_size", "kda_status_string", "kda_version"]:
+              "kda_recurrent_step_gated", "kda_recurrent_step_fused", "kda_backward",
+              "kda_backward_workspace_size", "kda_chunk_fwd_workspace_size", "kda_status_string",
+              "kda_version"]:
         assert n in names, names
 
 
@@ -284,6 +285,55 @@ def test_fused_empty_is_a_noop(lib):
 ])
 def test_step_fused_rejects_before_any_hip_call(lib, gate, flags, kw, code):
     assert step_fused_call(lib, gate, flags, **kw) == code
+
+
+def bwd_call(lib, **kw):
+    B, T, H, dk, dv = kw.get("B", 2), kw.get("T", 100), kw.get("H", 4), 128, 128
+    ws_need = lib.kda_backward_workspace_size(B, T, H, dk, dv, 0, 1)
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), s0=fake(5), do=fake(6),
+             dsT=fake(7), dq=fake(8), dk=fake(9), dv=fake(10), da=fake(11), db=fake(12),
+             ds0=fake(13), B=B, T=T, H=H, dkd=dk, dvd=dv, dt=1, cu_dev=None, cu_host=None,
+             num_seqs=0, scale=0.0, ws=fake(14), ws_bytes=ws_need, stream=None)
+    a.update(kw)
+    return lib.kda_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"], a["do"],
+                            a["dsT"], a["dq"], a["dk"], a["dv"], a["da"], a["db"], a["ds0"],
+                            a["B"], a["T"], a["H"], a["dkd"], a["dvd"], a["dt"], a["cu_dev"],
+                            a["cu_host"], a["num_seqs"], a["scale"], a["ws"], a["ws_bytes"],
+                            a["stream"])
+
+
+def test_backward_workspace_size(lib):
+    # checkpoints every 16 tokens (+ one slot per sequence and one spare) and
+    # one 16-token block of states per (sequence, head)
+    B, T, H, d = 2, 100, 4, 128
+    slots = (B * T + 15) // 16 + B + 1
+    ck = slots * H * d * d * 4
+    sb = B * H * 16 * d * d * 4
+    r = lambda x: (x + 255) // 256 * 256
+    assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 1) == r(ck) + r(sb)
+    assert lib.kda_backward_workspace_size(B, T, H, 96, d, 0, 1) == 0
+    assert lib.kda_backward_workspace_size(0, T, H, d, d, 0, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(dkd=32), NOT_SUPPORTED),
+    (dict(q=None), INVALID),
+    (dict(do=None), INVALID),
+    (dict(ds0=None), INVALID),                 # the initial-state gradient is always written
+    (dict(s0=fake(5, 8)), MISALIGNED),         # states: 16 bytes
+    (dict(ds0=fake(13, 4)), MISALIGNED),
+    (dict(ws=fake(14, 16)), MISALIGNED),       # workspace: 256 bytes
+    (dict(ws=None, ws_bytes=0), WORKSPACE),
+    (dict(ws_bytes=1024), WORKSPACE),
+    (dict(dq=fake(0, 256)), INVALID),          # gradient inside q
+    (dict(dk=fake(8, 1024)), INVALID),         # two gradients overlapping
+    (dict(ws=fake(12, 256)), INVALID),         # workspace inside dbeta
+    (dict(cu_dev=fake(15)), INVALID),          # cu_seqlens without num_seqs
+])
+def test_backward_rejects_before_any_hip_call(lib, kw, code):
+    assert bwd_call(lib, **kw) == code
 
 
 def test_python_binding_checks_arguments():

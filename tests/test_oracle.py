@@ -358,3 +358,59 @@ def _prep4(q, k, z, bl, flags):
 
 def _fwd_kw(qn, kn, a, b, v, s0):
     return oracle.forward(qn, kn, v, a, b, s0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_backward_matches_finite_differences(seed):
+    """oracle.backward_units against central differences of the oracle's own
+    forward (the C token loop, a separate implementation): L = <W, o> + <V,
+    S_T> with random weights, every input perturbed in turn."""
+    rng = np.random.default_rng(40 + seed)
+    T, dk, dv = 5, 3, 2
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    k = k * rng.uniform(0.6, 1.3, (T, 1))          # no special structure
+    W = rng.standard_normal((T, dv))
+    V = rng.standard_normal((dk, dv))
+    scale = 0.8
+    inputs = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, s0=s0)
+
+    def loss(x):
+        o, s = oracle_impl(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["s0"], scale)
+        return float(np.sum(W * o) + np.sum(V * s))
+    grads = oracle.backward_units(q[None], k[None], v[None], alpha[None], beta[None], s0[None],
+                                  W[None], V[None], scale=scale)
+    names = ["q", "k", "v", "alpha", "beta", "s0"]
+    h = 1e-6
+    for name, g in zip(names, grads):
+        x0 = inputs[name]
+        fd = np.zeros_like(x0)
+        for idx in np.ndindex(x0.shape):
+            xp = {n: a.copy() for n, a in inputs.items()}
+            xm = {n: a.copy() for n, a in inputs.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        assert rel(g[0], fd) < 1e-7, (name, rel(g[0], fd))
+
+
+def test_backward_special_cases():
+    """beta = 0 and alpha = 1: nothing is written or forgotten, S_t = S0 for
+    every t, so dq_t = scale S0 do_t, dS0 = dS_T + scale sum_t q_t do_t^T,
+    dalpha_t = rows of (dS_t (.) S0) and dk = dv = 0 (closed forms)."""
+    rng = np.random.default_rng(5)
+    U, T, dk, dv = 2, 6, 4, 3
+    q = rng.standard_normal((U, T, dk))
+    k = rng.standard_normal((U, T, dk))
+    v = rng.standard_normal((U, T, dv))
+    s0 = rng.standard_normal((U, dk, dv))
+    do = rng.standard_normal((U, T, dv))
+    dsT = rng.standard_normal((U, dk, dv))
+    g = oracle.backward_units(q, k, v, np.ones((U, T, dk)), np.zeros((U, T)), s0, do, dsT,
+                              scale=0.5)
+    assert np.allclose(g[0], 0.5 * np.einsum("uij,utj->uti", s0, do), atol=1e-13)
+    assert np.allclose(g[5], dsT + 0.5 * np.einsum("uti,utj->uij", q, do), atol=1e-12)
+    assert np.abs(g[1]).max() == 0.0 and np.abs(g[2]).max() == 0.0
+    # dS_t = dS_T + scale sum_{r > t} q_r do_r^T + scale q_t do_t^T, then rows against S0
+    for t in range(T):
+        dS_t = dsT + 0.5 * np.einsum("uri,urj->uij", q[:, t:], do[:, t:])
+        assert np.allclose(g[3][:, t], np.sum(dS_t * s0, axis=-1), atol=1e-12)
