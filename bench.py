@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="raw inputs (bf16 gate logits, beta logits, q and k not normalised) "
                          "prepared in the kernel")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time kda_backward (gradients of the same forward, random dL/do "
+                         "and dL/dS_T) on the chunk workload")
     ap.add_argument("--prep-baseline", action="store_true",
                     help="with --fused: also time the same preparation done by torch "
                          "elementwise kernels followed by the plain entry point")
@@ -229,6 +232,43 @@ def main():
                     "then kda_chunk_fwd_gated, same inputs",
             "prep_ms": time_fn(prep, n), "prep_plus_chunk_ms": time_fn(unfused, n),
             "fused_ms": ms}
+
+    if args.backward and gate == "channel" and not fused:
+        gg = torch.Generator(device=dev)
+        gg.manual_seed(11)
+        dout = torch.randn((B, T, H, dv), generator=gg, device=dev).to(d["q"].dtype)
+        dsT = torch.randn((B, H, dk, dv), generator=gg, device=dev)
+        ws = torch.empty(kda.kda_backward_workspace_size(B, T, H, dk, dv, 0), dtype=torch.uint8,
+                         device=dev)
+
+        def bstep():
+            return kda.kda_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                    d["initial_state"], dout, dsT, workspace=ws)
+        nb = max(2, args.steps // 20)
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(nb):
+            bstep()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / nb
+        # inputs q, k, v, alpha, beta, dout, S0, dS_T read once; dq, dk, dv,
+        # dalpha, dbeta (fp32) and dS_0 written once
+        es = 2
+        bbytes = (B * T * H * (2 * dk * es + dv * es + dk * 4 + 4 + dv * es
+                               + 4 * (2 * dk + dv + dk) + 4) + 3 * B * H * dk * dv * 4)
+        out["backward"] = {
+            "workload": "kda_backward bf16 B4 H16 T4096 dk128 dv128 (per-channel gate), "
+                        "fp32 gradients",
+            "ms_per_step": bms, "tokens_per_s": B * T / (bms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": bbytes / (bms / 1e3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "backward_kernel", "algorithmic_bytes_per_launch": bbytes}}
 
     if not args.skip_decode:
         dc = CONFIGS[3]

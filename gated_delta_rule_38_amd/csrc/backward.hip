@@ -14,16 +14,22 @@
 //   dS~ = dS + k_t dvh^T,             dalpha_t = rowsum(dS~ (.) S_{t-1}),
 //   dS_{t-1} = Diag(alpha_t) dS~.
 // The reverse sweep needs S_{t-1} of every token.  A first forward sweep
-// stores the state at the start of every 16-token block (workspace); the
+// stores the state at the start of every 8-token block (workspace); the
 // reverse sweep then, block by block from the last, recomputes the block's
-// 16 states forward from its checkpoint into a workspace buffer, with the
-// residuals v - vh in LDS, and walks the block backwards.
+// 8 states forward from its checkpoint into registers, with the residuals
+// v - vh in LDS, and walks the block backwards.
 //
-// Layout: one workgroup per (sequence, head) unit, dk/16 waves.  Lane l of
-// wave w owns state row w*16 + l%16 and the dv/4 columns of group l/16, so a
-// sum over columns (dq, dk, dalpha, dbeta) stays within the lane and two
-// cross-lane steps, and a sum over rows (vh, de) takes four DPP steps inside
-// the 16-lane row and one pass through LDS across the waves.
+// Layout: one workgroup per (sequence, head) unit and slice of DVS value
+// columns (the columns of S evolve independently), dk/16 waves.  Lane l of
+// wave w owns state row w*16 + l%16 and the DVS/4 columns of group l/16, so
+// a sum over the slice's columns (dq, dk, dalpha, dbeta) stays within the
+// lane and two cross-lane steps, and a sum over rows (vh, de) takes four DPP
+// steps inside the 16-lane row and one pass through LDS across the waves.
+// The slices of a unit add their column sums into the zeroed dq, dk, dalpha
+// and dbeta with float atomics; dv and the initial-state gradient are the
+// slice's own columns.
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -31,7 +37,7 @@ namespace kda {
 
 namespace {
 
-constexpr int BBLK = 16;  // tokens per checkpoint block
+constexpr int BBLK = 8;  // tokens per checkpoint block
 
 struct BwdParams {
     const void *q, *k, *v, *dout;
@@ -39,10 +45,15 @@ struct BwdParams {
     float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
     const int* cu_seqlens;
     float* ckpt;   // [slots per head][H][dk][dv]
-    float* sbuf;   // [units][BBLK][dk][dv]
-    int B, T, H, units;
+    int B, T, H, units, nslice;
     float scale;
 };
+
+__global__ void zero_kernel(float* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
+}
 
 // sum over the 16 lanes of a DPP row: every lane ends with the total
 __device__ __forceinline__ float row16_sum(float x) {
@@ -52,6 +63,16 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));  // mirror
     return x;
 }
+// Workgroup barrier that orders LDS only.  The waves exchange nothing but LDS
+// data; every global location a lane reads back (checkpoints, block states)
+// it wrote itself, and the gradient sums are atomics.  A full barrier would
+// also wait for every global store and atomic in flight, and with them for
+// the next token's loads issued ahead.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 // sum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float groups4_sum(float x) {
     x += __shfl_xor(x, 16, 64);
@@ -59,15 +80,14 @@ __device__ __forceinline__ float groups4_sum(float x) {
     return x;
 }
 
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, int DVS>
 __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
     constexpr int NW = DK / 16;   // waves, 16 state rows each
-    constexpr int CPL = DV / 4;   // columns per lane
-    __shared__ __align__(16) float part[NW][DV];     // per-wave partial sums over rows
-    __shared__ __align__(16) float red[DV];          // their total
-    __shared__ __align__(16) float resid[BBLK][DV];  // v - vh of the block tokens
+    constexpr int CPL = DVS / 4;  // columns per lane
+    __shared__ __align__(16) float part[2][NW][DVS];  // per-wave partial sums over rows
+    __shared__ __align__(16) float resid[BBLK][DVS];  // v - vh of the block tokens
 
-    const int unit = blockIdx.x;
+    const int unit = blockIdx.x / p.nslice, slice = blockIdx.x % p.nslice;
     const int H = p.H, seq = unit / H, h = unit % H;
     long t0;
     int len;
@@ -79,7 +99,8 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
         len = p.T;
     }
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int row = w * 16 + (l & 15), cg = l >> 4, c0 = cg * CPL;
+    const int row = w * 16 + (l & 15), cg = l >> 4, cs = cg * CPL;  // column in the slice
+    const int c0 = slice * DVS + cs;                                  // column in the state
     const Tin* __restrict__ gq = static_cast<const Tin*>(p.q);
     const Tin* __restrict__ gk = static_cast<const Tin*>(p.k);
     const Tin* __restrict__ gv = static_cast<const Tin*>(p.v);
@@ -91,7 +112,6 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
     auto ckpt_at = [&](int blk) {
         return p.ckpt + ((size_t)(slot0 + blk) * H + h) * DK * DV + (size_t)row * DV + c0;
     };
-    float* sb = p.sbuf + (size_t)unit * BBLK * DK * DV + (size_t)row * DV + c0;
 
     auto ld_cols = [&](const Tin* base, float (&x)[CPL]) {
 #pragma unroll
@@ -109,34 +129,42 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
         for (int j = 0; j < CPL; j += 4)
             *reinterpret_cast<float4*>(dst + j) = make_float4(x[j], x[j + 1], x[j + 2], x[j + 3]);
     };
-    // x[j] <- sum over the dk rows of x[j] (column c0 + j); two barriers
+    // x[j] <- sum over the dk rows of x[j] (column c0 + j): one barrier, the
+    // partials double-buffered so the next sum cannot overwrite them early
+    int rpar = 0;
     auto col_sum = [&](float (&x)[CPL]) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) x[j] = row16_sum(x[j]);
-        if ((l & 15) == 0) st_run(&part[w][c0], x);
-        __syncthreads();
-        for (int c = tid; c < DV; c += 64 * NW) {
-            float s = 0.f;
+        if ((l & 15) == 0) st_run(&part[rpar][w][cs], x);
+        lds_barrier();
+        float y[CPL];
+        ld_run(&part[rpar][0][cs], x);
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) s += part[ww][c];
-            red[c] = s;
+        for (int ww = 1; ww < NW; ++ww) {
+            ld_run(&part[rpar][ww][cs], y);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) x[j] += y[j];
         }
-        __syncthreads();
-        ld_run(&red[c0], x);
+        rpar ^= 1;
+    };
+    // A token's inputs for this lane, loaded one token ahead of their use so
+    // that the loads' latency overlaps the step before.
+    struct FIn { float kr, ar, b, vv[CPL]; };
+    auto ld_fin = [&](long tok, FIn& f) {
+        const size_t th = (size_t)tok * H + h;
+        f.kr = to_f32(gk[th * DK + row]);
+        f.ar = p.alpha[th * DK + row];
+        f.b = p.beta[th];
+        ld_cols(gv + th * DV, f.vv);
     };
     // one forward token step on this lane's run; r receives v - vh
-    auto fwd_step = [&](float (&S)[CPL], long tok, float (&r)[CPL]) {
-        const size_t th = (size_t)tok * H + h;
-        const float kr = to_f32(gk[th * DK + row]);
-        const float ar = p.alpha[th * DK + row];
-        const float b = p.beta[th];
-        float vv[CPL], x[CPL];
-        ld_cols(gv + th * DV, vv);
+    auto fwd_step = [&](float (&S)[CPL], const FIn& f, float (&r)[CPL]) {
+        float x[CPL];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) { S[j] *= ar; x[j] = S[j] * kr; }
+        for (int j = 0; j < CPL; ++j) { S[j] *= f.ar; x[j] = S[j] * f.kr; }
         col_sum(x);  // vh
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) { r[j] = vv[j] - x[j]; S[j] += kr * (b * r[j]); }
+        for (int j = 0; j < CPL; ++j) { r[j] = f.vv[j] - x[j]; S[j] += f.kr * (f.b * r[j]); }
     };
 
     const int nblk = (len + BBLK - 1) / BBLK;
@@ -147,10 +175,14 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
         for (int j = 0; j < CPL; ++j) S[j] = 0.f;
     }
     // sweep 1: checkpoints at the block starts
+    FIn fc, fn;
+    if (len > 0) ld_fin(t0, fn);
     for (int t = 0; t < len; ++t) {
+        fc = fn;
+        if (t + 1 < len) ld_fin(t0 + t + 1, fn);
         if (t % BBLK == 0) st_run(ckpt_at(t / BBLK), S);
         float r[CPL];
-        fwd_step(S, t0 + t, r);
+        fwd_step(S, fc, r);
     }
     // sweep 2: blocks from the last, each recomputed and then reversed
     float dS[CPL];
@@ -163,24 +195,47 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
     for (int blk = nblk - 1; blk >= 0; --blk) {
         const int tb = blk * BBLK, nt = min(BBLK, len - tb);
         ld_run(ckpt_at(blk), S);
-        for (int tt = 0; tt < nt; ++tt) {
-            st_run(sb + (size_t)tt * DK * DV, S);  // S_{t-1} of token tb + tt
-            float r[CPL];
-            fwd_step(S, t0 + tb + tt, r);
-            if (w == 0 && (l & 15) == 0) st_run(&resid[tt][c0], r);
+        // the block's states S_{t-1}, in registers (the loops are unrolled so
+        // that every index into SB is a constant; nt is uniform)
+        float SB[BBLK][CPL];
+        ld_fin(t0 + tb, fn);
+#pragma unroll
+        for (int tt = 0; tt < BBLK; ++tt) {
+            if (tt < nt) {
+                fc = fn;
+                if (tt + 1 < nt) ld_fin(t0 + tb + tt + 1, fn);
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) SB[tt][j] = S[j];
+                float r[CPL];
+                fwd_step(S, fc, r);
+                if (w == 0 && (l & 15) == 0) st_run(&resid[tt][cs], r);
+            }
         }
-        __syncthreads();
-        for (int tt = nt - 1; tt >= 0; --tt) {
+        lds_barrier();
+        // the reverse step's inputs, one token ahead as well
+        struct BIn { float kr, qr, ar, b, dov[CPL]; };
+        auto ld_bin = [&](int tt, BIn& f) {
+            const size_t th = (size_t)(t0 + tb + tt) * H + h;
+            f.kr = to_f32(gk[th * DK + row]);
+            f.qr = to_f32(gq[th * DK + row]);
+            f.ar = p.alpha[th * DK + row];
+            f.b = p.beta[th];
+            ld_cols(gdo + th * DV, f.dov);
+        };
+        BIn bc, bn;
+        ld_bin(nt - 1, bn);
+#pragma unroll
+        for (int tt = BBLK - 1; tt >= 0; --tt) {
+          if (tt < nt) {
+            bc = bn;
+            if (tt > 0) ld_bin(tt - 1, bn);
             const long tok = t0 + tb + tt;
             const size_t th = (size_t)tok * H + h;
-            const float kr = to_f32(gk[th * DK + row]);
-            const float qr = to_f32(gq[th * DK + row]);
-            const float ar = p.alpha[th * DK + row];
-            const float b = p.beta[th];
-            float sp[CPL], r[CPL], dov[CPL];
-            ld_run(sb + (size_t)tt * DK * DV, sp);
-            ld_run(&resid[tt][c0], r);
-            ld_cols(gdo + th * DV, dov);
+            const float kr = bc.kr, qr = bc.qr, ar = bc.ar, b = bc.b;
+            const float(&sp)[CPL] = SB[tt];
+            const float(&dov)[CPL] = bc.dov;
+            float r[CPL];
+            ld_run(&resid[tt][cs], r);
             float st[CPL], e[CPL];
             float dq = 0.f, dkr = 0.f;
 #pragma unroll
@@ -210,43 +265,53 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
             da = groups4_sum(da);
             db = groups4_sum(db);
             if (cg == 0) {
-                p.dq[th * DK + row] = sc * dq;
-                p.dk[th * DK + row] = dkr;
-                p.dalpha[th * DK + row] = da;
+                atomicAdd(p.dq + th * DK + row, sc * dq);
+                atomicAdd(p.dk + th * DK + row, dkr);
+                atomicAdd(p.dalpha + th * DK + row, da);
             }
             if (w == 0 && (l & 15) == 0) {
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) p.dv[th * DV + c0 + j] = b * de[j];
             }
-            if (tid == 0) p.dbeta[th] = db;
+            if (tid == 0) atomicAdd(p.dbeta + th, db);
+          }
         }
-        __syncthreads();  // resid is rewritten by the next block
+        lds_barrier();  // resid is rewritten by the next block
     }
     st_run(p.ds0 + sunit, dS);
 }
 
 template <typename Tin, int DK, int DV>
-hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((backward_kernel<Tin, DK, DV>), dim3(p.units), dim3(64 * (DK / 16)), 0,
-                       stream, p);
+hipError_t launch_bwd_t(BwdParams p, long tokens, hipStream_t stream) {
+    constexpr int DVS = 16;  // value columns per workgroup (4 per lane)
+    p.nslice = DV / DVS;
+    // the column sums are accumulated: clear dq, dk, dalpha (tokens*H*dk each) and dbeta
+    const size_t nk = (size_t)tokens * p.H * DK, nb = (size_t)tokens * p.H;
+    float* zs[] = {p.dq, p.dk, p.dalpha};
+    for (float* z : zs) {
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<size_t>((nk + 255) / 256, 4096)),
+                           dim3(256), 0, stream, z, nk);
+    }
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<size_t>((nb + 255) / 256, 4096)),
+                       dim3(256), 0, stream, p.dbeta, nb);
+    hipLaunchKernelGGL((backward_kernel<Tin, DK, DV, DVS>), dim3(p.units * p.nslice),
+                       dim3(64 * (DK / 16)), 0, stream, p);
     return hipGetLastError();
 }
 
 template <typename Tin>
-hipError_t launch_bwd_dt(const BwdParams& p, int dk, int dv, hipStream_t stream) {
-    if (dk == 128 && dv == 128) return launch_bwd_t<Tin, 128, 128>(p, stream);
-    if (dk == 128 && dv == 64) return launch_bwd_t<Tin, 128, 64>(p, stream);
-    if (dk == 64 && dv == 128) return launch_bwd_t<Tin, 64, 128>(p, stream);
-    return launch_bwd_t<Tin, 64, 64>(p, stream);
+hipError_t launch_bwd_dt(const BwdParams& p, int dk, int dv, long tokens, hipStream_t stream) {
+    if (dk == 128 && dv == 128) return launch_bwd_t<Tin, 128, 128>(p, tokens, stream);
+    if (dk == 128 && dv == 64) return launch_bwd_t<Tin, 128, 64>(p, tokens, stream);
+    if (dk == 64 && dv == 128) return launch_bwd_t<Tin, 64, 128>(p, tokens, stream);
+    return launch_bwd_t<Tin, 64, 64>(p, tokens, stream);
 }
 
 }  // namespace
 
 size_t backward_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv) {
     const size_t slots = (size_t)((tokens_total + BBLK - 1) / BBLK + nseq + 1);
-    const size_t ck = slots * H * dk * dv * 4;
-    const size_t sb = (size_t)nseq * H * BBLK * dk * dv * 4;
-    return (ck + 255) / 256 * 256 + (sb + 255) / 256 * 256;
+    return (slots * H * dk * dv * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
@@ -254,8 +319,6 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int units = nseq * a.H;
     if (units == 0) return hipSuccess;
     const long tokens = a.cu_seqlens ? a.T : (long)a.B * a.T;
-    const size_t slots = (size_t)((tokens + BBLK - 1) / BBLK + nseq + 1);
-    const size_t ck = (slots * a.H * a.dk * a.dv * 4 + 255) / 256 * 256;
     BwdParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout;
     p.alpha = a.alpha; p.beta = a.beta; p.s0 = a.s0; p.dsT = a.dsT;
@@ -263,11 +326,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     p.ds0 = a.g_s0;
     p.cu_seqlens = a.cu_seqlens;
     p.ckpt = static_cast<float*>(a.workspace);
-    p.sbuf = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ck);
     p.B = a.B; p.T = a.T; p.H = a.H; p.units = units;
     p.scale = a.scale;
-    return a.bf16 ? launch_bwd_dt<bf16_t>(p, a.dk, a.dv, stream)
-                   : launch_bwd_dt<float>(p, a.dk, a.dv, stream);
+    return a.bf16 ? launch_bwd_dt<bf16_t>(p, a.dk, a.dv, tokens, stream)
+                   : launch_bwd_dt<float>(p, a.dk, a.dv, tokens, stream);
 }
 
 }  // namespace kda

@@ -60,7 +60,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
-// workspace of launch_backward: block checkpoints and one block of states per unit
+// workspace of launch_backward: the state checkpoints of every unit
 size_t backward_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv);
 
 }  // namespace kda

@@ -225,10 +225,9 @@ kda_status kda_recurrent_step_fused(const void *q, const void *k, const void *v,
 
 /*
  * Device workspace (bytes) that kda_backward needs: a checkpoint of the
- * state every 16 tokens and one 16-token block of states per (sequence,
- * head), about (tokens/16 + sequences + 1) * H * dk * dv * 4 bytes plus
- * sequences * H * 16 * dk * dv * 4.  Returns 0 for arguments kda_backward
- * would reject.
+ * state every 8 tokens of every (sequence, head), (tokens/8 rounded up +
+ * sequences + 1) * H * dk * dv * 4 bytes rounded up to 256.  Returns 0 for
+ * arguments kda_backward would reject.
  */
 size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                    kda_dtype dtype);

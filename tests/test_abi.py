@@ -303,14 +303,12 @@ def bwd_call(lib, **kw):
 
 
 def test_backward_workspace_size(lib):
-    # checkpoints every 16 tokens (+ one slot per sequence and one spare) and
-    # one 16-token block of states per (sequence, head)
+    # checkpoints every 8 tokens (+ one slot per sequence and one spare)
     B, T, H, d = 2, 100, 4, 128
-    slots = (B * T + 15) // 16 + B + 1
+    slots = (B * T + 7) // 8 + B + 1
     ck = slots * H * d * d * 4
-    sb = B * H * 16 * d * d * 4
     r = lambda x: (x + 255) // 256 * 256
-    assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 1) == r(ck) + r(sb)
+    assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 1) == r(ck)
     assert lib.kda_backward_workspace_size(B, T, H, 96, d, 0, 1) == 0
     assert lib.kda_backward_workspace_size(0, T, H, d, d, 0, 1) == 0
 
