@@ -40,6 +40,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     static_assert(NCG <= 64 && 64 % NCG == 0 && RPG >= 1, "shape");
 
     __shared__ float red[4][NCG][NRED + 1];
+    __shared__ float sig[DK];  // sigmoid of per-channel gate logits, formed once per channel
 
     const int unit = blockIdx.x;  // sequence * H + head
     const int tid = threadIdx.x;
@@ -61,10 +62,14 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const bool gl = fuse & FUSE_GATE_LOGITS;
     float a[RPG], kk[RPG], qq[RPG];
     const float ah = gate == 1 ? (gl ? sigmoid_f(to_f32(glog[unit])) : alpha[unit]) : 1.f;
+    if (gate == 0 && gl) {  // every channel's sigmoid once, shared by the NCG column groups
+        if (tid < DK) sig[tid] = sigmoid_f(to_f32(glog[(size_t)unit * DK + tid]));
+        __syncthreads();
+    }
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
         const size_t ai = (size_t)unit * DK + row0 + r;
-        a[r] = gate == 0 ? (gl ? sigmoid_f(to_f32(glog[ai])) : alpha[ai]) : ah;
+        a[r] = gate == 0 ? (gl ? sig[row0 + r] : alpha[ai]) : ah;
         kk[r] = to_f32(k[(size_t)unit * DK + row0 + r]);
         qq[r] = to_f32(q[(size_t)unit * DK + row0 + r]);
     }
