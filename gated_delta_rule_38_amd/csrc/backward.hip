@@ -17,7 +17,8 @@
 // stores the state at the start of every 8-token block (workspace); the
 // reverse sweep then, block by block from the last, recomputes the block's
 // 8 states forward from its checkpoint into registers, with the residuals
-// v - vh in LDS, and walks the block backwards.
+// v - vh in LDS, and walks the block backwards.  Both sweeps issue each token's
+// input loads a few steps ahead.
 //
 // Layout: one workgroup per (sequence, head) unit and slice of DVS value
 // columns (the columns of S evolve independently), dk/16 waves.  Lane l of
@@ -38,6 +39,11 @@ namespace kda {
 namespace {
 
 constexpr int BBLK = 8;  // tokens per checkpoint block
+// tokens whose input loads are in flight ahead of their step in the first
+// sweep (fp32 inputs take more registers: one ahead keeps two workgroups per
+// compute unit)
+template <typename Tin>
+constexpr int prefetch_depth() { return sizeof(Tin) == 2 ? 3 : 1; }
 
 struct BwdParams {
     const void *q, *k, *v, *dout;
@@ -81,7 +87,7 @@ __device__ __forceinline__ float groups4_sum(float x) {
 }
 
 template <typename Tin, int DK, int DV, int DVS>
-__global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * (DK / 16), 4) void backward_kernel(BwdParams p) {
     constexpr int NW = DK / 16;   // waves, 16 state rows each
     constexpr int CPL = DVS / 4;  // columns per lane
     __shared__ __align__(16) float part[2][NW][DVS];  // per-wave partial sums over rows
@@ -147,24 +153,39 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
         }
         rpar ^= 1;
     };
-    // A token's inputs for this lane, loaded one token ahead of their use so
-    // that the loads' latency overlaps the step before.
-    struct FIn { float kr, ar, b, vv[CPL]; };
+    // A token's inputs for this lane, kept as loaded (bf16 unconverted) and
+    // issued PD steps ahead of their use, so that a token step does not wait
+    // for a load's latency (the block loops are unrolled: every index into
+    // the per-token arrays is a constant and nothing is copied).
+    // (CPL = 4 columns: one 8-byte load in bf16, 16 bytes in fp32)
+    typedef Tin Tin4 __attribute__((ext_vector_type(4)));
+    static_assert(CPL == 4, "four columns per lane");
+    struct FIn { Tin kr; float ar, b; Tin4 vv; };
+    struct QIn { Tin kr, qr; float ar, b; Tin4 dov; };  // the reverse step's
     auto ld_fin = [&](long tok, FIn& f) {
         const size_t th = (size_t)tok * H + h;
-        f.kr = to_f32(gk[th * DK + row]);
+        f.kr = gk[th * DK + row];
         f.ar = p.alpha[th * DK + row];
         f.b = p.beta[th];
-        ld_cols(gv + th * DV, f.vv);
+        f.vv = *reinterpret_cast<const Tin4*>(gv + th * DV + c0);
+    };
+    auto ld_qin = [&](long tok, QIn& g) {
+        const size_t th = (size_t)tok * H + h;
+        g.kr = gk[th * DK + row];
+        g.qr = gq[th * DK + row];
+        g.ar = p.alpha[th * DK + row];
+        g.b = p.beta[th];
+        g.dov = *reinterpret_cast<const Tin4*>(gdo + th * DV + c0);
     };
     // one forward token step on this lane's run; r receives v - vh
     auto fwd_step = [&](float (&S)[CPL], const FIn& f, float (&r)[CPL]) {
+        const float kr = to_f32(f.kr);
         float x[CPL];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) { S[j] *= f.ar; x[j] = S[j] * f.kr; }
+        for (int j = 0; j < CPL; ++j) { S[j] *= f.ar; x[j] = S[j] * kr; }
         col_sum(x);  // vh
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) { r[j] = f.vv[j] - x[j]; S[j] += f.kr * (f.b * r[j]); }
+        for (int j = 0; j < CPL; ++j) { r[j] = to_f32(f.vv[j]) - x[j]; S[j] += kr * (f.b * r[j]); }
     };
 
     const int nblk = (len + BBLK - 1) / BBLK;
@@ -174,15 +195,24 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) S[j] = 0.f;
     }
-    // sweep 1: checkpoints at the block starts
-    FIn fc, fn;
-    if (len > 0) ld_fin(t0, fn);
-    for (int t = 0; t < len; ++t) {
-        fc = fn;
-        if (t + 1 < len) ld_fin(t0 + t + 1, fn);
-        if (t % BBLK == 0) st_run(ckpt_at(t / BBLK), S);
-        float r[CPL];
-        fwd_step(S, fc, r);
+    // sweep 1: checkpoints at the block starts (the loops over a block are
+    // unrolled so that every index is a constant; nt is uniform)
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int tb = blk * BBLK, nt = min(BBLK, len - tb);
+        constexpr int PD = prefetch_depth<Tin>();
+        FIn f[BBLK];
+#pragma unroll
+        for (int tt = 0; tt < PD; ++tt)
+            if (tt < nt) ld_fin(t0 + tb + tt, f[tt]);
+        st_run(ckpt_at(blk), S);
+#pragma unroll
+        for (int tt = 0; tt < BBLK; ++tt) {
+            if (tt < nt) {
+                if (tt + PD < BBLK && tt + PD < nt) ld_fin(t0 + tb + tt + PD, f[tt + PD]);
+                float r[CPL];
+                fwd_step(S, f[tt], r);
+            }
+        }
     }
     // sweep 2: blocks from the last, each recomputed and then reversed
     float dS[CPL];
@@ -195,9 +225,10 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
     for (int blk = nblk - 1; blk >= 0; --blk) {
         const int tb = blk * BBLK, nt = min(BBLK, len - tb);
         ld_run(ckpt_at(blk), S);
-        // the block's states S_{t-1}, in registers (the loops are unrolled so
-        // that every index into SB is a constant; nt is uniform)
+        // the block's states S_{t-1}, in registers; each token's inputs are
+        // loaded one step ahead
         float SB[BBLK][CPL];
+        FIn fc, fn;
         ld_fin(t0 + tb, fn);
 #pragma unroll
         for (int tt = 0; tt < BBLK; ++tt) {
@@ -212,28 +243,20 @@ __global__ __launch_bounds__(64 * (DK / 16)) void backward_kernel(BwdParams p) {
             }
         }
         lds_barrier();
-        // the reverse step's inputs, one token ahead as well
-        struct BIn { float kr, qr, ar, b, dov[CPL]; };
-        auto ld_bin = [&](int tt, BIn& f) {
-            const size_t th = (size_t)(t0 + tb + tt) * H + h;
-            f.kr = to_f32(gk[th * DK + row]);
-            f.qr = to_f32(gq[th * DK + row]);
-            f.ar = p.alpha[th * DK + row];
-            f.b = p.beta[th];
-            ld_cols(gdo + th * DV, f.dov);
-        };
-        BIn bc, bn;
-        ld_bin(nt - 1, bn);
+        QIn bc, bn;
+        ld_qin(t0 + tb + nt - 1, bn);
 #pragma unroll
         for (int tt = BBLK - 1; tt >= 0; --tt) {
           if (tt < nt) {
             bc = bn;
-            if (tt > 0) ld_bin(tt - 1, bn);
+            if (tt > 0) ld_qin(t0 + tb + tt - 1, bn);
             const long tok = t0 + tb + tt;
             const size_t th = (size_t)tok * H + h;
-            const float kr = bc.kr, qr = bc.qr, ar = bc.ar, b = bc.b;
+            const float kr = to_f32(bc.kr), qr = to_f32(bc.qr), ar = bc.ar, b = bc.b;
             const float(&sp)[CPL] = SB[tt];
-            const float(&dov)[CPL] = bc.dov;
+            float dov[CPL];
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) dov[j] = to_f32(bc.dov[j]);
             float r[CPL];
             ld_run(&resid[tt][cs], r);
             float st[CPL], e[CPL];
