@@ -44,6 +44,7 @@ constexpr int BBLK = 8;  // tokens per checkpoint block
 // compute unit)
 template <typename Tin>
 constexpr int prefetch_depth() { return sizeof(Tin) == 2 ? 3 : 1; }
+constexpr int PD2 = 2;  // the same in the second sweep (whole blocks)
 
 struct BwdParams {
     const void *q, *k, *v, *dout;
@@ -225,31 +226,17 @@ __global__ __launch_bounds__(64 * (DK / 16), 4) void backward_kernel(BwdParams p
     for (int blk = nblk - 1; blk >= 0; --blk) {
         const int tb = blk * BBLK, nt = min(BBLK, len - tb);
         ld_run(ckpt_at(blk), S);
-        // the block's states S_{t-1}, in registers; each token's inputs are
-        // loaded one step ahead
+        // the block's states S_{t-1}, in registers (every index into SB is a
+        // constant once the block loops are unrolled)
         float SB[BBLK][CPL];
-        FIn fc, fn;
-        ld_fin(t0 + tb, fn);
+        auto rec_step = [&](int tt, const FIn& fi) {
 #pragma unroll
-        for (int tt = 0; tt < BBLK; ++tt) {
-            if (tt < nt) {
-                fc = fn;
-                if (tt + 1 < nt) ld_fin(t0 + tb + tt + 1, fn);
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) SB[tt][j] = S[j];
-                float r[CPL];
-                fwd_step(S, fc, r);
-                if (w == 0 && (l & 15) == 0) st_run(&resid[tt][cs], r);
-            }
-        }
-        lds_barrier();
-        QIn bc, bn;
-        ld_qin(t0 + tb + nt - 1, bn);
-#pragma unroll
-        for (int tt = BBLK - 1; tt >= 0; --tt) {
-          if (tt < nt) {
-            bc = bn;
-            if (tt > 0) ld_qin(t0 + tb + tt - 1, bn);
+            for (int j = 0; j < CPL; ++j) SB[tt][j] = S[j];
+            float r[CPL];
+            fwd_step(S, fi, r);
+            if (w == 0 && (l & 15) == 0) st_run(&resid[tt][cs], r);
+        };
+        auto rev_step = [&](int tt, const QIn& bc) {
             const long tok = t0 + tb + tt;
             const size_t th = (size_t)tok * H + h;
             const float kr = to_f32(bc.kr), qr = to_f32(bc.qr), ar = bc.ar, b = bc.b;
@@ -297,7 +284,52 @@ __global__ __launch_bounds__(64 * (DK / 16), 4) void backward_kernel(BwdParams p
                 for (int j = 0; j < CPL; ++j) p.dv[th * DV + c0 + j] = b * de[j];
             }
             if (tid == 0) atomicAdd(p.dbeta + th, db);
-          }
+        };
+        if (nt == BBLK) {
+            // a whole block: every token's loads issued PD2 steps ahead into
+            // slots with constant indices, each defined once
+            FIn f[BBLK];
+            QIn g[BBLK];
+#pragma unroll
+            for (int tt = 0; tt < PD2; ++tt) ld_fin(t0 + tb + tt, f[tt]);
+#pragma unroll
+            for (int tt = 0; tt < BBLK; ++tt) {
+                if (tt + PD2 < BBLK) ld_fin(t0 + tb + tt + PD2, f[tt + PD2]);
+                if (tt >= BBLK - PD2) {  // the reverse walk's first inputs
+                    const int tr = 2 * BBLK - PD2 - 1 - tt;
+                    ld_qin(t0 + tb + tr, g[tr]);
+                }
+                rec_step(tt, f[tt]);
+            }
+            lds_barrier();
+#pragma unroll
+            for (int tt = BBLK - 1; tt >= 0; --tt) {
+                if (tt >= PD2) ld_qin(t0 + tb + tt - PD2, g[tt >= PD2 ? tt - PD2 : 0]);
+                rev_step(tt, g[tt]);
+            }
+        } else {
+            // the short last block of a sequence: loads one step ahead
+            FIn fc, fn;
+            ld_fin(t0 + tb, fn);
+#pragma unroll
+            for (int tt = 0; tt < BBLK; ++tt) {
+                if (tt < nt) {
+                    fc = fn;
+                    if (tt + 1 < nt) ld_fin(t0 + tb + tt + 1, fn);
+                    rec_step(tt, fc);
+                }
+            }
+            lds_barrier();
+            QIn bc, bn;
+            ld_qin(t0 + tb + nt - 1, bn);
+#pragma unroll
+            for (int tt = BBLK - 1; tt >= 0; --tt) {
+                if (tt < nt) {
+                    bc = bn;
+                    if (tt > 0) ld_qin(t0 + tb + tt - 1, bn);
+                    rev_step(tt, bc);
+                }
+            }
         }
         lds_barrier();  // resid is rewritten by the next block
     }
