@@ -34,6 +34,7 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc")
 KERNEL_SOURCES = {
     "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "chunk_common.h", "kda_device.h"],
     "recurrent_step_kernel": ["recurrent_step.hip", "kda_device.h"],
+    "backward_kernel": ["backward.hip", "kda_device.h"],
 }
 
 
@@ -267,7 +268,8 @@ def main():
             "ms_per_step": bms, "tokens_per_s": B * T / (bms / 1e3),
             "roofline": {"bound": "hbm", "achieved": bbytes / (bms / 1e3) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                         "frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("backward_kernel"),
                          "kernel": "backward_kernel", "algorithmic_bytes_per_launch": bbytes}}
 
     if not args.skip_decode:
