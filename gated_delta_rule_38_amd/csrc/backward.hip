@@ -43,7 +43,7 @@ constexpr int BBLK = 8;  // tokens per checkpoint block
 // sweep (fp32 inputs take more registers: one ahead keeps two workgroups per
 // compute unit)
 template <typename Tin>
-constexpr int prefetch_depth() { return sizeof(Tin) == 2 ? 3 : 1; }
+constexpr int prefetch_depth() { return sizeof(Tin) == 2 ? 6 : 1; }
 constexpr int PD2 = 2;  // the same in the second sweep (whole blocks)
 
 struct BwdParams {
