@@ -2,40 +2,61 @@
 
 One step = one kda_chunk_fwd call over the headline workload (bf16, B=4,
 H=16, T=4096, dk=dv=128, chunk 64, nonzero initial state), inputs already
-resident in HBM.  value = tokens per second (B*T tokens per step).  The same
-line also carries the decode workload (256 sequences x 32 heads, d=128, fp32
-state in place, 100 consecutive steps) as GB/s against the HBM roofline.
+resident in HBM.  value = tokens per second (B*T tokens per step).
+
+The same JSON line carries the other workloads of the path, each timed with
+HIP events on the launch stream over its own loop of K launches:
+  long_context  chunk forward, bf16 B1 H32 T65536 (slow forgetting)
+  varlen        chunk forward, 64 packed sequences of 128..8192 tokens, H16
+  decode        100 consecutive in-place decode steps, N256 H32 d128
+  backward      gradients of the headline forward
+For the headline and the decode step it also reports the time of single
+launches that each follow a 1 GiB write (the 256 MB last-level cache then
+holds none of the launch's inputs): the HBM-cold figure beside the
+back-to-back one.
+
+Each workload reports a roofline: algorithmic bytes (every input read once,
+every output written once) and, for the chunk forward, algorithmic matrix
+flops, divided by the measured launch time, against the published MI355X
+peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16).  "traffic" and the executed
+matrix-core figures come from committed rocprofv3 counter runs
+(profiles/counters.json) and are reported only while the kernel source is
+unchanged since those runs.
 
 With --gate head (one decay per token and head: Gated DeltaNet) or --gate
-none (no forget gate: DeltaNet) the same workloads run through the *_gated
-entry points with alpha drawn per head (or absent); the default is the
-per-channel gate of KDA.  With --fused the inputs are stored raw (gate
-logits in bf16, beta logits, q and k not normalised) and the *_fused entry
-points prepare them in the kernel.
+none (no forget gate: DeltaNet) the headline and decode workloads run
+through the *_gated entry points; with --fused the inputs are stored raw
+(gate logits in bf16, beta logits, q and k not normalised) and the *_fused
+entry points prepare them in the kernel.  --only runs a single workload
+(for profiling).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--calib-copy] [--skip-decode] [--gate channel|head|none] [--fused]
+                       [--gate channel|head|none] [--fused] [--only NAME] [--no-flush]
+                       [--calib-copy] [--prep-baseline]
 """
 import argparse
 import hashlib
-import re
 import json
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix throughput, published (no sparsity)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc")
+CHUNK = 64
 # the sources each timed kernel is compiled from (its counters go stale when any changes)
 KERNEL_SOURCES = {
     "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "chunk_common.h", "kda_device.h"],
     "recurrent_step_kernel": ["recurrent_step.hip", "kda_device.h"],
     "backward_kernel": ["backward.hip", "kda_device.h"],
 }
+WORKLOADS = ["headline", "long_context", "varlen", "decode", "backward"]
 
 
 def _code_only(text):
@@ -47,8 +68,8 @@ def _code_only(text):
 
 
 def source_hash(kernel):
-    """Hash of the sources of a kernel; "name[gate=...]" names an instantiation
-    of the same sources."""
+    """Hash of the sources of a kernel; "name[...]" names an instantiation or a
+    workload of the same sources."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel.split("[")[0]]:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
@@ -56,17 +77,17 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when absent or taken on a different version of the kernel source."""
+def measured_counters(kernel):
+    """The committed counter record of a kernel (HBM bytes, matrix-core
+    figures per launch), or {} when absent or taken on other sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             rec = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
-        return None
+        return {}
     if rec.get("source_sha256_16") != source_hash(kernel):
-        return None
-    return rec.get("bytes_per_launch")
+        return {}
+    return rec
 
 
 # alpha values per token and head for each forget gate
@@ -74,21 +95,72 @@ GATE_WIDTH = {"channel": lambda dk: dk, "head": lambda dk: 1, "none": lambda dk:
 GATE_NAME = {"channel": "KDA", "head": "Gated DeltaNet", "none": "DeltaNet"}
 
 
-def chunk_bytes(B, T, H, dk, dv, es=2, nstates=None, gate="channel", ges=4):
-    """Algorithmic HBM bytes of one chunk-wise forward: every input read once,
-    every output written once (ges: bytes per gate element, 4 for float32
-    alpha, es for logits in the storage dtype)."""
-    ns = B if nstates is None else nstates
-    tok = B * T * H
+def chunk_bytes(tokens, H, dk, dv, nstates, es=2, gate="channel", ges=4):
+    """Algorithmic HBM bytes of one chunk-wise forward over `tokens` packed
+    tokens: every input read once, every output written once (ges: bytes per
+    gate element, 4 for float32 alpha, es for logits in the storage dtype)."""
+    tok = tokens * H
     aw = GATE_WIDTH[gate](dk)
     return (tok * (2 * dk * es + dv * es + aw * ges + 4 + dv * es)  # q, k, v, alpha, beta, o
-            + 2 * ns * H * dk * dv * 4)                              # initial + final state
+            + 2 * nstates * H * dk * dv * 4)                         # initial + final state
+
+
+def chunk_flops(tokens, H, dk, dv, C=CHUNK):
+    """Algorithmic matrix flops of one chunk-wise forward, triangle-aware, per
+    token and head: 6 dk dv (three state-sized products: Kr S, Qr S and the
+    state update) + C (3 dk + 2 dv) (the Gram, the intra-chunk attention, the
+    solve and M U, each over half a chunk on average) + 2 C^2 / 3 (the
+    triangular inverse)."""
+    return tokens * H * (6 * dk * dv + C * (3 * dk + 2 * dv) + 2 * C * C / 3)
 
 
 def decode_bytes(N, H, dk, dv, es=2, gate="channel", ges=4):
     """Algorithmic HBM bytes of one decode step."""
     aw = GATE_WIDTH[gate](dk)
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + aw * ges + 4 + dv * es)
+
+
+def backward_bytes(tokens, H, dk, dv, nstates, es=2):
+    """Algorithmic HBM bytes of one backward call: q, k, v, alpha, beta, dout,
+    S0 and dS_T read once; dq, dk, dv, dalpha, dbeta (float32) and dS0 written
+    once."""
+    return (tokens * H * (2 * dk * es + dv * es + dk * 4 + 4 + dv * es
+                          + 4 * (2 * dk + dv + dk) + 4) + 3 * nstates * H * dk * dv * 4)
+
+
+def roofline(bytes_alg, ms, kernel, flops_alg=None):
+    """The roofline object for one kernel: algorithmic bytes (and flops) per
+    launch over the measured launch time against the published peaks."""
+    gbs = bytes_alg / (ms / 1e3) / 1e9
+    rec = measured_counters(kernel)
+    r = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": gbs / HBM_PEAK_GBS, "traffic": rec.get("bytes_per_launch"),
+         "kernel": kernel.split("[")[0], "algorithmic_bytes_per_launch": bytes_alg,
+         "avg_launch_ms": ms}
+    if flops_alg is not None:
+        tfs = flops_alg / (ms / 1e3) / 1e12
+        r["mfma"] = {"achieved": tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": tfs / MFMA_BF16_PEAK_TFS, "algorithmic_flops_per_launch": flops_alg}
+        if rec.get("mfma_flops_bf16_per_launch") is not None:
+            r["mfma"]["executed_flops_per_launch"] = rec["mfma_flops_bf16_per_launch"]
+            r["mfma"]["busy_frac"] = rec.get("mfma_busy_frac")
+        # fraction of the binding roofline: the larger of the two floors over the time
+        floor = max(flops_alg / (MFMA_BF16_PEAK_TFS * 1e12), bytes_alg / (HBM_PEAK_GBS * 1e9))
+        r["binding_frac"] = floor / (ms / 1e3)
+        if flops_alg / (MFMA_BF16_PEAK_TFS * 1e12) > bytes_alg / (HBM_PEAK_GBS * 1e9):
+            r["bound"] = "mfma"
+    return r
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -101,6 +173,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--only", choices=WORKLOADS, default=None,
+                    help="run one workload only (profiling runs)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the single launches timed after a cache flush")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--gate", choices=sorted(GATE_WIDTH), default="channel",
@@ -109,9 +185,6 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="raw inputs (bf16 gate logits, beta logits, q and k not normalised) "
                          "prepared in the kernel")
-    ap.add_argument("--backward", action="store_true",
-                    help="also time kda_backward (gradients of the same forward, random dL/do "
-                         "and dL/dS_T) on the chunk workload")
     ap.add_argument("--prep-baseline", action="store_true",
                     help="with --fused: also time the same preparation done by torch "
                          "elementwise kernels followed by the plain entry point")
@@ -122,9 +195,15 @@ def main():
     ges = 2 if fused else 4
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the workload shards by (batch, head) with no exchange; see DESIGN.md). "
+              "(the workload shards by (batch, head) with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    plain = gate == "channel" and not fused
+    run = {w: (args.only is None or args.only == w) for w in WORKLOADS}
+    if args.skip_decode:
+        run["decode"] = False
+    if not plain:  # the variants cover the headline and the decode step
+        run["long_context"] = run["varlen"] = run["backward"] = False
 
     import torch
     import gated_delta_rule_38_amd as kda
@@ -132,152 +211,177 @@ def main():
 
     dev = torch.device("cuda:0")
     kda.load_library()
+    stream = torch.cuda.current_stream(dev)  # the launch stream of every libkda call
+
+    def timed(fn, steps, warmup):
+        """Average ms per call over `steps` calls after `warmup` untimed ones,
+        HIP events on the launch stream around the whole loop."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    flush_buf = [None]
+
+    def flushed(fn, n):
+        """Median and min ms of n single calls, each after a 1 GiB write (a
+        fill kernel) that leaves none of the call's inputs in the caches."""
+        if flush_buf[0] is None:
+            flush_buf[0] = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        ts = []
+        for _ in range(n):
+            flush_buf[0].fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return {"median_ms": ts[len(ts) // 2], "min_ms": ts[0], "launches": n}
+
+    out = {}
     cfg = CONFIGS[1]
-    d = gen.chunk_inputs(cfg, device=dev, gate=gate, raw=fused)
     B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
-    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
-    fs = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    d = None
+    if run["headline"] or run["backward"] or not args.no_cpu_baseline:
+        d = gen.chunk_inputs(cfg, device=dev, gate=gate, raw=fused)
+    ms = None
+    if run["headline"]:
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        fs = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
 
-    def step():
+        def step():
+            if fused:
+                kda.kda_chunk_fwd_fused(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                        d["initial_state"], o=o, final_state=fs, gate_kind=gate,
+                                        **fl)
+            elif gate == "channel":
+                kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                  d["initial_state"], o=o, final_state=fs)
+            else:
+                kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                        d["initial_state"], o=o, final_state=fs, gate=gate)
+
+        t0 = time.perf_counter()
+        ms = timed(step, args.steps, args.warmup)
+        wall = time.perf_counter() - t0
+        variant = ([] if gate == "channel" else ["gate=%s" % gate]) + (["fused"] if fused else [])
+        kname = "chunk_fwd_bf16_kernel" + ("[%s]" % ",".join(variant) if variant else "")
+        wl = {"channel": "kda_chunk_fwd", "head": "kda_chunk_fwd_gated (per-head alpha)",
+              "none": "kda_chunk_fwd_gated (no gate)"}[gate]
         if fused:
-            kda.kda_chunk_fwd_fused(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                    d["initial_state"], o=o, final_state=fs, gate_kind=gate, **fl)
-        elif gate == "channel":
-            kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
-                              o=o, final_state=fs)
-        else:
-            kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                    d["initial_state"], o=o, final_state=fs, gate=gate)
+            wl = ("kda_chunk_fwd_fused (%s gate, bf16 gate logits, beta logits, q/k L2 norm "
+                  "in-kernel)" % gate)
+        out.update({
+            "metric": "%s%s chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline" % (
+                GATE_NAME[gate], " (fused input preparation)" if fused else ""),
+            "value": B * T / (ms / 1e3),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": wl + " bf16 B4 H16 T4096 dk128 dv128 chunk64, "
+                                   "initial state N(0,0.02)",
+                       "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": CHUNK,
+                       "parallelism": "single GPU"},
+            "roofline": roofline(chunk_bytes(B * T, H, dk, dv, B, gate=gate, ges=ges), ms, kname,
+                                 chunk_flops(B * T, H, dk, dv)),
+            "timed_wall_s": wall,
+        })
+        if not args.no_flush:
+            out["roofline"]["hbm_cold"] = flushed(step, 20)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)  # the launch stream of kda_chunk_fwd
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
-    tokens = B * T
-    value = tokens * args.steps / (ms * args.steps / 1e3)
-    alg = chunk_bytes(B, T, H, dk, dv, gate=gate, ges=ges)
-    achieved = alg / (ms / 1e3) / 1e9
-    variant = ([] if gate == "channel" else ["gate=%s" % gate]) + (["fused"] if fused else [])
-    traffic = measured_traffic("chunk_fwd_bf16_kernel" +
-                               ("[%s]" % ",".join(variant) if variant else ""))
-    gname = GATE_NAME[gate]
-    wl = {"channel": "kda_chunk_fwd", "head": "kda_chunk_fwd_gated (per-head alpha)",
-          "none": "kda_chunk_fwd_gated (no gate)"}[gate]
-    if fused:
-        wl = ("kda_chunk_fwd_fused (%s gate, bf16 gate logits, beta logits, q/k L2 norm "
-              "in-kernel)" % gate)
+        if fused and args.prep_baseline:
+            def prep():
+                qn = torch.nn.functional.normalize(d["q"].float(), dim=-1, eps=1e-3).to(
+                    d["q"].dtype)
+                kn = torch.nn.functional.normalize(d["k"].float(), dim=-1, eps=1e-3).to(
+                    d["k"].dtype)
+                a = None if d["alpha"] is None else torch.sigmoid(d["alpha"].float())
+                return qn, kn, a, torch.sigmoid(d["beta"])
 
-    out = {
-        "metric": "%s%s chunk-fwd tokens/s (B4 H16 T4096 d128) + decode GB/s vs roofline" % (
-            gname, " (fused input preparation)" if fused else ""),
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl + " bf16 B4 H16 T4096 dk128 dv128 chunk64, "
-                               "initial state N(0,0.02)",
-                   "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": 64,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunk_fwd_bf16_kernel", "algorithmic_bytes_per_launch": alg,
-                     "avg_launch_ms": ms},
-        "timed_wall_s": wall,
-    }
+            def unfused():
+                qn, kn, a, b = prep()
+                kda.kda_chunk_fwd_gated(qn, kn, d["v"], a, b, d["initial_state"], o=o,
+                                        final_state=fs, gate=gate)
+            n = max(10, args.steps // 2)
+            out["prep_baseline"] = {
+                "what": "torch elementwise preparation (normalise q and k, sigmoid of the "
+                        "logits) then kda_chunk_fwd_gated, same inputs",
+                "prep_ms": timed(prep, n, n), "prep_plus_chunk_ms": timed(unfused, n, n),
+                "fused_ms": ms}
+        del o, fs
 
-    if fused and args.prep_baseline:
-        def prep():
-            qn = torch.nn.functional.normalize(d["q"].float(), dim=-1, eps=1e-3).to(d["q"].dtype)
-            kn = torch.nn.functional.normalize(d["k"].float(), dim=-1, eps=1e-3).to(d["k"].dtype)
-            a = None if d["alpha"] is None else torch.sigmoid(d["alpha"].float())
-            return qn, kn, a, torch.sigmoid(d["beta"])
+    for name, ci in (("long_context", 2), ("varlen", 4)):
+        if not run[name]:
+            continue
+        c = CONFIGS[ci]
+        dd = gen.chunk_inputs(c, device=dev)
+        toks = dd["q"].shape[0] * dd["q"].shape[1]
+        nst = dd["cu_seqlens"].numel() - 1 if dd["cu_seqlens"] is not None else c.B
+        ol = torch.empty_like(dd["v"])
+        fl_ = torch.empty((nst, c.H, c.dk, c.dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, kda.kda_chunk_fwd_workspace_size(
+            1, toks, c.H, c.dk, c.dv, nst if dd["cu_seqlens"] is not None else 0)),
+            dtype=torch.uint8, device=dev)
 
-        def unfused():
-            qn, kn, a, b = prep()
-            kda.kda_chunk_fwd_gated(qn, kn, d["v"], a, b, d["initial_state"], o=o, final_state=fs,
-                                    gate=gate)
+        def lstep():
+            kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"],
+                              dd["initial_state"], cu_seqlens=dd["cu_seqlens"],
+                              cu_seqlens_host=dd["cu_seqlens_host"], o=ol, final_state=fl_,
+                              workspace=ws)
+        lms = timed(lstep, args.steps, args.warmup if args.only else max(5, args.warmup // 10))
+        desc = ("kda_chunk_fwd bf16 B1 H32 T65536 dk128 dv128 chunk64, zero initial state, "
+                "alpha = sigmoid(N(5,1))" if name == "long_context" else
+                "kda_chunk_fwd bf16 varlen: 64 packed sequences, lengths U{128..8192} "
+                "(%d tokens), H16 dk128 dv128, initial states N(0,0.02)" % toks)
+        out[name] = {"workload": desc, "ms_per_step": lms, "tokens_per_s": toks / (lms / 1e3),
+                     "roofline": roofline(chunk_bytes(toks, c.H, c.dk, c.dv, nst), lms,
+                                          "chunk_fwd_bf16_kernel[%s]" % name,
+                                          chunk_flops(toks, c.H, c.dk, c.dv))}
+        del dd, ol, fl_, ws
 
-        def time_fn(fn, n):
-            for _ in range(n):
-                fn()
-            torch.cuda.synchronize()
-            g0 = torch.cuda.Event(enable_timing=True)
-            g1 = torch.cuda.Event(enable_timing=True)
-            g0.record(stream)
-            for _ in range(n):
-                fn()
-            g1.record(stream)
-            torch.cuda.synchronize()
-            return g0.elapsed_time(g1) / n
-        n = max(10, args.steps // 2)
-        out["prep_baseline"] = {
-            "what": "torch elementwise preparation (normalise q and k, sigmoid of the logits) "
-                    "then kda_chunk_fwd_gated, same inputs",
-            "prep_ms": time_fn(prep, n), "prep_plus_chunk_ms": time_fn(unfused, n),
-            "fused_ms": ms}
-
-    if args.backward and gate == "channel" and not fused:
+    if run["backward"]:
         gg = torch.Generator(device=dev)
         gg.manual_seed(11)
         dout = torch.randn((B, T, H, dv), generator=gg, device=dev).to(d["q"].dtype)
         dsT = torch.randn((B, H, dk, dv), generator=gg, device=dev)
-        ws = torch.empty(kda.kda_backward_workspace_size(B, T, H, dk, dv, 0), dtype=torch.uint8,
-                         device=dev)
+        ws = torch.empty(max(1, kda.kda_backward_workspace_size(B, T, H, dk, dv, 0)),
+                         dtype=torch.uint8, device=dev)
 
         def bstep():
             return kda.kda_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
                                     d["initial_state"], dout, dsT, workspace=ws)
         nb = max(2, args.steps // 20)
-        for _ in range(2):
-            bstep()
-        torch.cuda.synchronize()
-        b0 = torch.cuda.Event(enable_timing=True)
-        b1 = torch.cuda.Event(enable_timing=True)
-        b0.record(stream)
-        for _ in range(nb):
-            bstep()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        bms = b0.elapsed_time(b1) / nb
-        # inputs q, k, v, alpha, beta, dout, S0, dS_T read once; dq, dk, dv,
-        # dalpha, dbeta (fp32) and dS_0 written once
-        es = 2
-        bbytes = (B * T * H * (2 * dk * es + dv * es + dk * 4 + 4 + dv * es
-                               + 4 * (2 * dk + dv + dk) + 4) + 3 * B * H * dk * dv * 4)
+        bms = timed(bstep, nb, 2)
         out["backward"] = {
             "workload": "kda_backward bf16 B4 H16 T4096 dk128 dv128 (per-channel gate), "
                         "fp32 gradients",
             "ms_per_step": bms, "tokens_per_s": B * T / (bms / 1e3),
-            "roofline": {"bound": "hbm", "achieved": bbytes / (bms / 1e3) / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": bbytes / (bms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("backward_kernel"),
-                         "kernel": "backward_kernel", "algorithmic_bytes_per_launch": bbytes}}
+            "roofline": roofline(backward_bytes(B * T, H, dk, dv, B), bms, "backward_kernel")}
+        del dout, dsT, ws
 
-    if not args.skip_decode:
+    if run["decode"]:
         dc = CONFIGS[3]
-        dd = gen.decode_inputs(dc, device=dev, gate=gate, raw=fused)
-        state = dd["state"].clone()
+        ddc = gen.decode_inputs(dc, device=dev, gate=gate, raw=fused)
+        state = ddc["state"].clone()
         od = torch.empty((dc.B, dc.H, dc.dv), dtype=torch.bfloat16, device=dev)
-        sargs = [[None if dd[n] is None else dd[n][t] for n in ("q", "k", "v", "alpha", "beta")]
+        sargs = [[None if ddc[n] is None else ddc[n][t] for n in ("q", "k", "v", "alpha", "beta")]
                  for t in range(dc.steps)]
 
         def dstep(t, st):
@@ -301,7 +405,7 @@ def main():
         torch.cuda.synchronize()
         us = f0.elapsed_time(f1) * 1e3 / dc.steps
         dbytes = decode_bytes(dc.B, dc.H, dc.dk, dc.dv, gate=gate, ges=ges)
-        gbs = dbytes / (us / 1e6) / 1e9
+        kname = "recurrent_step_kernel" + ("" if plain else "[variant]")
         out["decode"] = {
             "workload": "%s bf16 N256 H32 dk128 dv128, fp32 state in place, "
                         "100 consecutive steps" % (
@@ -309,13 +413,38 @@ def main():
                             "kda_recurrent_step" if gate == "channel" else
                             "kda_recurrent_step_gated (gate %s)" % gate),
             "us_per_step": us, "tokens_per_s": dc.B / (us / 1e6),
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("recurrent_step_kernel")
-                         if gate == "channel" and not fused else None,
-                         "kernel": "recurrent_step_kernel",
-                         "algorithmic_bytes_per_launch": dbytes},
+            "roofline": roofline(dbytes, us / 1e3, kname),
         }
+        if not args.no_flush:
+            cnt = [0]
+
+            def one():
+                dstep(cnt[0] % dc.steps, state)
+                cnt[0] += 1
+            cold = flushed(one, 20)
+            cold["achieved_GBs_median"] = dbytes / (cold["median_ms"] / 1e3) / 1e9
+            cold["frac_median"] = cold["achieved_GBs_median"] / HBM_PEAK_GBS
+            out["decode"]["roofline"]["hbm_cold"] = cold
+        if "value" not in out:  # --only decode: the decode step is the line's workload
+            out.update({"metric": "KDA decode step GB/s (N256 H32 d128) vs roofline",
+                        "value": dbytes / (us / 1e6) / 1e9, "unit": "GB/s", "n_gpus": 1,
+                        "steps": dc.steps, "warmup": 3, "ms_per_step": us / 1e3,
+                        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                        "dtype": "f32", "data": "synthetic",
+                        "config": {"workload": out["decode"]["workload"]},
+                        "roofline": out["decode"]["roofline"]})
+        del ddc, state, sargs
+
+    for name in ("long_context", "varlen", "backward"):  # --only of one of these
+        if "value" not in out and name in out:
+            rec = out[name]
+            out.update({"metric": "KDA %s tokens/s vs roofline" % name, "value":
+                        rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                        "steps": args.steps, "warmup": args.warmup,
+                        "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
+                        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                        "data": "synthetic", "config": {"workload": rec["workload"]},
+                        "roofline": rec["roofline"]})
 
     if args.calib_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -326,7 +455,7 @@ def main():
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = src.numel() * 4
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and d is not None:
         import oracle
         # one unit per (batch, head): [B*H, T, d] blocks of the stored inputs
         def units(x):
@@ -345,8 +474,8 @@ def main():
             alpha = oracle.channel_gate(a_units, gate, dk, (B * H, T))
         oracle.forward_units(qh, kh, host["v"], alpha, bh, s0, threads=cores)
         cw = time.perf_counter() - c0
-        out["cpu_baseline"] = {"value": tokens / cw, "unit": "tokens/s", "cores": cores,
-                               "kind": "oracle",
+        out["cpu_baseline"] = {"value": B * T / cw, "unit": "tokens/s", "cores": cores,
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": "the whole B4 H16 T4096 workload (64 (batch, head) "
                                          "units x 4096 tokens), fp64 token loop incl. input "
                                          "widening; wall %.2f s" % cw}

@@ -120,10 +120,6 @@ __global__ __launch_bounds__(64 * (DK / 16), 4) void backward_kernel(BwdParams p
         return p.ckpt + ((size_t)(slot0 + blk) * H + h) * DK * DV + (size_t)row * DV + c0;
     };
 
-    auto ld_cols = [&](const Tin* base, float (&x)[CPL]) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) x[j] = to_f32(base[c0 + j]);
-    };
     auto ld_run = [&](const float* src, float (&x)[CPL]) {
 #pragma unroll
         for (int j = 0; j < CPL; j += 4) {
@@ -342,13 +338,17 @@ hipError_t launch_bwd_t(BwdParams p, long tokens, hipStream_t stream) {
     p.nslice = DV / DVS;
     // the column sums are accumulated: clear dq, dk, dalpha (tokens*H*dk each) and dbeta
     const size_t nk = (size_t)tokens * p.H * DK, nb = (size_t)tokens * p.H;
-    float* zs[] = {p.dq, p.dk, p.dalpha};
-    for (float* z : zs) {
-        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<size_t>((nk + 255) / 256, 4096)),
-                           dim3(256), 0, stream, z, nk);
+    // (no tokens: nothing to clear, and a grid of zero workgroups is not a launch)
+    if (nk > 0) {
+        float* zs[] = {p.dq, p.dk, p.dalpha};
+        for (float* z : zs) {
+            hipLaunchKernelGGL(zero_kernel,
+                               dim3((unsigned)std::min<size_t>((nk + 255) / 256, 4096)), dim3(256),
+                               0, stream, z, nk);
+        }
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<size_t>((nb + 255) / 256, 4096)),
+                           dim3(256), 0, stream, p.dbeta, nb);
     }
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<size_t>((nb + 255) / 256, 4096)),
-                       dim3(256), 0, stream, p.dbeta, nb);
     hipLaunchKernelGGL((backward_kernel<Tin, DK, DV, DVS>), dim3(p.units * p.nslice),
                        dim3(64 * (DK / 16)), 0, stream, p);
     return hipGetLastError();

@@ -230,9 +230,11 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
                            !dalpha || !dbeta))
             return KDA_ERROR_INVALID_VALUE;
         if (units > 0 && !dinitial_state) return KDA_ERROR_INVALID_VALUE;
-        const void* elems[] = {q, k, v, dout};
+        const void* elems[] = {q, k};
         for (const void* ptr : elems)
             if (!aligned(ptr, es)) return KDA_ERROR_MISALIGNED;
+        // v and dout are read as runs of four elements
+        if (!aligned(v, 4 * es) || !aligned(dout, 4 * es)) return KDA_ERROR_MISALIGNED;
         const void* words[] = {alpha, beta, dq, dk, dv, dalpha, dbeta};
         for (const void* ptr : words)
             if (!aligned(ptr, 4)) return KDA_ERROR_MISALIGNED;

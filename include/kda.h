@@ -249,10 +249,16 @@ size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_
  *   dalpha        [B, T, H, dk]  float32 (written)
  *   dbeta         [B, T, H]      float32 (written)
  *   dinitial_state [Ns, H, dk, dv] float32 (written; required)
- * The states and their gradients need 16-byte alignment.  workspace: device
- * memory of at least kda_backward_workspace_size() bytes, 256-byte aligned.
- * Outputs must not overlap inputs, each other or the workspace.  Errors as
- * for kda_chunk_fwd.
+ * The states and their gradients need 16-byte alignment, v and dout four
+ * times their element size (8 bytes for bf16, 16 for float32), the other
+ * tensors their element size.  workspace: device memory of at least
+ * kda_backward_workspace_size() bytes, 256-byte aligned.  Outputs must not
+ * overlap inputs, each other or the workspace.  Errors as for kda_chunk_fwd.
+ * T == 0 (or varlen with every sequence empty) is valid: dinitial_state is
+ * then dfinal_state (zero if NULL).
+ * Determinism: dv and dinitial_state are bitwise reproducible; dq, dk,
+ * dalpha and dbeta sum the contributions of the dv/16 column slices of a
+ * unit with float atomics, so their last bits can differ from run to run.
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const float *alpha,
                         const float *beta, const float *initial_state, const void *dout,

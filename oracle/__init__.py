@@ -52,6 +52,10 @@ def _load():
         lib.kda_oracle_step.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                         ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_double, ctypes.c_int]
+        lib.kda_oracle_backward.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [dp] * 14 + [ctypes.c_long, ctypes.c_long,
+                                                        ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_double, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -185,19 +189,45 @@ def forward(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, scale=Non
     return o_all, s_all
 
 
-def backward_units(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, scale=None):
-    """Gradients of the token loop, float64, by the chain rule through its four
-    steps in reverse order (forget, predict, correct and write, read; the
-    update equation of "Kimi Delta Attention", section "KDA 的更新式", with
-    the order of bugfactory.tech news 3610, second to fourth paragraphs).
+def backward_units(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, scale=None,
+                   threads=0):
+    """Gradients of the token loop, float64: ``kda_oracle_backward`` in
+    ``kda_oracle.c``, the chain rule through the four steps of each token
+    (forget, predict, correct and write, read; the update equation of "Kimi
+    Delta Attention", section "KDA 的更新式", with the order of
+    bugfactory.tech news 3610, second to fourth paragraphs) in reverse token
+    order, threaded over the independent units.
 
     q, k, alpha: [U, T, dk]; v: [U, T, dv]; beta: [U, T]; initial_state
     [U, dk, dv] or None; do: [U, T, dv] (gradient of o); dfinal_state
     [U, dk, dv] or None (gradient of the final state).
     Returns dq, dk, dv, dalpha, dbeta, dinitial_state (same shapes as the
-    inputs).  The forward states are kept for the reverse sweep, so this is
-    for small cases only.
+    inputs).  Each thread keeps one unit's T forward states (T * dk * dv
+    doubles).
     """
+    q, k, v, alpha, beta, do = (_f64(x) for x in (q, k, v, alpha, beta, do))
+    s0, dsT = _f64(initial_state), _f64(dfinal_state)
+    U, T, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (U, T, dk) and alpha.shape == (U, T, dk) and beta.shape == (U, T)
+    assert v.shape == (U, T, dv) and do.shape == (U, T, dv)
+    if scale is None:
+        scale = dk ** -0.5
+    g = [np.zeros_like(x) for x in (q, k, v, alpha, beta)] + [np.zeros((U, dk, dv))]
+    rc = _load().kda_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(s0), _ptr(do), _ptr(dsT), *[_ptr(x) for x in g],
+                                     U, T, dk, dv, float(scale), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_backward failed with %d" % rc)
+    return tuple(g)
+
+
+def backward_units_numpy(q, k, v, alpha, beta, initial_state, do, dfinal_state=None,
+                         scale=None):
+    """The same gradients written a second time, in NumPy with the steps as
+    whole-array operations (small cases only: the forward states of every
+    unit are kept).  It serves to pin ``backward_units``; both are pinned by
+    central differences of the forward."""
     q, k, v, alpha, beta, do = (_f64(x) for x in (q, k, v, alpha, beta, do))
     U, T, dk = q.shape
     dv = v.shape[2]
@@ -239,45 +269,54 @@ def backward_units(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, s
 
 
 def backward(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, cu_seqlens=None,
-             scale=None):
+             scale=None, threads=0, heads=None):
     """backward_units in the library's token layout (dense [B, T, H, d], or
     B == 1 with cu_seqlens); returns dq, dk, dv, dalpha, dbeta, dinitial_state
-    ([B or N, H, dk, dv])."""
+    ([B or N, H, dk, dv]).  heads: optional list of head indices (a sample);
+    the results then hold only those heads, in that order."""
     q, k, v, alpha, beta, do = (_f64(x) for x in (q, k, v, alpha, beta, do))
     s0 = _f64(initial_state)
     ds = _f64(dfinal_state)
     B, T, H, dk = q.shape
     dv = v.shape[3]
+    hs = list(range(H)) if heads is None else list(heads)
+    sel = np.asarray(hs, dtype=np.int64)
     if cu_seqlens is None:
         starts = [(b, 0, T) for b in range(B)]
     else:
+        assert B == 1
         cu = [int(c) for c in cu_seqlens]
         starts = [(0, cu[n], cu[n + 1] - cu[n]) for n in range(len(cu) - 1)]
-    outs = [np.zeros_like(x) for x in (q, k, v, alpha, beta)]
-    g_s0 = np.zeros((len(starts), H, dk, dv))
+    Hs = len(hs)
+    outs = [np.zeros((B, T, Hs) + x.shape[3:]) for x in (q, k, v, alpha, beta)]
+    g_s0 = np.zeros((len(starts), Hs, dk, dv))
     for n, (b, t0, L) in enumerate(starts):
-        def units(x):  # [L, H, d] -> [H, L, d]
-            return np.moveaxis(x[b, t0:t0 + L], 1, 0)
-        res = backward_units(units(q), units(k), units(v), units(alpha),
-                             beta[b, t0:t0 + L].T, None if s0 is None else s0[n],
-                             units(do), None if ds is None else ds[n], scale=scale)
-        for i in range(4):
+        def units(x):  # [L, H, ...] -> [Hs, L, ...]
+            return np.ascontiguousarray(np.moveaxis(x[b, t0:t0 + L][:, sel], 1, 0))
+        res = backward_units(units(q), units(k), units(v), units(alpha), units(beta),
+                             None if s0 is None else s0[n][sel], units(do),
+                             None if ds is None else ds[n][sel], scale=scale, threads=threads)
+        for i in range(5):
             outs[i][b, t0:t0 + L] = np.moveaxis(res[i], 0, 1)
-        outs[4][b, t0:t0 + L] = res[4].T
         g_s0[n] = res[5]
     return tuple(outs) + (g_s0,)
 
 
-def step(q, k, v, alpha, beta, state, scale=None, threads=0):
+def step(q, k, v, alpha, beta, state, scale=None, threads=0, in_place=False):
     """One decode step.  q, k, alpha [N, H, dk]; v [N, H, dv]; beta [N, H];
-    state [N, H, dk, dv].  Returns (o [N, H, dv], new_state), float64; the
-    input state is not modified."""
-    q, k, v, alpha, beta, st = (_f64(x) for x in (q, k, v, alpha, beta, state))
+    state [N, H, dk, dv].  Returns (o [N, H, dv], new_state), float64.  The
+    input state is not modified unless in_place is set and it is already a
+    contiguous float64 array, which is then rewritten and returned."""
+    q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
     N, H, dk = q.shape
     dv = v.shape[2]
     if scale is None:
         scale = dk ** -0.5
-    st = st.reshape(N * H, dk, dv).copy()
+    if in_place and isinstance(state, np.ndarray) and state.dtype == np.float64 \
+            and state.flags.c_contiguous:
+        st = state.reshape(N * H, dk, dv)
+    else:
+        st = _f64(state).reshape(N * H, dk, dv).copy()
     o = np.zeros((N * H, dv), np.float64)
     rc = _load().kda_oracle_step(_ptr(np.ascontiguousarray(q.reshape(N * H, dk))),
                                  _ptr(np.ascontiguousarray(k.reshape(N * H, dk))),

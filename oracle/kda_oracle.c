@@ -210,3 +210,236 @@ int kda_oracle_step(const double *q, const double *k, const double *v,
     return kda_oracle_forward(q, k, v, alpha, beta, state, o, state,
                               n_units, 1, dk, dv, scale, n_threads);
 }
+
+/*
+ * Gradients of the token loop above, by the chain rule through its four steps
+ * taken in reverse token order.  For one unit, with e_t = beta_t (v_t - vhat_t)
+ * the written error and dS the gradient of the loss with respect to the state
+ * after token t (dS_T given, zero if absent):
+ *
+ *   read      o_t = scale S_t^T q_t      dq_t  = scale S_t do_t
+ *                                        dS   += scale q_t do_t^T
+ *   write     S_t = S~ + k_t e_t^T       dk_t  = dS e_t,   de = dS^T k_t
+ *   correct   e_t = beta_t (v_t - vhat)  dbeta_t = de . (v_t - vhat)
+ *                                        dv_t  = beta_t de,  dvhat = -beta_t de
+ *   predict   vhat = S~^T k_t            dS~   = dS + k_t dvhat^T
+ *                                        dk_t += S~ dvhat
+ *   forget    S~ = Diag(alpha_t) S_{t-1} dalpha_t[i] = sum_j dS~[i][j] S_{t-1}[i][j]
+ *                                        dS    = Diag(alpha_t) dS~
+ *
+ * and dS_0 is dS after token 0.  The steps and their order are those of the
+ * forward ("Kimi Delta Attention", section "KDA 的更新式"; bugfactory.tech
+ * news 3610, second to fourth paragraphs).  The forward states S_{t-1} of the
+ * unit are kept for the reverse sweep (T * dk * dv doubles per thread), so
+ * nothing is recomputed and nothing is blocked.
+ *
+ * Layouts as for kda_oracle_forward; dout [n_units][T][dv]; dsT [n_units][dk][dv]
+ * or NULL; the gradients have the shapes of their inputs (dbeta [n_units][T],
+ * ds0 [n_units][dk][dv]).
+ */
+typedef struct {
+    const double *q, *k, *v, *alpha, *beta, *s0, *dout, *dsT;
+    double *gq, *gk, *gv, *ga, *gb, *gs0;
+    long n_units, T;
+    int dk, dv;
+    double scale;
+    long next_unit;
+    pthread_mutex_t lock;
+} bwd_job_t;
+
+typedef struct {
+    double *sprev;  /* [T][dk][dv]: S_{t-1} for every token */
+    double *resid;  /* [T][dv]: v_t - vhat_t */
+    double *S, *dS, *dSt, *vhat, *de;
+} bwd_scratch_t;
+
+static void bwd_unit(const bwd_job_t *J, long u, bwd_scratch_t *W)
+{
+    const int dk = J->dk, dv = J->dv;
+    const long T = J->T, dd = (long)dk * dv;
+    const double *q = J->q + u * T * dk, *k = J->k + u * T * dk;
+    const double *a = J->alpha + u * T * dk, *b = J->beta + u * T;
+    const double *v = J->v + u * T * dv, *dout = J->dout + u * T * dv;
+    double *gq = J->gq + u * T * dk, *gk = J->gk + u * T * dk;
+    double *gv = J->gv + u * T * dv, *ga = J->ga + u * T * dk, *gb = J->gb + u * T;
+    double *S = W->S, *dS = W->dS, *dSt = W->dSt, *vhat = W->vhat, *de = W->de;
+
+    /* forward sweep, keeping S_{t-1} and the residual v_t - vhat_t */
+    if (J->s0)
+        memcpy(S, J->s0 + u * dd, sizeof(double) * dd);
+    else
+        memset(S, 0, sizeof(double) * dd);
+    for (long t = 0; t < T; ++t) {
+        const double *at = a + t * dk, *kt = k + t * dk, *vt = v + t * dv;
+        double *rt = W->resid + t * dv;
+        memcpy(W->sprev + t * dd, S, sizeof(double) * dd);
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[i * dv + j] *= at[i];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += S[i * dv + j] * kt[i];
+            rt[j] = vt[j] - acc;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[i * dv + j] += b[t] * kt[i] * rt[j];
+    }
+
+    /* reverse sweep */
+    if (J->dsT)
+        memcpy(dS, J->dsT + u * dd, sizeof(double) * dd);
+    else
+        memset(dS, 0, sizeof(double) * dd);
+    for (long t = T - 1; t >= 0; --t) {
+        const double *at = a + t * dk, *kt = k + t * dk, *qt = q + t * dk;
+        const double *dot = dout + t * dv, *rt = W->resid + t * dv;
+        const double *sp = W->sprev + t * dd;
+        const double bt = b[t];
+        /* S~ = Diag(alpha_t) S_{t-1} (kept in dSt for now) and S_t = S~ + k e^T */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[i * dv + j] = at[i] * sp[i * dv + j] + kt[i] * bt * rt[j];
+        /* read */
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j)
+                acc += S[i * dv + j] * dot[j];
+            gq[t * dk + i] = J->scale * acc;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                dS[i * dv + j] += J->scale * qt[i] * dot[j];
+        /* write */
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j)
+                acc += dS[i * dv + j] * bt * rt[j];
+            gk[t * dk + i] = acc;
+        }
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += dS[i * dv + j] * kt[i];
+            de[j] = acc;
+        }
+        /* correct */
+        {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j)
+                acc += de[j] * rt[j];
+            gb[t] = acc;
+        }
+        for (int j = 0; j < dv; ++j) {
+            gv[t * dv + j] = bt * de[j];
+            vhat[j] = -bt * de[j];  /* dvhat */
+        }
+        /* predict: dS~ = dS + k dvhat^T, dk += S~ dvhat */
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                dSt[i * dv + j] = dS[i * dv + j] + kt[i] * vhat[j];
+                acc += at[i] * sp[i * dv + j] * vhat[j];
+            }
+            gk[t * dk + i] += acc;
+        }
+        /* forget */
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j)
+                acc += dSt[i * dv + j] * sp[i * dv + j];
+            ga[t * dk + i] = acc;
+            for (int j = 0; j < dv; ++j)
+                dS[i * dv + j] = at[i] * dSt[i * dv + j];
+        }
+    }
+    memcpy(J->gs0 + u * dd, dS, sizeof(double) * dd);
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job_t *J = (bwd_job_t *)arg;
+    const long dd = (long)J->dk * J->dv;
+    bwd_scratch_t W;
+    W.sprev = (double *)malloc(sizeof(double) * (J->T > 0 ? J->T : 1) * dd);
+    W.resid = (double *)malloc(sizeof(double) * (J->T > 0 ? J->T : 1) * J->dv);
+    W.S = (double *)malloc(sizeof(double) * dd);
+    W.dS = (double *)malloc(sizeof(double) * dd);
+    W.dSt = (double *)malloc(sizeof(double) * dd);
+    W.vhat = (double *)malloc(sizeof(double) * J->dv);
+    W.de = (double *)malloc(sizeof(double) * J->dv);
+    void *ret = NULL;
+    if (!W.sprev || !W.resid || !W.S || !W.dS || !W.dSt || !W.vhat || !W.de) {
+        ret = (void *)1;
+    } else {
+        for (;;) {
+            pthread_mutex_lock(&J->lock);
+            long u = J->next_unit++;
+            pthread_mutex_unlock(&J->lock);
+            if (u >= J->n_units)
+                break;
+            bwd_unit(J, u, &W);
+        }
+    }
+    free(W.sprev); free(W.resid); free(W.S); free(W.dS); free(W.dSt);
+    free(W.vhat); free(W.de);
+    return ret;
+}
+
+/*
+ * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure.
+ * n_threads <= 0 means one thread per online CPU.
+ */
+int kda_oracle_backward(const double *q, const double *k, const double *v,
+                        const double *alpha, const double *beta, const double *s0,
+                        const double *dout, const double *dsT,
+                        double *gq, double *gk, double *gv, double *ga, double *gb,
+                        double *gs0, long n_units, long T, int dk, int dv,
+                        double scale, int n_threads)
+{
+    if (n_units < 0 || T < 0 || dk <= 0 || dv <= 0 || !gs0)
+        return -1;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !dout || !gq || !gk || !gv ||
+                  !ga || !gb))
+        return -1;
+    if (n_units == 0)
+        return 0;
+
+    bwd_job_t J;
+    J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.s0 = s0;
+    J.dout = dout; J.dsT = dsT;
+    J.gq = gq; J.gk = gk; J.gv = gv; J.ga = ga; J.gb = gb; J.gs0 = gs0;
+    J.n_units = n_units; J.T = T; J.dk = dk; J.dv = dv; J.scale = scale;
+    J.next_unit = 0;
+    pthread_mutex_init(&J.lock, NULL);
+    if (n_threads <= 0) {
+        long nc = sysconf(_SC_NPROCESSORS_ONLN);
+        n_threads = nc > 0 ? (int)nc : 1;
+    }
+    if (n_threads > n_units)
+        n_threads = (int)n_units;
+    int rc = 0;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * n_threads);
+    if (!tid) {
+        pthread_mutex_destroy(&J.lock);
+        return -2;
+    }
+    int started = 0;
+    for (int i = 0; i < n_threads; ++i) {
+        if (pthread_create(&tid[i], NULL, bwd_worker, &J) != 0)
+            break;
+        ++started;
+    }
+    if (started == 0 && bwd_worker(&J) != NULL)
+        rc = -2;
+    for (int i = 0; i < started; ++i) {
+        void *ret = NULL;
+        pthread_join(tid[i], &ret);
+        if (ret != NULL)
+            rc = -2;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J.lock);
+    return rc;
+}

@@ -329,6 +329,9 @@ def test_backward_workspace_size(lib):
     (dict(dk=fake(8, 1024)), INVALID),         # two gradients overlapping
     (dict(ws=fake(12, 256)), INVALID),         # workspace inside dbeta
     (dict(cu_dev=fake(15)), INVALID),          # cu_seqlens without num_seqs
+    (dict(v=fake(2, 2)), MISALIGNED),          # v and dout: runs of four elements
+    (dict(do=fake(6, 4)), MISALIGNED),
+    (dict(dt=0, v=fake(2, 8)), MISALIGNED),    # 16 bytes for float32
 ])
 def test_backward_rejects_before_any_hip_call(lib, kw, code):
     assert bwd_call(lib, **kw) == code

@@ -93,5 +93,69 @@ def test_backward_varlen(kda):
 
 
 def test_backward_longer(kda):
-    """512 tokens (32 checkpoint blocks), two heads, d128."""
+    """512 tokens, two heads, d128."""
     check(kda, grads_inputs("bf16", 1, 512, 2, 128, 128, 0.02, True, seed=795))
+
+
+def test_backward_varlen_more_heads(kda):
+    """Eight heads, lengths that are not multiples of 8 or 64 (and an empty
+    sequence), dk = 128, dv = 64."""
+    lens = [77, 3, 0, 130, 9, 200]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    d = grads_inputs("bf16", 1, cu[-1], 8, 128, 64, 0.1, True, seed=797, num_states=len(lens))
+    d["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=dev())
+    check(kda, d, cu=cu)
+
+
+def test_backward_no_tokens(kda):
+    """Units but no tokens (T = 0 dense, and varlen with every sequence empty):
+    the initial-state gradient is the final-state gradient."""
+    d = grads_inputs("bf16", 2, 0, 3, 128, 128, 0.1, True, seed=798)
+    got = kda.kda_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
+                           d["dout"], d["dsT"])
+    torch.cuda.synchronize()
+    assert torch.equal(got[5], d["dsT"])
+    cu = [0, 0, 0]
+    d = grads_inputs("bf16", 1, 0, 3, 64, 64, 0.1, True, seed=799, num_states=2)
+    got = kda.kda_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
+                           d["dout"], d["dsT"], cu_seqlens_host=cu)
+    torch.cuda.synchronize()
+    assert torch.equal(got[5], d["dsT"])
+
+
+def test_backward_full_B4_H16_T4096(kda):
+    """The benchmarked backward call (bf16 B4 H16 T4096 d128, S0 ~ N(0, 0.02),
+    random dL/do and dL/dS_T): every (batch, head) unit compared with the
+    oracle, four heads (16 units) at a time."""
+    from workloads import CONFIGS
+    cfg = CONFIGS[1]
+    d = gen.chunk_inputs(cfg, device=dev())
+    B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
+    g = torch.Generator(device=dev())
+    g.manual_seed(11)
+    dout = torch.randn((B, T, H, dv), generator=g, device=dev(), dtype=torch.float64).to(
+        torch.bfloat16)
+    dsT = torch.randn((B, H, dk, dv), generator=g, device=dev(), dtype=torch.float64).float()
+    got = kda.kda_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
+                           dout, dsT)
+    torch.cuda.synchronize()
+    got = [x.double().cpu().numpy() for x in got]
+    for x in got:
+        assert not np.isnan(x).any(), "NaN in GPU output"
+    num = [0.0] * 6
+    den = [0.0] * 6
+    for h0 in range(0, H, 4):
+        heads = list(range(h0, h0 + 4))
+        ref = oracle.backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"],
+                              dout, dsT, heads=heads)
+        for i in range(6):
+            gx = got[i][:, heads] if i == 5 else got[i][:, :, heads]
+            num[i] = max(num[i], float(np.max(np.abs(gx - ref[i]))))
+            den[i] = max(den[i], float(np.max(np.abs(ref[i]))))
+    errs = {n: num[i] / den[i] for i, n in enumerate(NAMES)}
+    print("B4 H16 T4096 backward, all units:", {n: "%.1e" % e for n, e in errs.items()},
+          flush=True)
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)

@@ -360,11 +360,15 @@ def _fwd_kw(qn, kn, a, b, v, s0):
     return oracle.forward(qn, kn, v, a, b, s0)
 
 
+BACKWARD_IMPLS = {"c": oracle.backward_units, "numpy": oracle.backward_units_numpy}
+
+
+@pytest.mark.parametrize("impl", sorted(BACKWARD_IMPLS))
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_backward_matches_finite_differences(seed):
-    """oracle.backward_units against central differences of the oracle's own
-    forward (the C token loop, a separate implementation): L = <W, o> + <V,
-    S_T> with random weights, every input perturbed in turn."""
+def test_backward_matches_finite_differences(impl, seed):
+    """Both backward implementations against central differences of the
+    oracle's own forward (the C token loop, a separate implementation): L =
+    <W, o> + <V, S_T> with random weights, every input perturbed in turn."""
     rng = np.random.default_rng(40 + seed)
     T, dk, dv = 5, 3, 2
     q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
@@ -377,8 +381,8 @@ def test_backward_matches_finite_differences(seed):
     def loss(x):
         o, s = oracle_impl(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["s0"], scale)
         return float(np.sum(W * o) + np.sum(V * s))
-    grads = oracle.backward_units(q[None], k[None], v[None], alpha[None], beta[None], s0[None],
-                                  W[None], V[None], scale=scale)
+    grads = BACKWARD_IMPLS[impl](q[None], k[None], v[None], alpha[None], beta[None], s0[None],
+                                 W[None], V[None], scale=scale)
     names = ["q", "k", "v", "alpha", "beta", "s0"]
     h = 1e-6
     for name, g in zip(names, grads):
@@ -393,7 +397,8 @@ def test_backward_matches_finite_differences(seed):
         assert rel(g[0], fd) < 1e-7, (name, rel(g[0], fd))
 
 
-def test_backward_special_cases():
+@pytest.mark.parametrize("impl", sorted(BACKWARD_IMPLS))
+def test_backward_special_cases(impl):
     """beta = 0 and alpha = 1: nothing is written or forgotten, S_t = S0 for
     every t, so dq_t = scale S0 do_t, dS0 = dS_T + scale sum_t q_t do_t^T,
     dalpha_t = rows of (dS_t (.) S0) and dk = dv = 0 (closed forms)."""
@@ -405,8 +410,8 @@ def test_backward_special_cases():
     s0 = rng.standard_normal((U, dk, dv))
     do = rng.standard_normal((U, T, dv))
     dsT = rng.standard_normal((U, dk, dv))
-    g = oracle.backward_units(q, k, v, np.ones((U, T, dk)), np.zeros((U, T)), s0, do, dsT,
-                              scale=0.5)
+    g = BACKWARD_IMPLS[impl](q, k, v, np.ones((U, T, dk)), np.zeros((U, T)), s0, do, dsT,
+                             scale=0.5)
     assert np.allclose(g[0], 0.5 * np.einsum("uij,utj->uti", s0, do), atol=1e-13)
     assert np.allclose(g[5], dsT + 0.5 * np.einsum("uti,utj->uij", q, do), atol=1e-12)
     assert np.abs(g[1]).max() == 0.0 and np.abs(g[2]).max() == 0.0
@@ -414,3 +419,99 @@ def test_backward_special_cases():
     for t in range(T):
         dS_t = dsT + 0.5 * np.einsum("uri,urj->uij", q[:, t:], do[:, t:])
         assert np.allclose(g[3][:, t], np.sum(dS_t * s0, axis=-1), atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_backward_c_and_numpy_agree(seed):
+    """The C and NumPy backward implementations (written separately, each pinned
+    by finite differences above) agree on larger random units, with and without
+    an initial state and a final-state gradient, for dk != dv and for T = 0, 1."""
+    rng = np.random.default_rng(60 + seed)
+    for U, T, dk, dv, with_s0, with_dsT in [(3, 40, 8, 5, True, True), (2, 17, 4, 9, False, True),
+                                            (2, 23, 6, 6, True, False), (1, 1, 5, 3, True, True),
+                                            (2, 0, 4, 4, True, True)]:
+        q = rng.standard_normal((U, T, dk))
+        k = unit(rng.standard_normal((U, T, dk))) if T else np.zeros((U, 0, dk))
+        v = rng.standard_normal((U, T, dv))
+        a = rng.uniform(0.5, 1.0, (U, T, dk))
+        b = rng.uniform(0.0, 1.0, (U, T))
+        s0 = rng.standard_normal((U, dk, dv)) if with_s0 else None
+        do = rng.standard_normal((U, T, dv))
+        dsT = rng.standard_normal((U, dk, dv)) if with_dsT else None
+        gc = oracle.backward_units(q, k, v, a, b, s0, do, dsT, scale=0.7, threads=2)
+        gn = oracle.backward_units_numpy(q, k, v, a, b, s0, do, dsT, scale=0.7)
+        for x, y in zip(gc, gn):
+            assert x.shape == y.shape
+            assert np.max(np.abs(x - y), initial=0.0) <= 1e-12 * max(1.0, np.max(np.abs(y), initial=0.0))
+        if T == 0:  # nothing happens: dS0 = dS_T
+            assert np.array_equal(gc[5], dsT)
+
+
+def test_backward_layouts_and_varlen_match_units():
+    """oracle.backward in the [B, T, H, d] layout, the varlen split (with empty and
+    one-token sequences) and a head sample are re-arrangements of backward_units on
+    independent units: each unit is compared with its own call."""
+    rng = np.random.default_rng(70)
+    B, T, H, dk, dv = 2, 9, 3, 4, 5
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    a = rng.uniform(0.3, 1.0, (B, T, H, dk))
+    b = rng.uniform(0.0, 1.0, (B, T, H))
+    s0 = rng.standard_normal((B, H, dk, dv))
+    do = rng.standard_normal((B, T, H, dv))
+    dsT = rng.standard_normal((B, H, dk, dv))
+    g = oracle.backward(q, k, v, a, b, s0, do, dsT, scale=0.6)
+    for bb in range(B):
+        for h in range(H):
+            gu = oracle.backward_units_numpy(q[bb, :, h][None], k[bb, :, h][None],
+                                             v[bb, :, h][None], a[bb, :, h][None],
+                                             b[bb, :, h][None], s0[bb, h][None],
+                                             do[bb, :, h][None], dsT[bb, h][None], scale=0.6)
+            for i in range(5):
+                assert rel(g[i][bb, :, h], gu[i][0]) < 1e-13, (bb, h, i)
+            assert rel(g[5][bb, h], gu[5][0]) < 1e-13
+    # varlen: lengths 0, 4, 1, 0, 13 over the packed tokens of both batch rows
+    lens = [0, 4, 1, 0, 13]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    pk = lambda x: x.reshape((1, B * T) + x.shape[2:])
+    s0v = rng.standard_normal((len(lens), H, dk, dv))
+    dsv = rng.standard_normal((len(lens), H, dk, dv))
+    gv = oracle.backward(pk(q), pk(k), pk(v), pk(a), pk(b), s0v, pk(do), dsv, cu_seqlens=cu,
+                         scale=0.6)
+    for n, L in enumerate(lens):
+        t0 = cu[n]
+        for h in range(H):
+            sl = lambda x: x[0, t0:t0 + L, h][None]
+            gu = oracle.backward_units_numpy(sl(pk(q)), sl(pk(k)), sl(pk(v)), sl(pk(a)),
+                                             sl(pk(b)), s0v[n, h][None], sl(pk(do)),
+                                             dsv[n, h][None], scale=0.6)
+            for i in range(5):
+                got = gv[i][0, t0:t0 + L, h]
+                assert got.shape == gu[i][0].shape
+                if L:
+                    assert rel(got, gu[i][0]) < 1e-13, (n, h, i)
+            assert rel(gv[5][n, h], gu[5][0]) < 1e-13
+            if L == 0:  # an empty sequence passes the state gradient through
+                assert np.array_equal(gv[5][n, h], dsv[n, h])
+    # head sample
+    gh = oracle.backward(q, k, v, a, b, s0, do, dsT, scale=0.6, heads=[2, 0])
+    for i in range(5):
+        assert np.array_equal(gh[i], g[i][:, :, [2, 0]])
+    assert np.array_equal(gh[5], g[5][:, [2, 0]])
+
+
+def test_step_in_place_matches_copy():
+    """oracle.step with in_place rewrites the given float64 state and returns the
+    same values as the copying call."""
+    rng = np.random.default_rng(80)
+    N, H, dk, dv = 3, 2, 4, 5
+    q, k = rng.standard_normal((N, H, dk)), rng.standard_normal((N, H, dk))
+    v = rng.standard_normal((N, H, dv))
+    a, b = rng.uniform(0.3, 1.0, (N, H, dk)), rng.uniform(0.0, 1.0, (N, H))
+    s = rng.standard_normal((N, H, dk, dv))
+    o1, s1 = oracle.step(q, k, v, a, b, s)
+    s2 = s.copy()
+    o2, s3 = oracle.step(q, k, v, a, b, s2, in_place=True)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s3) and np.array_equal(s2, s1)
+    assert not np.array_equal(s, s1)  # the copying call left its input alone
