@@ -11,7 +11,7 @@ HIP events on the launch stream over its own loop of K launches:
   decode        100 consecutive in-place decode steps, N256 H32 d128
   backward      gradients of the headline forward
 For the headline and the decode step it also reports the time of single
-launches that each follow a 1 GiB write (the 256 MB last-level cache then
+launches that each follow a 1 GiB read (the 256 MB last-level cache then
 holds none of the launch's inputs): the HBM-cold figure beside the
 back-to-back one.
 
@@ -231,13 +231,15 @@ def main():
     flush_buf = [None]
 
     def flushed(fn, n):
-        """Median and min ms of n single calls, each after a 1 GiB write (a
-        fill kernel) that leaves none of the call's inputs in the caches."""
+        """Median and min ms of n single calls, each after a 1 GiB read (a sum
+        over a buffer) that leaves none of the call's inputs in the caches and
+        only clean lines behind (a write there would leave dirty lines whose
+        write-back then competes with the call)."""
         if flush_buf[0] is None:
-            flush_buf[0] = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            flush_buf[0] = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         ts = []
         for _ in range(n):
-            flush_buf[0].fill_(1.0)
+            flush_buf[0].sum()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)

@@ -5,7 +5,8 @@ TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 library never calls it, and the two share no code.
 
 The arithmetic lives in ``kda_oracle.c`` (plain C, double precision, a token
-loop: forget, predict, correct and write, read).  This module only converts
+loop: forget, predict, correct and write, read; for Gated DeltaNet-2 forget,
+predict, erase, write, read; and the chain rule of the KDA loop in reverse).  This module only converts
 inputs to contiguous float64 arrays, reorders the [B, T, H, d] token layout
 into per-unit blocks, and calls the C library through ctypes.
 
@@ -52,6 +53,10 @@ def _load():
         lib.kda_oracle_step.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                         ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_double, ctypes.c_int]
+        lib.gdn2_oracle_forward.restype = ctypes.c_int
+        lib.gdn2_oracle_forward.argtypes = [dp] * 9 + [ctypes.c_long, ctypes.c_long,
+                                                       ctypes.c_int, ctypes.c_int,
+                                                       ctypes.c_double, ctypes.c_int]
         lib.kda_oracle_backward.restype = ctypes.c_int
         lib.kda_oracle_backward.argtypes = [dp] * 14 + [ctypes.c_long, ctypes.c_long,
                                                         ctypes.c_int, ctypes.c_int,
@@ -187,6 +192,82 @@ def forward(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, scale=Non
         o_all[b, t0:t0 + L] = np.moveaxis(o_u, 0, 1)
         s_all[n] = s_u
     return o_all, s_all
+
+
+def gdn2_forward_units(q, k, v, alpha, erase, write, initial_state=None, scale=None,
+                       threads=0):
+    """Gated DeltaNet-2 token loop over independent units (``run_unit_gdn2`` in
+    ``kda_oracle.c``): forget with alpha, predict, erase along e . k, write
+    along w . k, read ("线性注意力机制：从标准注意力到 Gated DeltaNet-2",
+    jindou-blog, section 4, with the reading stated in the C source).
+
+    q, k, alpha, erase, write: [U, T, dk]; v: [U, T, dv]; initial_state
+    [U, dk, dv] or None.  Returns (o [U, T, dv], final_state [U, dk, dv])."""
+    q, k, v, alpha, erase, write = (_f64(x) for x in (q, k, v, alpha, erase, write))
+    s0 = _f64(initial_state)
+    U, T, dk = q.shape
+    dv = v.shape[2]
+    for x in (k, alpha, erase, write):
+        assert x.shape == (U, T, dk)
+    assert v.shape == (U, T, dv)
+    if s0 is not None:
+        assert s0.shape == (U, dk, dv)
+    if scale is None:
+        scale = dk ** -0.5
+    o = np.zeros((U, T, dv), np.float64)
+    sT = np.zeros((U, dk, dv), np.float64)
+    rc = _load().gdn2_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+                                     _ptr(write), _ptr(s0), _ptr(o), _ptr(sT), U, T, dk, dv,
+                                     float(scale), int(threads))
+    if rc != 0:
+        raise RuntimeError("gdn2_oracle_forward failed with %d" % rc)
+    return o, sT
+
+
+def gdn2_forward(q, k, v, alpha, erase, write, initial_state=None, cu_seqlens=None,
+                 scale=None, threads=0, heads=None):
+    """gdn2_forward_units in the library's token layout: q, k, alpha, erase,
+    write [B, T, H, dk] (alpha None: no forget gate, alpha = 1); v [B, T, H, dv];
+    initial_state [B or N, H, dk, dv] or None; cu_seqlens and heads as for
+    ``forward``.  Returns (o [B, T, Hs, dv], final_state [B or N, Hs, dk, dv])."""
+    q, k, v, erase, write = (_f64(x) for x in (q, k, v, erase, write))
+    alpha = np.ones_like(k) if alpha is None else _f64(alpha)
+    s0 = _f64(initial_state)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    hs = list(range(H)) if heads is None else list(heads)
+    sel = np.asarray(hs, dtype=np.int64)
+    if cu_seqlens is None:
+        starts = [(b, 0, T) for b in range(B)]
+    else:
+        assert B == 1
+        cu = [int(c) for c in cu_seqlens]
+        starts = [(0, cu[n], cu[n + 1] - cu[n]) for n in range(len(cu) - 1)]
+    o_all = np.zeros((B, T, len(hs), dv), np.float64)
+    s_all = np.zeros((len(starts), len(hs), dk, dv), np.float64)
+    for n, (b, t0, L) in enumerate(starts):
+        def units(x):  # [L, Hs, d] -> [Hs, L, d]
+            return np.ascontiguousarray(np.moveaxis(x[b, t0:t0 + L][:, sel], 1, 0))
+        init = None if s0 is None else s0[n][sel]
+        o_u, s_u = gdn2_forward_units(units(q), units(k), units(v), units(alpha), units(erase),
+                                      units(write), init, scale=scale, threads=threads)
+        o_all[b, t0:t0 + L] = np.moveaxis(o_u, 0, 1)
+        s_all[n] = s_u
+    return o_all, s_all
+
+
+def gdn2_step(q, k, v, alpha, erase, write, state, scale=None, threads=0):
+    """One Gated DeltaNet-2 decode step: q, k, alpha, erase, write [N, H, dk]
+    (alpha None: no forget gate); v [N, H, dv]; state [N, H, dk, dv].  Returns
+    (o [N, H, dv], new_state), float64; the input state is not modified."""
+    q, k, v, erase, write = (_f64(x) for x in (q, k, v, erase, write))
+    alpha = np.ones_like(k) if alpha is None else _f64(alpha)
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    unit = lambda x: x.reshape(N * H, 1, x.shape[-1])
+    o, s = gdn2_forward_units(unit(q), unit(k), unit(v), unit(alpha), unit(erase), unit(write),
+                              _f64(state).reshape(N * H, dk, dv), scale=scale, threads=threads)
+    return o.reshape(N, H, dv), s.reshape(N, H, dk, dv)
 
 
 def backward_units(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, scale=None,

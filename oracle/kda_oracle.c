@@ -46,6 +46,7 @@
 
 typedef struct {
     const double *q, *k, *v, *alpha, *beta, *s0;
+    const double *erase, *write;  /* Gated DeltaNet-2 gates, or NULL for KDA */
     double *o, *sT;
     long n_units, T;
     int dk, dv;
@@ -109,6 +110,76 @@ static void run_unit(const job_t *J, long u, double *S, double *vhat)
         memcpy(J->sT + u * (long)dk * dv, S, sizeof(double) * dk * dv);
 }
 
+/*
+ * Gated DeltaNet-2, one unit, token by token ("线性注意力机制：从标准注意力到
+ * Gated DeltaNet-2", jindou-blog, section 4 "Gated DeltaNet-2：解耦擦除与写入",
+ * and its table of erase/write control).  The page splits the one scalar gate
+ * of the delta rule, which scales both the removal of the old association and
+ * the writing of the new one, into an erase gate e_t and a write gate w_t,
+ * each a vector over the d channels.  Its printed update is garbled; the
+ * reading taken here keeps KDA's steps (so that KDA, Gated DeltaNet and
+ * linear attention are special cases, as the page's table claims) and gates
+ * the two halves of the write per key channel (row i of S):
+ *
+ *   1. forget   S <- Diag(alpha_t) S
+ *   2. predict  vhat = S^T k_t
+ *   3. erase    S <- S - (e_t . k_t) vhat^T      ((e_t . k_t)_i = e_t[i] k_t[i])
+ *   4. write    S <- S + (w_t . k_t) v_t^T
+ *   5. read     o_t = scale * S^T q_t
+ *
+ * With e_t = w_t = beta_t 1 this is the KDA token step above; with e_t = 0 it
+ * is a gated linear attention with a per-channel write gate.
+ */
+static void run_unit_gdn2(const job_t *J, long u, double *S, double *vhat)
+{
+    const int dk = J->dk, dv = J->dv;
+    const long T = J->T;
+    const double *q = J->q + u * T * dk;
+    const double *k = J->k + u * T * dk;
+    const double *a = J->alpha + u * T * dk;
+    const double *er = J->erase + u * T * dk;
+    const double *wr = J->write + u * T * dk;
+    const double *v = J->v + u * T * dv;
+    double *o = J->o ? J->o + u * T * dv : NULL;
+
+    if (J->s0)
+        memcpy(S, J->s0 + u * (long)dk * dv, sizeof(double) * dk * dv);
+    else
+        memset(S, 0, sizeof(double) * dk * dv);
+
+    for (long t = 0; t < T; ++t) {
+        const double *at = a + t * dk, *kt = k + t * dk, *qt = q + t * dk;
+        const double *et = er + t * dk, *wt = wr + t * dk;
+        const double *vt = v + t * dv;
+        /* 1. forget */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[i * dv + j] *= at[i];
+        /* 2. predict */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += S[i * dv + j] * kt[i];
+            vhat[j] = acc;
+        }
+        /* 3. erase and 4. write */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[i * dv + j] += -et[i] * kt[i] * vhat[j] + wt[i] * kt[i] * vt[j];
+        /* 5. read */
+        if (o) {
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    acc += S[i * dv + j] * qt[i];
+                o[t * dv + j] = J->scale * acc;
+            }
+        }
+    }
+    if (J->sT)
+        memcpy(J->sT + u * (long)dk * dv, S, sizeof(double) * dk * dv);
+}
+
 static void *worker(void *arg)
 {
     job_t *J = (job_t *)arg;
@@ -125,12 +196,17 @@ static void *worker(void *arg)
         pthread_mutex_unlock(&J->lock);
         if (u >= J->n_units)
             break;
-        run_unit(J, u, S, vhat);
+        if (J->erase)
+            run_unit_gdn2(J, u, S, vhat);
+        else
+            run_unit(J, u, S, vhat);
     }
     free(S);
     free(vhat);
     return NULL;
 }
+
+static int run_job(job_t *Jp, int n_threads);
 
 /*
  * Forward over n_units independent units of T tokens each.
@@ -153,17 +229,25 @@ int kda_oracle_forward(const double *q, const double *k, const double *v,
 
     job_t J;
     J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.s0 = s0;
+    J.erase = NULL; J.write = NULL;
     J.o = o; J.sT = sT;
     J.n_units = n_units; J.T = T; J.dk = dk; J.dv = dv; J.scale = scale;
     J.next_unit = 0;
+    return run_job(&J, n_threads);
+}
+
+/* Runs J's units on n_threads threads (<= 0: one per online CPU). */
+static int run_job(job_t *Jp, int n_threads)
+{
+    job_t J = *Jp;
     pthread_mutex_init(&J.lock, NULL);
 
     if (n_threads <= 0) {
         long nc = sysconf(_SC_NPROCESSORS_ONLN);
         n_threads = nc > 0 ? (int)nc : 1;
     }
-    if (n_threads > n_units)
-        n_threads = (int)n_units;
+    if (n_threads > J.n_units)
+        n_threads = (int)J.n_units;
 
     int rc = 0;
     pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * n_threads);
@@ -443,3 +527,29 @@ int kda_oracle_backward(const double *q, const double *k, const double *v,
     pthread_mutex_destroy(&J.lock);
     return rc;
 }
+
+/*
+ * Gated DeltaNet-2 forward (run_unit_gdn2) over n_units units: layouts as for
+ * kda_oracle_forward with erase and write [n_units][T][dk] in place of beta.
+ */
+int gdn2_oracle_forward(const double *q, const double *k, const double *v,
+                        const double *alpha, const double *erase, const double *write,
+                        const double *s0, double *o, double *sT, long n_units, long T,
+                        int dk, int dv, double scale, int n_threads)
+{
+    if (n_units < 0 || T < 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (T > 0 && (!q || !k || !v || !alpha || !erase || !write))
+        return -1;
+    if (n_units == 0)
+        return 0;
+    job_t J;
+    J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = NULL; J.s0 = s0;
+    J.erase = erase ? erase : q;  /* T == 0: any non-NULL marks the mode */
+    J.write = write;
+    J.o = o; J.sT = sT;
+    J.n_units = n_units; J.T = T; J.dk = dk; J.dv = dv; J.scale = scale;
+    J.next_unit = 0;
+    return run_job(&J, n_threads);
+}
+
