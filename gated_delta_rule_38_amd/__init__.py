@@ -13,7 +13,8 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused", "kda_recurrent_step",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused",
+           "kda_chunk_fwd_noalloc", "KDA_NOALLOC_MAX_SEQS", "kda_recurrent_step",
            "kda_recurrent_step_gated", "kda_recurrent_step_fused", "kda_backward",
            "kda_backward_workspace_size", "kda_chunk_fwd_workspace_size",
            "kda_status_string", "kda_version", "KDAError", "LIB_PATH", "load_library"]
@@ -32,6 +33,8 @@ _GATES = {"channel": KDA_GATE_CHANNEL, "head": KDA_GATE_HEAD, "none": KDA_GATE_N
 KDA_FUSE_GATE_LOGITS = 1
 KDA_FUSE_BETA_LOGITS = 2
 KDA_FUSE_QK_L2NORM = 4
+# packed sequences kda_chunk_fwd_noalloc accepts (its fixed device scratch)
+KDA_NOALLOC_MAX_SEQS = 65536
 _STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
            3: "KDA_ERROR_MISALIGNED", 4: "KDA_ERROR_INSUFFICIENT_WORKSPACE", 5: "KDA_ERROR_HIP"}
 
@@ -61,6 +64,9 @@ def load_library():
         lib.kda_chunk_fwd_gated.restype = i
         lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, i,
                                             vp, ip, i, f, i, vp, sz, vp]
+        lib.kda_chunk_fwd_noalloc.restype = i
+        lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
+                                              vp, ip, i, f, i, vp]
         lib.kda_recurrent_step.restype = i
         lib.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, vp]
         lib.kda_recurrent_step_gated.restype = i
@@ -271,6 +277,49 @@ def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd_fused" if flags is not None else
                        "kda_chunk_fwd" if gate is None else "kda_chunk_fwd_gated")
+    return o, final_state
+
+
+def kda_chunk_fwd_noalloc(q, k, v, alpha, beta, initial_state, o, final_state=None,
+                          cu_seqlens=None, cu_seqlens_host=None, scale=None, chunk_size=64):
+    """kda_chunk_fwd through the entry point that allocates nothing: the caller
+    passes every output (o, and final_state unless the state is not wanted)
+    and, for packed sequences, both the int32 device tensor cu_seqlens and its
+    host copy.  Nothing is allocated on the device, here or in the library.
+    Returns (o, final_state)."""
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(q, "q", dt, dev)
+    _check(k, "k", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    _check(alpha, "alpha", torch.float32, dev, (B, T, H, dk))
+    _check(beta, "beta", torch.float32, dev, (B, T, H))
+    _check(o, "o", dt, dev, (B, T, H, dv))
+    num_seqs, cu_host_arr = 0, None
+    if (cu_seqlens is None) != (cu_seqlens_host is None):
+        raise ValueError("packed sequences need both cu_seqlens and cu_seqlens_host")
+    if cu_seqlens is not None:
+        host = [int(x) for x in (cu_seqlens_host.tolist() if isinstance(cu_seqlens_host, torch.Tensor)
+                                 else cu_seqlens_host)]
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (len(host),))
+        num_seqs = len(host) - 1
+        cu_host_arr = (ctypes.c_int * len(host))(*host)
+    sshape = (num_seqs if num_seqs > 0 else B, H, dk, dv)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.float32, dev, sshape)
+    if final_state is not None:
+        _check(final_state, "final_state", torch.float32, dev, sshape)
+    st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, dk,
+                                   dv, code, _ptr(cu_seqlens), cu_host_arr, num_seqs,
+                                   float(scale) if scale is not None else 0.0, int(chunk_size),
+                                   _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_noalloc")
     return o, final_state
 
 

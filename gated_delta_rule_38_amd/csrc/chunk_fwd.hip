@@ -39,6 +39,8 @@
 // alpha reads hit the same L2.
 #include "chunk_common.h"
 
+#include <mutex>
+
 namespace kda {
 
 constexpr int NTH = 256;
@@ -685,6 +687,43 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
                            : launch_chunk_dk<bf16_t, 64>(a, dvt, order, stream);
     return a.dk == 128 ? launch_chunk_dk<float, 128>(a, dvt, order, stream)
                        : launch_chunk_dk<float, 64>(a, dvt, order, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The scratch of kda_chunk_fwd_noalloc: the longest-first order of the packed
+// sequences (written in full by order_sequences_kernel before each use, so it
+// needs no clearing) lives in this file-scope device array instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code the array's name is only
+// a host-side stand-in: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) int scratch[NOALLOC_MAX_SEQS];
+
+hipError_t noalloc_order_buffer(hipStream_t stream, int** out) {
+    constexpr int kMaxDevices = 64;
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = static_cast<int*>(addr[dev]);
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -88,7 +88,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
                           kda_dtype dtype, int gate, unsigned flags, const int* cu_seqlens_dev,
                           const int* cu_seqlens_host, int num_seqs, float scale,
                           int chunk_size, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream);
+                          hipStream_t stream, bool noalloc = false);
 kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const void* alpha,
                                const float* beta, float* state, void* o, int N, int H, int dk,
                                int dv, kda_dtype dtype, int gate, unsigned flags, float scale,
@@ -155,6 +155,18 @@ kda_status kda_chunk_fwd_fused(const void* q, const void* k, const void* v, cons
     return chunk_fwd_impl(q, k, v, gate, beta, initial_state, o, final_state, B, T, H, dk, dv,
                           dtype, (int)gate_kind, flags, cu_seqlens_dev, cu_seqlens_host,
                           num_seqs, scale, chunk_size, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta,
+                                 const float* initial_state, void* o, float* final_state, int B,
+                                 int T, int H, int dk, int dv, kda_dtype dtype,
+                                 const int* cu_seqlens_dev, const int* cu_seqlens_host,
+                                 int num_seqs, float scale, int chunk_size, hipStream_t stream) {
+    static_assert(KDA_NOALLOC_MAX_SEQS == kda::NOALLOC_MAX_SEQS, "scratch size");
+    return chunk_fwd_impl(q, k, v, alpha, beta, initial_state, o, final_state, B, T, H, dk, dv,
+                          dtype, KDA_GATE_CHANNEL, 0u, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                          scale, chunk_size, nullptr, 0, stream, true);
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
@@ -292,11 +304,13 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
                           kda_dtype dtype, int gate, unsigned flags, const int* cu_seqlens_dev,
                           const int* cu_seqlens_host, int num_seqs, float scale,
                           int chunk_size, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool noalloc) {
     try {
         if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
         if (!valid_gate(gate) || !valid_flags(gate, flags)) return KDA_ERROR_INVALID_VALUE;
         if (gate == KDA_GATE_NONE && alpha) return KDA_ERROR_INVALID_VALUE;
+        // the no-allocation variant keeps the sequence order in a fixed device array
+        if (noalloc && num_seqs > KDA_NOALLOC_MAX_SEQS) return KDA_ERROR_NOT_SUPPORTED;
         if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return KDA_ERROR_INVALID_VALUE;
         if (chunk_size != kChunk) return KDA_ERROR_NOT_SUPPORTED;
         if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
@@ -339,7 +353,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
             if (!aligned(ptr, 4)) return KDA_ERROR_MISALIGNED;
 
         const size_t need_ws =
-            kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype);
+            noalloc ? 0 : kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype);
         if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
             return KDA_ERROR_INSUFFICIENT_WORKSPACE;
 
@@ -373,6 +387,11 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
         a.cu_seqlens = varlen ? cu_seqlens_dev : nullptr;
         a.num_seqs = varlen ? num_seqs : 0;
         a.order = (varlen && num_seqs <= 65536) ? static_cast<int*>(workspace) : nullptr;
+        if (noalloc && varlen) {
+            int* order = nullptr;
+            if (kda::noalloc_order_buffer(stream, &order) != hipSuccess) return KDA_ERROR_HIP;
+            a.order = order;
+        }
         a.scale = default_scale(scale, dk);
         a.dvt = env_dvt();
         a.generic = env_generic();

@@ -44,6 +44,13 @@ struct ChunkArgs {
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
 
+// Sequences a call of kda_chunk_fwd_noalloc may pack: the size of the device
+// array that holds their order in place of a caller workspace.
+constexpr int NOALLOC_MAX_SEQS = 65536;
+// Device address of that array on the device of `stream` (looked up once per
+// device, then reused).  Every call on one device shares the array.
+hipError_t noalloc_order_buffer(hipStream_t stream, int **out);
+
 // value-column tile the planner picks for a given number of units
 int plan_chunk_dvt(int units, int dv, bool bf16);
 

@@ -186,6 +186,29 @@ kda_status kda_chunk_fwd_fused(const void *q, const void *k, const void *v, cons
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, and the same results bit for bit.
+ * It calls no hipMalloc, hipFree or allocating library routine.  The only
+ * scratch, the longest-first order of the packed sequences, lives in a
+ * fixed device array of KDA_NOALLOC_MAX_SEQS ints (256 KiB) that each GPU
+ * the library runs on holds until the process ends; the order is rewritten
+ * in full by every variable-length call, and dense calls do not use it.
+ * Errors as for kda_chunk_fwd, plus KDA_ERROR_NOT_SUPPORTED for
+ * num_seqs > KDA_NOALLOC_MAX_SEQS (nothing is launched).  Every call on one
+ * GPU shares that array: variable-length calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race on it and must
+ * be ordered by the caller.
+ */
+#define KDA_NOALLOC_MAX_SEQS 65536
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *beta,
+                                 const float *initial_state, void *o, float *final_state, int B,
+                                 int T, int H, int dk, int dv, kda_dtype dtype,
+                                 const int *cu_seqlens_dev, const int *cu_seqlens_host,
+                                 int num_seqs, float scale, int chunk_size, hipStream_t stream);
+
+/*
  * One decode step, state updated in place.
  * Source: the fused recurrent mode of bugfactory.tech news 3610, fifth
  * paragraph (the sequence is processed token by token, state tiles updated

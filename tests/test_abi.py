@@ -146,6 +146,31 @@ def test_chunk_varlen_validation(lib):
     assert chunk_call(lib, **dict(good, ws=fake(9, 2))) == MISALIGNED
 
 
+def test_noalloc_validation(lib):
+    """kda_chunk_fwd_noalloc validates like kda_chunk_fwd (no workspace) and
+    rejects more packed sequences than its fixed scratch holds."""
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), beta=fake(4), s0=fake(5), o=fake(6),
+             sT=fake(7), B=2, T=100, H=4, dk=128, dv=128, dt=1, cu_dev=None, cu_host=None,
+             num_seqs=0, scale=0.0, chunk=64, stream=None)
+
+    def call(**kw):
+        x = dict(a, **kw)
+        return lib.kda_chunk_fwd_noalloc(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["s0"],
+                                         x["o"], x["sT"], x["B"], x["T"], x["H"], x["dk"],
+                                         x["dv"], x["dt"], x["cu_dev"], x["cu_host"],
+                                         x["num_seqs"], x["scale"], x["chunk"], x["stream"])
+    n = 65537
+    assert call(B=1, T=0, num_seqs=n, cu_dev=fake(8), cu_host=host_cu([0] * (n + 1))) == \
+        NOT_SUPPORTED
+    assert call(dk=96) == NOT_SUPPORTED
+    assert call(q=None) == INVALID
+    assert call(o=fake(0, 64)) == INVALID
+    assert call(k=fake(1, 4)) == MISALIGNED
+    cu = host_cu([0, 10, 5, 40])
+    assert call(B=1, T=40, num_seqs=3, cu_dev=fake(8), cu_host=cu) == INVALID
+    assert call(B=0) == SUCCESS
+
+
 def test_workspace_size(lib):
     assert lib.kda_chunk_fwd_workspace_size(2, 100, 4, 128, 128, 0, 1) == 0
     assert lib.kda_chunk_fwd_workspace_size(1, 100, 4, 128, 128, 64, 1) == 256
