@@ -95,14 +95,15 @@ GATE_WIDTH = {"channel": lambda dk: dk, "head": lambda dk: 1, "none": lambda dk:
 GATE_NAME = {"channel": "KDA", "head": "Gated DeltaNet", "none": "DeltaNet"}
 
 
-def chunk_bytes(tokens, H, dk, dv, nstates, es=2, gate="channel", ges=4):
+def chunk_bytes(tokens, H, dk, dv, nstates, es=2, gate="channel", ges=4, initial=True):
     """Algorithmic HBM bytes of one chunk-wise forward over `tokens` packed
     tokens: every input read once, every output written once (ges: bytes per
-    gate element, 4 for float32 alpha, es for logits in the storage dtype)."""
+    gate element, 4 for float32 alpha, es for logits in the storage dtype;
+    initial: whether an initial state is read)."""
     tok = tokens * H
     aw = GATE_WIDTH[gate](dk)
     return (tok * (2 * dk * es + dv * es + aw * ges + 4 + dv * es)  # q, k, v, alpha, beta, o
-            + 2 * nstates * H * dk * dv * 4)                         # initial + final state
+            + (2 if initial else 1) * nstates * H * dk * dv * 4)     # initial + final state
 
 
 def chunk_flops(tokens, H, dk, dv, C=CHUNK):
@@ -353,7 +354,9 @@ def main():
                 "kda_chunk_fwd bf16 varlen: 64 packed sequences, lengths U{128..8192} "
                 "(%d tokens), H16 dk128 dv128, initial states N(0,0.02)" % toks)
         out[name] = {"workload": desc, "ms_per_step": lms, "tokens_per_s": toks / (lms / 1e3),
-                     "roofline": roofline(chunk_bytes(toks, c.H, c.dk, c.dv, nst), lms,
+                     "roofline": roofline(chunk_bytes(toks, c.H, c.dk, c.dv, nst,
+                                                      initial=dd["initial_state"] is not None),
+                                          lms,
                                           "chunk_fwd_bf16_kernel[%s]" % name,
                                           chunk_flops(toks, c.H, c.dk, c.dv))}
         del dd, ol, fl_, ws
