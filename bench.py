@@ -10,6 +10,8 @@ HIP events on the launch stream over its own loop of K launches:
   varlen        chunk forward, 64 packed sequences of 128..8192 tokens, H16
   decode        100 consecutive in-place decode steps, N256 H32 d128
   backward      gradients of the headline forward
+  gdn2          Gated DeltaNet-2 chunk forward at the headline's shapes, and its
+                decode step at the decode workload's shapes
 For the headline and the decode step it also reports the time of single
 launches that each follow a 1 GiB read (the 256 MB last-level cache then
 holds none of the launch's inputs): the HBM-cold figure beside the
@@ -55,8 +57,10 @@ KERNEL_SOURCES = {
     "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "chunk_common.h", "kda_device.h"],
     "recurrent_step_kernel": ["recurrent_step.hip", "kda_device.h"],
     "backward_kernel": ["backward.hip", "kda_device.h"],
+    "gdn2_chunk_kernel": ["gdn2_chunk.hip", "chunk_common.h", "kda_device.h"],
+    "gdn2_step_kernel": ["gdn2_step.hip", "kda_device.h"],
 }
-WORKLOADS = ["headline", "long_context", "varlen", "decode", "backward"]
+WORKLOADS = ["headline", "long_context", "varlen", "decode", "backward", "gdn2"]
 
 
 def _code_only(text):
@@ -113,6 +117,28 @@ def chunk_flops(tokens, H, dk, dv, C=CHUNK):
     solve and M U, each over half a chunk on average) + 2 C^2 / 3 (the
     triangular inverse)."""
     return tokens * H * (6 * dk * dv + C * (3 * dk + 2 * dv) + 2 * C * C / 3)
+
+
+def gdn2_chunk_bytes(tokens, H, dk, dv, nstates, es=2, initial=True):
+    """Algorithmic HBM bytes of one Gated DeltaNet-2 chunk-wise forward: q, k, v
+    and o in the storage dtype, alpha, erase and write float32 per key channel,
+    the states float32."""
+    return (tokens * H * (2 * dk * es + dv * es + 3 * dk * 4 + dv * es)
+            + (2 if initial else 1) * nstates * H * dk * dv * 4)
+
+
+def gdn2_chunk_flops(tokens, H, dk, dv, C=CHUNK):
+    """Algorithmic matrix flops of one Gated DeltaNet-2 chunk-wise forward per
+    token and head: 8 dk dv (Kr S, Qr S, and the state update over the two
+    rows each token writes) + C (4 dk + 4 dv) (four Gram products, L_c V, the
+    solve and the two-row intra-chunk product, each over half a chunk on
+    average) + 2 C^2 / 3 (the triangular inverse)."""
+    return tokens * H * (8 * dk * dv + C * (4 * dk + 4 * dv) + 2 * C * C / 3)
+
+
+def gdn2_step_bytes(N, H, dk, dv, es=2):
+    """Algorithmic HBM bytes of one Gated DeltaNet-2 decode step."""
+    return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * es + 3 * dk * 4 + dv * es)
 
 
 def decode_bytes(N, H, dk, dv, es=2, gate="channel", ges=4):
@@ -204,7 +230,7 @@ def main():
     if args.skip_decode:
         run["decode"] = False
     if not plain:  # the variants cover the headline and the decode step
-        run["long_context"] = run["varlen"] = run["backward"] = False
+        run["long_context"] = run["varlen"] = run["backward"] = run["gdn2"] = False
 
     import torch
     import gated_delta_rule_38_amd as kda
@@ -440,7 +466,48 @@ def main():
                         "roofline": out["decode"]["roofline"]})
         del ddc, state, sargs
 
-    for name in ("long_context", "varlen", "backward"):  # --only of one of these
+    if run["gdn2"]:
+        g2 = gen.draw_gdn2(B, T, H, dk, dv, "bf16", alpha_mu=4.0, s0_std=0.02, seed=1, device=dev)
+        og = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        fg = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+        def gstep():
+            kda.kda_gdn2_chunk_fwd(g2["q"], g2["k"], g2["v"], g2["alpha"], g2["erase"],
+                                   g2["write"], g2["initial_state"], o=og, final_state=fg)
+        gms = timed(gstep, args.steps, args.warmup if args.only else max(5, args.warmup // 10))
+        out["gdn2"] = {
+            "workload": "kda_gdn2_chunk_fwd (Gated DeltaNet-2: per-channel forget, erase and "
+                        "write gates) bf16 B4 H16 T4096 dk128 dv128 chunk64, initial state "
+                        "N(0,0.02)",
+            "ms_per_step": gms, "tokens_per_s": B * T / (gms / 1e3),
+            "roofline": roofline(gdn2_chunk_bytes(B * T, H, dk, dv, B), gms, "gdn2_chunk_kernel",
+                                 gdn2_chunk_flops(B * T, H, dk, dv))}
+        del g2, og, fg
+        dc = CONFIGS[3]
+        g = torch.Generator(device=dev)
+        g.manual_seed(3)
+        gst = (0.05 * torch.randn((dc.B, dc.H, dc.dk, dc.dv), generator=g, device=dev,
+                                  dtype=torch.float64)).float()
+        steps_in = gen.draw_gdn2(dc.B, 8, dc.H, dc.dk, dc.dv, "bf16", alpha_mu=4.0, seed=5,
+                                 device=dev)
+        sin = [[steps_in[n][:, t].contiguous() for n in ("q", "k", "v", "alpha", "erase",
+                                                          "write")] for t in range(8)]
+        ogd = torch.empty((dc.B, dc.H, dc.dv), dtype=torch.bfloat16, device=dev)
+        cnt = [0]
+
+        def gdstep():
+            kda.kda_gdn2_recurrent_step(*sin[cnt[0] % 8], gst, o=ogd)
+            cnt[0] += 1
+        gus = timed(gdstep, dc.steps, 3) * 1e3
+        gb = gdn2_step_bytes(dc.B, dc.H, dc.dk, dc.dv)
+        out["gdn2_decode"] = {
+            "workload": "kda_gdn2_recurrent_step bf16 N256 H32 dk128 dv128, fp32 state in place, "
+                        "100 consecutive steps (8 input sets in turn)",
+            "us_per_step": gus, "tokens_per_s": dc.B / (gus / 1e6),
+            "roofline": roofline(gb, gus / 1e3, "gdn2_step_kernel")}
+        del gst, steps_in, sin, ogd
+
+    for name in ("long_context", "varlen", "backward", "gdn2"):  # --only of one of these
         if "value" not in out and name in out:
             rec = out[name]
             out.update({"metric": "KDA %s tokens/s vs roofline" % name, "value":

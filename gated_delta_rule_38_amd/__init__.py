@@ -14,7 +14,8 @@ import os
 import torch
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused",
-           "kda_chunk_fwd_noalloc", "KDA_NOALLOC_MAX_SEQS", "kda_recurrent_step",
+           "kda_chunk_fwd_noalloc", "KDA_NOALLOC_MAX_SEQS", "kda_gdn2_chunk_fwd",
+           "kda_gdn2_recurrent_step", "kda_recurrent_step",
            "kda_recurrent_step_gated", "kda_recurrent_step_fused", "kda_backward",
            "kda_backward_workspace_size", "kda_chunk_fwd_workspace_size",
            "kda_status_string", "kda_version", "KDAError", "LIB_PATH", "load_library"]
@@ -67,6 +68,12 @@ def load_library():
         lib.kda_chunk_fwd_noalloc.restype = i
         lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
                                               vp, ip, i, f, i, vp]
+        lib.kda_gdn2_chunk_fwd.restype = i
+        lib.kda_gdn2_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
+                                           vp, ip, i, f, i, vp, sz, vp]
+        lib.kda_gdn2_recurrent_step.restype = i
+        lib.kda_gdn2_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, f,
+                                                vp]
         lib.kda_recurrent_step.restype = i
         lib.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, vp]
         lib.kda_recurrent_step_gated.restype = i
@@ -321,6 +328,100 @@ def kda_chunk_fwd_noalloc(q, k, v, alpha, beta, initial_state, o, final_state=No
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd_noalloc")
     return o, final_state
+
+
+def _cu(cu_seqlens, cu_seqlens_host, dev):
+    """(num_seqs, device tensor, host int array) of optional packed-sequence offsets."""
+    if cu_seqlens is None and cu_seqlens_host is None:
+        return 0, None, None
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.to("cpu")
+    host = [int(x) for x in (cu_seqlens_host.tolist() if isinstance(cu_seqlens_host, torch.Tensor)
+                             else cu_seqlens_host)]
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor(host, dtype=torch.int32, device=dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev, (len(host),))
+    return len(host) - 1, cu_seqlens, (ctypes.c_int * len(host))(*host)
+
+
+def kda_gdn2_chunk_fwd(q, k, v, alpha, erase, write, initial_state=None, cu_seqlens=None,
+                       cu_seqlens_host=None, scale=None, output_final_state=True,
+                       final_state=None, o=None, chunk_size=64, workspace=None):
+    """Chunk-wise Gated DeltaNet-2 forward: q, k [B, T, H, dk] and v [B, T, H, dv]
+    bf16; alpha (or None: no forget gate), erase and write [B, T, H, dk] fp32;
+    initial_state [B or N, H, dk, dv] fp32 or None; varlen and outputs as for
+    kda_chunk_fwd.  Returns (o, final_state or None)."""
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(q, "q", dt, dev)
+    _check(k, "k", dt, dev, (B, T, H, dk))
+    _check(v, "v", dt, dev, (B, T, H, dv))
+    if alpha is not None:
+        _check(alpha, "alpha", torch.float32, dev, (B, T, H, dk))
+    _check(erase, "erase", torch.float32, dev, (B, T, H, dk))
+    _check(write, "write", torch.float32, dev, (B, T, H, dk))
+    num_seqs, cu_dev, cu_host = _cu(cu_seqlens, cu_seqlens_host, dev)
+    sshape = (num_seqs if num_seqs > 0 else B, H, dk, dv)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.float32, dev, sshape)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dt, dev, (B, T, H, dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", torch.float32, dev, sshape)
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, code))
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < ws_bytes:
+            raise ValueError("workspace holds %d bytes, the call needs %d" % (workspace.numel(), ws_bytes))
+        ws, ws_bytes = workspace, workspace.numel()
+    else:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.kda_gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                                _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, dk, dv,
+                                code, _ptr(cu_dev), cu_host, num_seqs,
+                                float(scale) if scale is not None else 0.0, int(chunk_size),
+                                _ptr(ws), ws_bytes, _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_gdn2_chunk_fwd")
+    return o, final_state
+
+
+def kda_gdn2_recurrent_step(q, k, v, alpha, erase, write, state, scale=None, o=None):
+    """One Gated DeltaNet-2 decode step; ``state`` [N, H, dk, dv] fp32 is updated
+    in place.  q, k [N, H, dk]; v [N, H, dv]; alpha (or None), erase, write
+    [N, H, dk] fp32.  Returns o [N, H, dv]."""
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(q, "q", dt, dev)
+    _check(k, "k", dt, dev, (N, H, dk))
+    _check(v, "v", dt, dev, (N, H, dv))
+    if alpha is not None:
+        _check(alpha, "alpha", torch.float32, dev, (N, H, dk))
+    _check(erase, "erase", torch.float32, dev, (N, H, dk))
+    _check(write, "write", torch.float32, dev, (N, H, dk))
+    _check(state, "state", torch.float32, dev, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dt, dev, (N, H, dv))
+    st = lib.kda_gdn2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+                                     _ptr(write), _ptr(state), _ptr(o), N, H, dk, dv, code,
+                                     float(scale) if scale is not None else 0.0, _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_gdn2_recurrent_step")
+    return o
 
 
 def kda_backward_workspace_size(B, T, H, dk, dv, num_seqs, dtype=torch.bfloat16):

@@ -606,6 +606,14 @@ __global__ void order_sequences_kernel(const int* __restrict__ cu, int n, int* _
     order[rank] = i;
 }
 
+hipError_t launch_order_sequences(const int* cu_seqlens, int num_seqs, int* order,
+                                  hipStream_t stream) {
+    const int nb = (num_seqs + 255) / 256;
+    hipLaunchKernelGGL(order_sequences_kernel, dim3(nb), dim3(256), 0, stream, cu_seqlens,
+                       num_seqs, order);
+    return hipGetLastError();
+}
+
 template <typename Tin, int DK, int DVT>
 static hipError_t launch_chunk_t(const ChunkArgs& a, const int* order, hipStream_t stream) {
     using Lay = ChunkLayout<Tin, DK, DVT>;
@@ -661,10 +669,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
     if (units == 0) return hipSuccess;
     const int* order = nullptr;
     if (a.cu_seqlens && a.order) {
-        const int nb = (a.num_seqs + 255) / 256;
-        hipLaunchKernelGGL(order_sequences_kernel, dim3(nb), dim3(256), 0, stream, a.cu_seqlens,
-                           a.num_seqs, a.order);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_order_sequences(a.cu_seqlens, a.num_seqs, a.order, stream);
         if (e != hipSuccess) return e;
         order = a.order;
     }

@@ -1,0 +1,613 @@
+// gdn2_chunk.hip -- chunk-wise Gated DeltaNet-2 forward on gfx950 matrix cores.
+//
+// Method: "线性注意力机制：从标准注意力到 Gated DeltaNet-2" (jindou-blog),
+// section 4 "Gated DeltaNet-2：解耦擦除与写入", read as the KDA step with the
+// delta rule's write strength split into an erase gate e_t and a write gate
+// w_t per key channel (row of S):
+//     S_t = S~ - a_t (S~^T k_t)^T + c_t v_t^T,   S~ = Diag(alpha_t) S_{t-1},
+//     a_t = e_t . k_t,  c_t = w_t . k_t,         o_t = scale S_t^T q_t,
+// computed in the chunk-wise mode of bugfactory.tech news 3610, fifth
+// paragraph (matrix products inside a chunk, the state carried between
+// chunks; the kongchang.com page, section "硬件效率的优化策略").  The chunk
+// identities follow from the update (the pages print none).  For a chunk of
+// C = 64 tokens from state S0 with P_r the running product of alpha up to
+// token r, write Kbar = K*P, A~ = A/P, C~ = C/P (rows scaled per channel) and
+// let p_r = S~_r^T k_r be the predictions.  Unrolling the chunk gives
+//     (I + L_a) Pred = Kbar S0 + L_c V,   L_a = tril_-1(Kbar A~^T), L_c = tril_-1(Kbar C~^T)
+//     O   = scale (Qbar S0 + M_c V - M_a Pred),  M_* = tril(Qbar *~^T)
+//     S_C = Diag(P_63) (S0 + C~^T V - A~^T Pred).
+// Each token writes two rows (c_r with v_r, a_r with -p_r), so the output and
+// the state update are 128-deep products over the stacked rows F = [C~; A~]
+// and Z = [V; -Pred].  As in the KDA kernels, decays are referenced to the
+// middle of the chunk (Pm = P_31) so that both factors of every Gram product
+// stay within 2^{+-126} while alpha's product over half a chunk does:
+//     Kr = K*P/Pm, Qr = Q*P/Pm, Ec = (e.K)*Pm/P, Wc = (w.K)*Pm/P,  SP = Pm*S0
+//     Y = Kr SP + tril_-1(Kr Wc^T) V,  Pred = (I + tril_-1(Kr Ec^T))^{-1} Y
+//     O = scale (Qr SP + [tril(Qr Wc^T) | tril(Qr Ec^T)] Z)
+//     S_C = Pn*S0 + (Pn/Pm) * ([Wc; Ec]^T Z)
+// Past the end of a sequence the chunk is padded with q = k = v = 0,
+// e = w = 0, alpha = 1, an exact no-op.
+//
+// Work decomposition as in the KDA kernels: one workgroup of four waves owns
+// one (unit, value-column slice) and walks the unit's chunks with its fp32
+// state slice in matrix-core accumulator registers; the column-independent
+// work (decays, Gram products, the triangular inverse) is recomputed per
+// slice, and the slices of a unit share an XCD.  A chunk runs in five phases
+// separated by workgroup barriers (decays; operands; Gram products and Kr SP,
+// Qr SP; Y and the inverse; the solve; outputs and the state update), with
+// the next chunk's inputs loaded into registers one chunk ahead.
+#include "chunk_common.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int G2_NTH = 256;
+
+struct G2Params {
+    KParams base;                // q, k, v, alpha (NULL: no forget gate), s0, o, sT, mapping
+    const float *erase, *write;  // [tokens, H, dk]
+};
+
+template <int DK, int DVT>
+struct G2Layout {
+    static constexpr int ES = 2;                  // bf16 operands
+    static constexpr int LDK = DK + 8;            // [token][channel] tiles
+    static constexpr int LDC = CH + 8;            // [*][token] tiles
+    static constexpr int LDC2 = 2 * CH + 8;       // [*][stacked row] tiles (pad holds the decay totals)
+    static constexpr int LDD = 16 + 8;            // 16x16 blocks
+    static constexpr int LDL = 20;                // fp32 diagonal blocks of L_a
+    static constexpr int NJT = DVT / 16;
+    static constexpr int NCT = DK / 16;
+    static constexpr int NST = NCT * NJT;
+    static constexpr int STW = (NST + 3) / 4;
+    // region A, phases 0b-1: chunk operands
+    static constexpr size_t oKr = 0;
+    static constexpr size_t oQr = oKr + (size_t)CH * LDK * ES;
+    static constexpr size_t oEc = oQr + (size_t)CH * LDK * ES;
+    static constexpr size_t oWc = oEc + (size_t)CH * LDK * ES;
+    static constexpr size_t oSP = oWc + (size_t)CH * LDK * ES;
+    static constexpr size_t endA1 = oSP + (size_t)DVT * LDK * ES;
+    // region A, phases 1b-3 (overlays the above)
+    static constexpr size_t oTm = 0;
+    static constexpr size_t oYT = oTm + (size_t)CH * LDC * ES;
+    static constexpr size_t oDr = oYT + (size_t)DVT * LDC * ES;
+    static constexpr size_t oDc = oDr + (size_t)4 * 4 * 16 * LDD * ES;
+    static constexpr size_t endA2 = oDc + (size_t)4 * 4 * 16 * LDD * ES;
+    static constexpr size_t endA = endA1 > endA2 ? endA1 : endA2;
+    // region B
+    static constexpr size_t oFT = (endA + 255) / 256 * 256;        // [DK][LDC2]: [Wc; Ec]^T
+    static constexpr size_t oM = oFT + (size_t)DK * LDC2 * ES;     // [CH][LDC2]: [M_c | M_a]
+    static constexpr size_t oZT = oM + (size_t)CH * LDC2 * ES;     // [DVT][LDC2]: [V; -Pred]^T
+    static constexpr size_t oAc = oZT + (size_t)DVT * LDC2 * ES;   // [CH][LDC]: L_c
+    static constexpr size_t oLo = oAc + (size_t)CH * LDC * ES;     // [CH][LDC]: L_a off-diagonal
+    static constexpr size_t oLd = oLo + (size_t)CH * LDC * ES;     // fp32 [4][16][LDL]
+    static constexpr size_t bytes = oLd + (size_t)4 * 16 * LDL * 4;
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+// CPT = DK/64 consecutive channels of one token row in their stored form
+template <int CPT> struct G2Row;
+template <> struct G2Row<1> {
+    typedef uint16_t B;  // bf16
+    typedef float F;
+    static __device__ __forceinline__ B ldb(const bf16_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
+    static __device__ __forceinline__ F ldf(const float* p) { return *p; }
+    static __device__ __forceinline__ void ub(B w, float* x) { x[0] = __uint_as_float(uint32_t(w) << 16); }
+    static __device__ __forceinline__ void uf(F w, float* x) { x[0] = w; }
+    static __device__ __forceinline__ F one() { return 1.f; }
+};
+template <> struct G2Row<2> {
+    typedef uint32_t B;
+    typedef float2 F;
+    static __device__ __forceinline__ B ldb(const bf16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    static __device__ __forceinline__ F ldf(const float* p) { return *reinterpret_cast<const float2*>(p); }
+    static __device__ __forceinline__ void ub(B w, float* x) {
+        x[0] = __uint_as_float(w << 16);
+        x[1] = __uint_as_float(w & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void uf(F w, float* x) { x[0] = w.x; x[1] = w.y; }
+    static __device__ __forceinline__ F one() { return make_float2(1.f, 1.f); }
+};
+
+template <int DK, int DVT>
+__global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
+    using Top = bf16_t;
+    using L = G2Layout<DK, DVT>;
+    using M = Mma<Top>;
+    constexpr int CPT = DK / 64;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDC2 = L::LDC2, LDD = L::LDD, NJT = L::NJT;
+    constexpr int NST = L::NST, STW = L::STW;
+    using R = G2Row<CPT>;
+    const KParams& p = gp.base;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    Top* sKr = reinterpret_cast<Top*>(smem + L::oKr);
+    Top* sQr = reinterpret_cast<Top*>(smem + L::oQr);
+    Top* sEc = reinterpret_cast<Top*>(smem + L::oEc);
+    Top* sWc = reinterpret_cast<Top*>(smem + L::oWc);
+    Top* sSP = reinterpret_cast<Top*>(smem + L::oSP);
+    Top* sTm = reinterpret_cast<Top*>(smem + L::oTm);
+    Top* sYT = reinterpret_cast<Top*>(smem + L::oYT);
+    Top* sDr = reinterpret_cast<Top*>(smem + L::oDr);
+    Top* sDc = reinterpret_cast<Top*>(smem + L::oDc);
+    Top* sFT = reinterpret_cast<Top*>(smem + L::oFT);
+    Top* sM = reinterpret_cast<Top*>(smem + L::oM);
+    Top* sZT = reinterpret_cast<Top*>(smem + L::oZT);
+    Top* sAc = reinterpret_cast<Top*>(smem + L::oAc);
+    Top* sLo = reinterpret_cast<Top*>(smem + L::oLo);
+    float* sLd = reinterpret_cast<float*>(smem + L::oLd);
+    // the decay total of row block b for channel c sits in the 16-byte pad of FT row c
+    auto tot = [&](int b, int c) -> float& {
+        return reinterpret_cast<float*>(sFT + (size_t)c * LDC2 + 2 * CH)[b];
+    };
+
+    const WorkItem wi = decode_work(p);
+    if (!wi.valid) return;
+    const int H = p.H, h = wi.h, seq = wi.seq, jt = wi.jt, len = wi.len;
+    const long t0 = wi.t0;
+    const int DV = p.dv;
+    const bf16_t* __restrict__ gq = static_cast<const bf16_t*>(p.q);
+    const bf16_t* __restrict__ gk = static_cast<const bf16_t*>(p.k);
+    const bf16_t* __restrict__ gv = static_cast<const bf16_t*>(p.v);
+    const float* __restrict__ ga = static_cast<const float*>(p.alpha);
+    const float* __restrict__ ge = gp.erase;
+    const float* __restrict__ gw = gp.write;
+    bf16_t* __restrict__ go = static_cast<bf16_t*>(p.o);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int ln = l & 15;
+    const int lg = l >> 4;
+    const int col0 = jt * DVT;
+
+    // ---- state slice in C-layout registers: wave w owns tiles w, w+4, ... ----
+    f32x4 S[STW];
+    const size_t sbase = ((size_t)seq * H + h) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < STW; ++i) {
+        const int st = w + 4 * i;
+        S[i] = zero4();
+        if (st < NST && p.s0) {
+            const int ct = st / NJT, jj = st % NJT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                S[i][e] = p.s0[sbase + (size_t)(ct * 16 + lg * 4 + e) * DV + col0 + jj * 16 + ln];
+        }
+    }
+
+    // Blocks above the diagonal of M (both halves) and of L_c are read by the
+    // 32-deep steps and must be zero; nothing else writes them.
+    for (int idx = tid; idx < CH * 2 * CH; idx += G2_NTH) {
+        const int r = idx / (2 * CH), c = idx % (2 * CH);
+        if (((c & (CH - 1)) >> 4) > (r >> 4)) sM[r * LDC2 + c] = from_f32<Top>(0.f);
+    }
+    for (int idx = tid; idx < CH * CH; idx += G2_NTH) {
+        const int r = idx / CH, c = idx % CH;
+        if ((c >> 4) > (r >> 4)) sAc[r * LDC + c] = from_f32<Top>(0.f);
+    }
+
+    // ---- register prefetch: row block w, channels l*CPT.. ----
+    typename R::B pq[16], pk[16];
+    typename R::F pa[16], pe[16], pw[16];
+    bf16_t pv[NJT][4];
+    const int c0 = l * CPT;
+    auto load_rows = [&](int ch) {
+        const int base_r = ch * CH + w * 16;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = min(base_r + r, len - 1);  // rows past the end are replaced when used
+            const size_t off = ((size_t)(t0 + t) * H + h) * DK + c0;
+            pq[r] = R::ldb(gq + off);
+            pk[r] = R::ldb(gk + off);
+            pa[r] = ga ? R::ldf(ga + off) : R::one();
+            pe[r] = R::ldf(ge + off);
+            pw[r] = R::ldf(gw + off);
+        }
+    };
+    auto load_v = [&](int ch) {
+#pragma unroll
+        for (int jb = 0; jb < NJT; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = min(ch * CH + w * 16 + lg * 4 + e, len - 1);
+                pv[jb][e] = gv[((size_t)(t0 + t) * H + h) * DV + col0 + jb * 16 + ln];
+            }
+    };
+
+    const int nch = (len + CH - 1) / CH;
+    if (nch > 0) { load_rows(0); load_v(0); }
+
+    float pn_s[STW][4], pnm_s[STW][4];
+
+    for (int ch = 0; ch < nch; ++ch) {
+        // ================= phase 0a: running products inside row block w ======
+        float pr[16][CPT];
+        const int nvalid = len - (ch * CH + w * 16);
+        {
+            float run[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) run[c] = 1.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float a[CPT];
+                R::uf(pa[r], a);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    run[c] *= (r < nvalid) ? a[c] : 1.f;
+                    pr[r][c] = run[c];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) tot(w, c0 + c) = run[c];
+        }
+        __syncthreads();  // B1
+
+        // ================= phase 0b: decayed operands ==========================
+        {
+            float pre[CPT], ipm[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const float t0v = tot(0, c0 + c), t1v = tot(1, c0 + c), t2v = tot(2, c0 + c);
+                pre[c] = (w == 0) ? 1.f : (w == 1) ? t0v : (w == 2) ? t0v * t1v : t0v * t1v * t2v;
+                ipm[c] = fast_rcp(t0v * t1v);  // 1 / P_31
+            }
+            Top wct[CPT][16], ect[CPT][16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = w * 16 + r;
+                const bool ok = r < nvalid;
+                float kx[CPT], qx[CPT], ex[CPT], wx[CPT];
+                R::ub(pk[r], kx);
+                R::ub(pq[r], qx);
+                R::uf(pe[r], ex);
+                R::uf(pw[r], wx);
+                Top kr[CPT], qr[CPT], ec[CPT], wc[CPT];
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    const float kv = ok ? kx[c] : 0.f;
+                    const float qv = ok ? qx[c] : 0.f;
+                    const float ratio = pre[c] * pr[r][c] * ipm[c];  // P_row / P_31
+                    const float inv = fast_rcp(ratio);
+                    kr[c] = from_f32<Top>(kv * ratio);
+                    qr[c] = from_f32<Top>(qv * ratio);
+                    ec[c] = from_f32<Top>(ex[c] * kv * inv);
+                    wc[c] = from_f32<Top>(wx[c] * kv * inv);
+                    ect[c][r] = ec[c];
+                    wct[c][r] = wc[c];
+                }
+                store_run<Top, CPT>(sKr + row * LDK + c0, kr);
+                store_run<Top, CPT>(sQr + row * LDK + c0, qr);
+                store_run<Top, CPT>(sEc + row * LDK + c0, ec);
+                store_run<Top, CPT>(sWc + row * LDK + c0, wc);
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + w * 16, wct[c]);
+                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + CH + w * 16, ect[c]);
+            }
+            // V^T into the first half of Z (4 consecutive tokens per lane)
+#pragma unroll
+            for (int jb = 0; jb < NJT; ++jb) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = (ch * CH + w * 16 + lg * 4 + e < len) ? to_f32(pv[jb][e]) : 0.f;
+                M::st4(sZT + (jb * 16 + ln) * LDC2 + w * 16 + lg * 4, x);
+            }
+            // SP = (Pm * S0)^T and the per-row decays kept for the state update
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int st = w + 4 * i;
+                if (st < NST) {
+                    const int ct = st / NJT, jj = st % NJT;
+                    f32x4 sp;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = ct * 16 + lg * 4 + e;
+                        const float a0 = tot(0, c), a1 = tot(1, c), a2 = tot(2, c), a3 = tot(3, c);
+                        const float pm = a0 * a1;
+                        pn_s[i][e] = pm * a2 * a3;
+                        pnm_s[i][e] = a2 * a3;  // Pn / Pm
+                        sp[e] = pm * S[i][e];
+                    }
+                    M::st4(sSP + (jj * 16 + ln) * LDK + ct * 16 + lg * 4, sp);
+                }
+            }
+        }
+        if (ch + 1 < nch) load_rows(ch + 1);
+        __syncthreads();  // B2
+
+        // ================= phase 1: Gram blocks, X = Kr SP and OI = Qr SP =====
+        f32x4 xr[NJT], oi[NJT];
+        {
+            // jobs (a, b), b <= a, round-robin over the waves; transposed tiles
+            // F_b Kr_a^T give each lane 4 consecutive i of row r = 16a + ln
+#pragma unroll
+            for (int jn = w; jn < 10; jn += 4) {
+                const int a = (jn >= 6) ? 3 : (jn >= 3) ? 2 : (jn >= 1) ? 1 : 0;
+                const int b = jn - a * (a + 1) / 2;
+                f32x4 cLa = zero4(), cLc = zero4(), cMa = zero4(), cMc = zero4();
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s) {
+                    const auto fe = M::ld32(sEc + (b * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fw = M::ld32(sWc + (b * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fk = M::ld32(sKr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fq = M::ld32(sQr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
+                    cLa = M::k32(fe, fk, cLa);
+                    cLc = M::k32(fw, fk, cLc);
+                    cMa = M::k32(fe, fq, cMa);
+                    cMc = M::k32(fw, fq, cMc);
+                }
+                const int r = a * 16 + ln;
+                if (a == b) {
+                    float4 ld;
+                    ld.x = (lg * 4 + 0 < ln) ? cLa[0] : 0.f;
+                    ld.y = (lg * 4 + 1 < ln) ? cLa[1] : 0.f;
+                    ld.z = (lg * 4 + 2 < ln) ? cLa[2] : 0.f;
+                    ld.w = (lg * 4 + 3 < ln) ? cLa[3] : 0.f;
+                    *reinterpret_cast<float4*>(sLd + (a * 16 + ln) * L::LDL + lg * 4) = ld;
+                    f32x4 lc, mc, ma;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lc[e] = (lg * 4 + e < ln) ? cLc[e] : 0.f;
+                        mc[e] = (lg * 4 + e <= ln) ? cMc[e] : 0.f;
+                        ma[e] = (lg * 4 + e <= ln) ? cMa[e] : 0.f;
+                    }
+                    M::st4(sAc + r * LDC + b * 16 + lg * 4, lc);
+                    M::st4(sM + r * LDC2 + b * 16 + lg * 4, mc);
+                    M::st4(sM + r * LDC2 + CH + b * 16 + lg * 4, ma);
+                } else {
+                    M::st4(sLo + r * LDC + b * 16 + lg * 4, cLa);
+                    M::st4(sAc + r * LDC + b * 16 + lg * 4, cLc);
+                    M::st4(sM + r * LDC2 + b * 16 + lg * 4, cMc);
+                    M::st4(sM + r * LDC2 + CH + b * 16 + lg * 4, cMa);
+                }
+            }
+#pragma unroll
+            for (int jb = 0; jb < NJT; ++jb) {
+                f32x4 cx = zero4(), co = zero4();
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s) {
+                    const auto fs = M::ld32(sSP + (jb * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fk = M::ld32(sKr + (w * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fq = M::ld32(sQr + (w * 16 + ln) * LDK + s * 32 + lg * 8);
+                    cx = M::k32(fk, fs, cx);
+                    co = M::k32(fq, fs, co);
+                }
+                xr[jb] = cx;
+                oi[jb] = co;
+            }
+        }
+        if (ch + 1 < nch) load_v(ch + 1);
+        __syncthreads();  // B3
+
+        // ================= phase 2: Y = X + L_c V, T = (I + L_a)^{-1} ===========
+        {
+            const int ns = (w >= 2) ? 2 : 1;
+#pragma unroll
+            for (int jb = 0; jb < NJT; ++jb) {
+                f32x4 cy = xr[jb];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s < ns) {
+                        const auto fa = M::ld32(sAc + (w * 16 + ln) * LDC + s * 32 + lg * 8);
+                        const auto fv = M::ld32(sZT + (jb * 16 + ln) * LDC2 + s * 32 + lg * 8);
+                        cy = M::k32(fa, fv, cy);
+                    }
+                }
+                M::st4(sYT + (jb * 16 + ln) * LDC + w * 16 + lg * 4, cy);
+            }
+            // diagonal blocks: lane (block lg, column ln) solves L_aa x = e_ln
+            float x[16];
+            const float* La = sLd + lg * 16 * L::LDL;
+            float4 lrow[16][4];
+#pragma unroll
+            for (int r = 1; r < 16; ++r)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    if (q4 * 4 < r) lrow[r][q4] = *reinterpret_cast<const float4*>(La + r * L::LDL + q4 * 4);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                for (int r = i + 1; r < 16; ++r) {
+                    const float4 v4 = lrow[r][i / 4];
+                    const float lv = (i % 4 == 0) ? v4.x : (i % 4 == 1) ? v4.y : (i % 4 == 2) ? v4.z : v4.w;
+                    x[r] -= lv * x[i];
+                }
+            }
+            Top* Dr = sDr + (size_t)w * 4 * 16 * LDD;
+            Top* Dc = sDc + (size_t)w * 4 * 16 * LDD;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Dr[(lg * 16 + r) * LDD + ln] = from_f32<Top>(x[r]);
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 t4 = {x[r4 * 4], x[r4 * 4 + 1], x[r4 * 4 + 2], x[r4 * 4 + 3]};
+                M::st4(Dc + (lg * 16 + ln) * LDD + r4 * 4, t4);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+            // column block b = w: T_bb = D_b, T_ab = -D_a sum_{j=b}^{a-1} L_aj T_jb
+            const int b = w;
+            f32x4 TB[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) TB[0][e] = to_f32(Dc[(b * 16 + ln) * LDD + lg * 4 + e]);
+#pragma unroll
+            for (int d = 1; d < 4; ++d) {
+                const int a = b + d;
+                if (a < 4) {
+                    f32x4 y = zero4();
+#pragma unroll
+                    for (int jd = 0; jd < d; ++jd) {
+                        const int j = b + jd;
+                        const auto fa = M::ld16(sLo + (a * 16 + ln) * LDC + j * 16 + lg * 4);
+                        y = M::k16(fa, M::pack16(TB[jd]), y);
+                    }
+                    const auto fd = M::ld16(Dr + (a * 16 + ln) * LDD + lg * 4);
+                    f32x4 t = M::k16(fd, M::pack16(y), zero4());
+                    TB[d][0] = -t[0]; TB[d][1] = -t[1]; TB[d][2] = -t[2]; TB[d][3] = -t[3];
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int a = b + d;
+                if (a < 4) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(TB[d][e]);
+                }
+            }
+            for (int a = 0; a < b; ++a) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(0.f);
+            }
+        }
+        __syncthreads();  // B4
+
+        // ================= phase 3: Pred = T Y, stored as -Pred^T in Z ==========
+        {
+            const int ns = (w >= 2) ? 2 : 1;
+#pragma unroll
+            for (int jb = 0; jb < NJT; ++jb) {
+                f32x4 cp = zero4();
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s < ns) {
+                        const auto ft = M::ld32(sTm + (w * 16 + ln) * LDC + s * 32 + lg * 8);
+                        const auto fy = M::ld32(sYT + (jb * 16 + ln) * LDC + s * 32 + lg * 8);
+                        cp = M::k32(ft, fy, cp);
+                    }
+                }
+                f32x4 np = {-cp[0], -cp[1], -cp[2], -cp[3]};
+                M::st4(sZT + (jb * 16 + ln) * LDC2 + CH + w * 16 + lg * 4, np);
+            }
+        }
+        __syncthreads();  // B5
+
+        // ================= phase 4: outputs and the next state =================
+        {
+            const int ns = (w >= 2) ? 2 : 1;
+#pragma unroll
+            for (int jb = 0; jb < NJT; ++jb) {
+                f32x4 co = oi[jb];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        if (s < ns) {
+                            const int k0 = half * CH + s * 32 + lg * 8;
+                            const auto fm = M::ld32(sM + (w * 16 + ln) * LDC2 + k0);
+                            const auto fz = M::ld32(sZT + (jb * 16 + ln) * LDC2 + k0);
+                            co = M::k32(fm, fz, co);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = ch * CH + w * 16 + lg * 4 + e;
+                    if (t < len)
+                        go[((size_t)(t0 + t) * H + h) * DV + col0 + jb * 16 + ln] =
+                            from_f32<bf16_t>(p.scale * co[e]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int st = w + 4 * i;
+                if (st < NST) {
+                    const int ct = st / NJT, jj = st % NJT;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const auto ff = M::ld32(sFT + (ct * 16 + ln) * LDC2 + s * 32 + lg * 8);
+                        const auto fz = M::ld32(sZT + (jj * 16 + ln) * LDC2 + s * 32 + lg * 8);
+                        acc = M::k32(ff, fz, acc);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[i][e] = pn_s[i][e] * S[i][e] + pnm_s[i][e] * acc[e];
+                }
+            }
+        }
+    }
+
+    if (p.sT) {
+#pragma unroll
+        for (int i = 0; i < STW; ++i) {
+            const int st = w + 4 * i;
+            if (st < NST) {
+                const int ct = st / NJT, jj = st % NJT;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p.sT[sbase + (size_t)(ct * 16 + lg * 4 + e) * DV + col0 + jj * 16 + ln] = S[i][e];
+            }
+        }
+    }
+}
+
+template <int DK, int DVT>
+hipError_t launch_g2(const G2Params& gp, hipStream_t stream) {
+    using Lay = G2Layout<DK, DVT>;
+    const int groups = (gp.base.units + 7) / 8;
+    const long grid = 8L * gp.base.njt_all * groups;
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void*)gdn2_chunk_kernel<DK, DVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)Lay::bytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gdn2_chunk_kernel<DK, DVT>), dim3((unsigned)grid), dim3(G2_NTH),
+                       Lay::bytes, stream, gp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Value-column tile: the widest that still gives every compute unit a
+// workgroup (at most 32 at dk = 128, where wider slices do not fit in LDS).
+int plan_gdn2_dvt(int units, int dk, int dv) {
+    const int widest = dk == 128 ? 32 : 64;
+    for (int dvt = widest; dvt >= 16; dvt /= 2)
+        if (dvt <= dv && (long)units * (dv / dvt) >= 256) return dvt;
+    return 16;
+}
+
+hipError_t launch_gdn2_chunk_fwd(const Gdn2ChunkArgs& a, hipStream_t stream) {
+    const int nseq = a.cu_seqlens ? a.num_seqs : a.B;
+    const int units = nseq * a.H;
+    if (units == 0) return hipSuccess;
+    const int* order = nullptr;
+    if (a.cu_seqlens && a.order) {
+        hipError_t e = launch_order_sequences(a.cu_seqlens, a.num_seqs, a.order, stream);
+        if (e != hipSuccess) return e;
+        order = a.order;
+    }
+    int dvt = a.dvt > 0 ? a.dvt : plan_gdn2_dvt(units, a.dk, a.dv);
+    if (dvt > a.dv) dvt = a.dv;
+    if (a.dk == 128 && dvt > 32) dvt = 32;
+    G2Params gp;
+    KParams& p = gp.base;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.beta = nullptr; p.s0 = a.s0;
+    p.o = a.o; p.sT = a.sT; p.cu_seqlens = a.cu_seqlens; p.order = order;
+    p.B = a.B; p.T = a.T; p.H = a.H; p.dv = a.dv;
+    p.units = units;
+    p.njt_all = a.dv / dvt;
+    p.gate = 0;
+    p.fuse = 0;
+    p.scale = a.scale;
+    gp.erase = a.erase;
+    gp.write = a.write;
+    if (a.dk == 128) {
+        return dvt == 16 ? launch_g2<128, 16>(gp, stream) : launch_g2<128, 32>(gp, stream);
+    }
+    switch (dvt) {
+        case 16: return launch_g2<64, 16>(gp, stream);
+        case 32: return launch_g2<64, 32>(gp, stream);
+        default: return launch_g2<64, 64>(gp, stream);
+    }
+}
+
+}  // namespace kda

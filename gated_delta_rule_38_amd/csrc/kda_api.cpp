@@ -447,3 +447,126 @@ kda_status recurrent_step_impl(const void* q, const void* k, const void* v, cons
 }
 
 }  // namespace
+
+extern "C" {
+
+kda_status kda_gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* erase, const float* write,
+                              const float* initial_state, void* o, float* final_state, int B,
+                              int T, int H, int dk, int dv, kda_dtype dtype,
+                              const int* cu_seqlens_dev, const int* cu_seqlens_host,
+                              int num_seqs, float scale, int chunk_size, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    try {
+        if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
+        if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return KDA_ERROR_INVALID_VALUE;
+        if (chunk_size != kChunk) return KDA_ERROR_NOT_SUPPORTED;
+        if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
+        // the chunk kernel keeps bf16 operands only (float32 ones do not fit in LDS)
+        if (dtype != KDA_DTYPE_BF16) return KDA_ERROR_NOT_SUPPORTED;
+        const bool varlen = num_seqs > 0;
+        if (!varlen && (cu_seqlens_dev || cu_seqlens_host)) return KDA_ERROR_INVALID_VALUE;
+        const size_t es = 2;
+        int nstates = B;
+        if (varlen) {
+            if (!cu_seqlens_dev || !cu_seqlens_host || B != 1) return KDA_ERROR_INVALID_VALUE;
+            if (cu_seqlens_host[0] != 0 || cu_seqlens_host[num_seqs] != T)
+                return KDA_ERROR_INVALID_VALUE;
+            for (int n = 0; n < num_seqs; ++n)
+                if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERROR_INVALID_VALUE;
+            if ((reinterpret_cast<uintptr_t>(cu_seqlens_dev) & 3u) != 0)
+                return KDA_ERROR_MISALIGNED;
+            nstates = num_seqs;
+        }
+        size_t b_qk, b_v, b_g, b_s;
+        if (!bytes_of(B, T, H, dk, es, &b_qk) || !bytes_of(B, T, H, dv, es, &b_v) ||
+            !bytes_of(B, T, H, dk, 4, &b_g) || !bytes_of(nstates, H, dk, dv, 4, &b_s))
+            return KDA_ERROR_INVALID_VALUE;
+        if ((long long)nstates * H * (dv / 16) > (1LL << 30)) return KDA_ERROR_NOT_SUPPORTED;
+        if ((long long)B * T > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
+        const size_t tokens = (size_t)B * T * H;
+        const size_t units = (size_t)nstates * H;
+        if (tokens > 0 && (!q || !k || !v || !erase || !write || !o))
+            return KDA_ERROR_INVALID_VALUE;
+        // q, k and the three gates are read in pairs of channels
+        const void* pairs[] = {q, k, alpha, erase, write};
+        for (const void* ptr : pairs)
+            if (!aligned(ptr, 8)) return KDA_ERROR_MISALIGNED;
+        if (!aligned(v, es) || !aligned(o, es)) return KDA_ERROR_MISALIGNED;
+        const void* words[] = {initial_state, final_state, workspace};
+        for (const void* ptr : words)
+            if (!aligned(ptr, 4)) return KDA_ERROR_MISALIGNED;
+        const size_t need_ws = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype);
+        if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+            return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+        const Range r_o = range_of(o, tokens ? b_v : 0);
+        const Range r_f = range_of(final_state, units ? b_s : 0);
+        const Range r_ws = range_of(workspace, need_ws);
+        const Range ins[] = {range_of(q, b_qk), range_of(k, b_qk), range_of(v, b_v),
+                             range_of(alpha, tokens ? b_g : 0), range_of(erase, b_g),
+                             range_of(write, b_g),
+                             range_of(cu_seqlens_dev, varlen ? (size_t)(num_seqs + 1) * 4 : 0)};
+        for (const Range& r : ins)
+            if (overlap(r_o, r) || overlap(r_f, r) || overlap(r_ws, r))
+                return KDA_ERROR_INVALID_VALUE;
+        const Range r_i = range_of(initial_state, units ? b_s : 0);
+        if (overlap(r_o, r_i) || overlap(r_o, r_f) || overlap(r_o, r_ws) || overlap(r_f, r_ws) ||
+            overlap(r_i, r_ws))
+            return KDA_ERROR_INVALID_VALUE;
+        if (overlap(r_f, r_i) && final_state != initial_state) return KDA_ERROR_INVALID_VALUE;
+        if (units == 0) return KDA_SUCCESS;
+
+        kda::Gdn2ChunkArgs a;
+        a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.erase = erase; a.write = write;
+        a.s0 = initial_state; a.o = o; a.sT = final_state;
+        a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
+        a.bf16 = true;
+        a.cu_seqlens = varlen ? cu_seqlens_dev : nullptr;
+        a.num_seqs = varlen ? num_seqs : 0;
+        a.order = (varlen && num_seqs <= 65536) ? static_cast<int*>(workspace) : nullptr;
+        a.scale = default_scale(scale, dk);
+        a.dvt = env_dvt();
+        return kda::launch_gdn2_chunk_fwd(a, stream) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+    } catch (...) {
+        return KDA_ERROR_HIP;
+    }
+}
+
+kda_status kda_gdn2_recurrent_step(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* erase, const float* write,
+                                   float* state, void* o, int N, int H, int dk, int dv,
+                                   kda_dtype dtype, float scale, hipStream_t stream) {
+    try {
+        if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
+        if (N < 0 || H < 0) return KDA_ERROR_INVALID_VALUE;
+        if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
+        if ((long long)N * H > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
+        const size_t units = (size_t)N * H;
+        if (units == 0) return KDA_SUCCESS;
+        if (!q || !k || !v || !erase || !write || !state || !o) return KDA_ERROR_INVALID_VALUE;
+        const size_t es = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+        if (!aligned(state, 16)) return KDA_ERROR_MISALIGNED;
+        if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(o, es) ||
+            !aligned(alpha, 4) || !aligned(erase, 4) || !aligned(write, 4))
+            return KDA_ERROR_MISALIGNED;
+        const Range r_s = range_of(state, units * dk * dv * 4);
+        const Range r_o = range_of(o, units * dv * es);
+        const Range ins[] = {range_of(q, units * dk * es), range_of(k, units * dk * es),
+                             range_of(v, units * dv * es), range_of(alpha, units * dk * 4),
+                             range_of(erase, units * dk * 4), range_of(write, units * dk * 4)};
+        for (const Range& r : ins)
+            if (overlap(r_s, r) || overlap(r_o, r)) return KDA_ERROR_INVALID_VALUE;
+        if (overlap(r_s, r_o)) return KDA_ERROR_INVALID_VALUE;
+        kda::Gdn2StepArgs a;
+        a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.erase = erase; a.write = write;
+        a.state = state; a.o = o;
+        a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+        a.bf16 = dtype == KDA_DTYPE_BF16;
+        a.scale = default_scale(scale, dk);
+        return kda::launch_gdn2_step(a, stream) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+    } catch (...) {
+        return KDA_ERROR_HIP;
+    }
+}
+
+}  // extern "C"

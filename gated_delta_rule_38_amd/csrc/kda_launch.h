@@ -54,6 +54,38 @@ hipError_t noalloc_order_buffer(hipStream_t stream, int **out);
 // value-column tile the planner picks for a given number of units
 int plan_chunk_dvt(int units, int dv, bool bf16);
 
+// Gated DeltaNet-2: per-key-channel erase and write gates in place of beta
+struct Gdn2StepArgs {
+    const void *q, *k, *v;
+    const float *alpha;          // [N, H, dk] decays, or NULL (no forget gate)
+    const float *erase, *write;  // [N, H, dk]
+    float *state;
+    void *o;
+    int N, H, dk, dv;
+    bool bf16;
+    float scale;
+};
+
+hipError_t launch_gdn2_step(const Gdn2StepArgs &a, hipStream_t stream);
+
+struct Gdn2ChunkArgs {
+    const void *q, *k, *v;
+    const float *alpha;          // [B, T, H, dk] decays, or NULL (no forget gate)
+    const float *erase, *write;  // [B, T, H, dk]
+    const float *s0;
+    void *o;
+    float *sT;
+    int B, T, H, dk, dv;
+    bool bf16;
+    const int *cu_seqlens;  // device, NULL in dense mode
+    int num_seqs;
+    int *order;             // device workspace for the longest-first order (varlen), or NULL
+    float scale;
+    int dvt;                // value columns per workgroup (0 = choose)
+};
+
+hipError_t launch_gdn2_chunk_fwd(const Gdn2ChunkArgs &a, hipStream_t stream);
+
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *alpha, *beta, *s0, *dsT;

@@ -291,6 +291,49 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
                         const int *cu_seqlens_host, int num_seqs, float scale, void *workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Gated DeltaNet-2 ("线性注意力机制：从标准注意力到 Gated DeltaNet-2",
+ * jindou-blog, section 4 "Gated DeltaNet-2：解耦擦除与写入"): the delta rule's
+ * one write strength beta is split into an erase gate e_t and a write gate
+ * w_t, each one value per key channel, with KDA's per-channel forget gate
+ * kept.  Per token (the page prints the update garbled; this is the reading
+ * under which KDA, Gated DeltaNet and linear attention are its special cases,
+ * as the page's table states):
+ *   forget  S~  = Diag(alpha_t) S_{t-1}
+ *   predict vh  = S~^T k_t
+ *   erase   S'  = S~ - (e_t . k_t) vh^T        ((e . k)_i = e_i k_i)
+ *   write   S_t = S' + (w_t . k_t) v_t^T
+ *   read    o_t = scale * S_t^T q_t
+ * e_t = w_t = beta_t is KDA exactly; e_t = 0 is a gated linear attention.
+ *
+ * kda_gdn2_chunk_fwd: the chunk-wise forward; arguments as for
+ * kda_chunk_fwd, with erase and write [B, T, H, dk] float32 in place of beta,
+ * and alpha [B, T, H, dk] float32 or NULL (no forget gate, alpha = 1).
+ * q, k, alpha, erase and write need 8-byte alignment.  Only bf16 q, k, v
+ * (dtype KDA_DTYPE_BF16) are supported (KDA_ERROR_NOT_SUPPORTED otherwise).
+ * workspace as for kda_chunk_fwd (kda_chunk_fwd_workspace_size).  The decay
+ * domain is that of kda_chunk_fwd.
+ */
+kda_status kda_gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *alpha,
+                              const float *erase, const float *write,
+                              const float *initial_state, void *o, float *final_state, int B,
+                              int T, int H, int dk, int dv, kda_dtype dtype,
+                              const int *cu_seqlens_dev, const int *cu_seqlens_host,
+                              int num_seqs, float scale, int chunk_size, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_gdn2_recurrent_step: one Gated DeltaNet-2 decode step, state updated in
+ * place; arguments as for kda_recurrent_step with erase and write [N, H, dk]
+ * float32 in place of beta and alpha [N, H, dk] float32 or NULL.  bf16 and
+ * float32 q, k, v are supported, and any alpha in (0, 1] (the step takes no
+ * running products).
+ */
+kda_status kda_gdn2_recurrent_step(const void *q, const void *k, const void *v,
+                                   const float *alpha, const float *erase, const float *write,
+                                   float *state, void *o, int N, int H, int dk, int dv,
+                                   kda_dtype dtype, float scale, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *kda_status_string(kda_status status);
 

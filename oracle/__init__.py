@@ -256,18 +256,31 @@ def gdn2_forward(q, k, v, alpha, erase, write, initial_state=None, cu_seqlens=No
     return o_all, s_all
 
 
-def gdn2_step(q, k, v, alpha, erase, write, state, scale=None, threads=0):
+def gdn2_step(q, k, v, alpha, erase, write, state, scale=None, threads=0, in_place=False):
     """One Gated DeltaNet-2 decode step: q, k, alpha, erase, write [N, H, dk]
     (alpha None: no forget gate); v [N, H, dv]; state [N, H, dk, dv].  Returns
-    (o [N, H, dv], new_state), float64; the input state is not modified."""
+    (o [N, H, dv], new_state), float64.  The input state is not modified unless
+    in_place is set and it is a contiguous float64 array, which is then
+    rewritten and returned (each unit reads its state before writing it)."""
     q, k, v, erase, write = (_f64(x) for x in (q, k, v, erase, write))
     alpha = np.ones_like(k) if alpha is None else _f64(alpha)
     N, H, dk = q.shape
     dv = v.shape[2]
-    unit = lambda x: x.reshape(N * H, 1, x.shape[-1])
-    o, s = gdn2_forward_units(unit(q), unit(k), unit(v), unit(alpha), unit(erase), unit(write),
-                              _f64(state).reshape(N * H, dk, dv), scale=scale, threads=threads)
-    return o.reshape(N, H, dv), s.reshape(N, H, dk, dv)
+    if scale is None:
+        scale = dk ** -0.5
+    if in_place and isinstance(state, np.ndarray) and state.dtype == np.float64 \
+            and state.flags.c_contiguous:
+        st = state
+    else:
+        st = _f64(state).copy()
+    o = np.zeros((N, H, dv), np.float64)
+    c = lambda x: np.ascontiguousarray(x)
+    rc = _load().gdn2_oracle_forward(_ptr(c(q)), _ptr(c(k)), _ptr(c(v)), _ptr(c(alpha)),
+                                     _ptr(c(erase)), _ptr(c(write)), _ptr(st), _ptr(o), _ptr(st),
+                                     N * H, 1, dk, dv, float(scale), int(threads))
+    if rc != 0:
+        raise RuntimeError("gdn2_oracle_forward failed with %d" % rc)
+    return o, st
 
 
 def backward_units(q, k, v, alpha, beta, initial_state, do, dfinal_state=None, scale=None,

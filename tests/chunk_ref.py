@@ -93,3 +93,49 @@ def chunk_forward_unit(q, k, v, alpha, beta, s0, scale, bf16_ops=False):
             S = f32(S)
         o[c0:c0 + n] = O[:n]
     return o, S
+
+
+def gdn2_chunk_forward_unit(q, k, v, alpha, erase, write, s0, scale, bf16_ops=False):
+    """Gated DeltaNet-2, one unit, in the chunk decomposition of the HIP kernel
+    (erase vectors a = e . k, write vectors c = w . k; Pred = the predictions
+    S~_r^T k_r of the chunk's tokens):
+
+      Kr = K * P / Pm, Qr = Q * P / Pm, Ec = (E.K) * Pm / P, Wc = (W.K) * Pm / P
+      Y    = Kr (Pm * S0) + strict_lower(Kr Wc^T) V
+      Pred = (I + strict_lower(Kr Ec^T))^{-1} Y                (blocked over 16 rows)
+      O    = scale (Qr (Pm * S0) + [lower(Qr Wc^T) | lower(Qr Ec^T)] [V; -Pred])
+      S    = Pn * S0 + (Pn / Pm) * ([Wc; Ec]^T [V; -Pred])
+    """
+    rnd = bf16 if bf16_ops else (lambda x: x)
+    T_, dk = k.shape
+    dv = v.shape[1]
+    S = s0.astype(np.float64).copy()
+    o = np.zeros((T_, dv))
+    for c0 in range(0, T_, C):
+        n = min(C, T_ - c0)
+        Q = np.zeros((C, dk)); K = np.zeros((C, dk)); V = np.zeros((C, dv))
+        Al = np.ones((C, dk)); E = np.zeros((C, dk)); W = np.zeros((C, dk))
+        Q[:n], K[:n], V[:n] = q[c0:c0 + n], k[c0:c0 + n], v[c0:c0 + n]
+        Al[:n], E[:n], W[:n] = alpha[c0:c0 + n], erase[c0:c0 + n], write[c0:c0 + n]
+        P = np.cumprod(Al, axis=0)
+        if bf16_ops:
+            P = f32(np.cumprod(f32(Al), axis=0))
+        Pm, Pn = P[31], P[C - 1]
+        Kr, Qr = K * P / Pm, Q * P / Pm
+        Ec, Wc = E * K * Pm / P, W * K * Pm / P
+        La = np.tril(rnd(Kr) @ rnd(Ec).T, -1)
+        Lc = np.tril(rnd(Kr) @ rnd(Wc).T, -1)
+        Ma = np.tril(rnd(Qr) @ rnd(Ec).T, 0)
+        Mc = np.tril(rnd(Qr) @ rnd(Wc).T, 0)
+        SP = rnd(Pm[:, None] * S)
+        Y = rnd(Kr) @ SP + rnd(Lc) @ rnd(V)
+        Tm = blocked_unit_lower_inverse(np.eye(C) + La, rnd)
+        Pred = rnd(Tm) @ rnd(Y)
+        Z = np.concatenate([V, -Pred])
+        O = scale * (rnd(Qr) @ SP + rnd(np.concatenate([Mc, Ma], 1)) @ rnd(Z))
+        F = np.concatenate([Wc, Ec])
+        S = Pn[:, None] * S + (Pn / Pm)[:, None] * (rnd(F).T @ rnd(Z))
+        if bf16_ops:
+            S = f32(S)
+        o[c0:c0 + n] = O[:n]
+    return o, S

@@ -241,3 +241,34 @@ def test_gdn2_layouts_match_units():
     of, sf = oracle.gdn2_forward(q[:, :1], k[:, :1], v[:, :1], a[:, :1], e[:, :1], w[:, :1],
                                  s0, scale=0.4)
     assert np.array_equal(os_, of[:, 0]) and np.array_equal(ss, sf)
+
+
+@pytest.mark.parametrize("T,dk,dv", [(64, 8, 4), (150, 16, 8), (1, 8, 8), (200, 32, 16)])
+def test_gdn2_chunk_algebra_matches_the_oracle(T, dk, dv):
+    """The chunk decomposition the HIP kernel uses (tests/chunk_ref.py, fp64)
+    equals the oracle's token loop: full and partial chunks, mid-chunk decay
+    references and the stacked [V; -Pred] products."""
+    import chunk_ref
+    rng = np.random.default_rng(T + dk)
+    q, k = unit(rng.standard_normal((T, dk))), unit(rng.standard_normal((T, dk)))
+    v = rng.standard_normal((T, dv))
+    alpha = sig(rng.normal(3.0, 1.0, (T, dk)))
+    erase, write = sig(rng.standard_normal((T, dk))), sig(rng.standard_normal((T, dk)))
+    s0 = 0.2 * rng.standard_normal((dk, dv))
+    o, s = chunk_ref.gdn2_chunk_forward_unit(q, k, v, alpha, erase, write, s0, 0.5)
+    ro, rs = gdn2_impl(q, k, v, alpha, erase, write, s0, 0.5)
+    assert rel(o, ro) < 1e-12 and rel(s, rs) < 1e-12
+
+
+def test_gdn2_step_in_place_matches_copy():
+    rng = np.random.default_rng(11)
+    N, H, dk, dv = 3, 2, 4, 5
+    q, k, v = rng.standard_normal((N, H, dk)), rng.standard_normal((N, H, dk)), \
+        rng.standard_normal((N, H, dv))
+    a, e, w = (rng.uniform(0.2, 1.0, (N, H, dk)) for _ in range(3))
+    s = rng.standard_normal((N, H, dk, dv))
+    o1, s1 = oracle.gdn2_step(q, k, v, a, e, w, s)
+    s2 = s.copy()
+    o2, s3 = oracle.gdn2_step(q, k, v, a, e, w, s2, in_place=True)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2) and s3 is s2
+    assert not np.array_equal(s, s1)

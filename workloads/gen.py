@@ -124,3 +124,27 @@ def decode_inputs(cfg, device="cpu", N=None, H=None, steps=None, seed=None, gate
     alpha = _alpha((steps, N, H), cfg.dk, gate, g, device, cfg.alpha_mu, logits=raw, dtype=dt)
     return dict(state=state.contiguous(), q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
                 alpha=alpha, beta=beta.contiguous(), gate=gate, raw=raw)
+
+
+def draw_gdn2(B, T, H, dk, dv, dtype="bf16", alpha_mu=4.0, s0_std=None, num_states=None, seed=0,
+              device="cpu", forget=True):
+    """Gated DeltaNet-2 inputs: q, k (L2-normalised), v as for draw_chunk; alpha =
+    sigmoid(N(alpha_mu, 1)) per key channel (None with forget=False); erase and
+    write gates sigmoid(N(0, 1)) per key channel (drawn like beta, one per
+    channel); all gates float32 [B, T, H, dk].  Draw order: q, k, v, erase,
+    write, alpha, S0."""
+    g = _gen(device, seed)
+    dt = _DT[dtype]
+    q = _unit(_normal((B, T, H, dk), g, device)).to(dt)
+    k = _unit(_normal((B, T, H, dk), g, device)).to(dt)
+    v = _normal((B, T, H, dv), g, device).to(dt)
+    erase = torch.sigmoid(_normal((B, T, H, dk), g, device)).to(torch.float32)
+    write = torch.sigmoid(_normal((B, T, H, dk), g, device)).to(torch.float32)
+    alpha = (torch.sigmoid(_normal((B, T, H, dk), g, device, alpha_mu)).to(torch.float32)
+             if forget else None)
+    ns = B if num_states is None else num_states
+    s0 = None
+    if s0_std is not None:
+        s0 = _normal((ns, H, dk, dv), g, device, 0.0, s0_std).to(torch.float32)
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), alpha=alpha,
+                erase=erase.contiguous(), write=write.contiguous(), initial_state=s0)
