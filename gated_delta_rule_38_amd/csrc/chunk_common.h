@@ -84,10 +84,6 @@ __device__ __forceinline__ void store_run(Top* p, const Top* v) {
 }
 
 
-// longest-first order of packed sequences into `order` (num_seqs ints)
-hipError_t launch_order_sequences(const int* cu_seqlens, int num_seqs, int* order,
-                                  hipStream_t stream);
-
 // the pipelined bf16 chunk kernel (chunk_fwd_bf16.hip)
 hipError_t launch_chunk_bf16(const KParams& p, int dk, int dvt, hipStream_t stream);
 bool chunk_bf16_supports(int dvt);

@@ -146,8 +146,13 @@ __device__ __forceinline__ Mma<bf16_t>::F32 gather32<bf16_t>(const bf16_t* p, in
 }
 
 
+// ckpt (may be NULL): the state at the start of every chunk of every unit, and
+// after its last chunk, for the chunk-wise backward.  Unit (seq, h) uses slots
+// slot0 .. slot0 + nch with slot0 = t0 / 64 + 2 seq (t0 its first token), so
+// sequences never share a slot; slot s of head h is the float32 [dk][dv] block
+// at ((s * H + h) * dk * dv).  With p.o == NULL no output is formed.
 template <typename Tin, int DK, int DVT>
-__global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p, float* __restrict__ ckpt) {
     using Top = Tin;
     using L = ChunkLayout<Top, DK, DVT>;
     using M = Mma<Top>;
@@ -349,6 +354,12 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
                 const int st = w + 4 * i;
                 if (st < NST) {
                     const int ct = st / NJT_S, jj = st % NJT_S;
+                    if (ckpt) {
+                        float* cp = ckpt + ((size_t)(wi.t0 / CH + 2 * (long)seq + ch) * H + h) * DK * DV;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            cp[(size_t)(ct * 16 + lg * 4 + e) * DV + col0 + jj * 16 + ln] = S[i][e];
+                    }
                     f32x4 sp;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -539,6 +550,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
             const int ns = (w >= 2) ? 2 : 1;
 #pragma unroll
             for (int jb = 0; jb < NJT; ++jb) {
+                if (!go) break;
                 f32x4 co = oi[jb];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
@@ -577,6 +589,19 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p) {
     }
 
     // ---- final state ----
+    if (ckpt) {
+        float* cp = ckpt + ((size_t)(wi.t0 / CH + 2 * (long)seq + nch) * H + h) * DK * DV;
+#pragma unroll
+        for (int i = 0; i < STW; ++i) {
+            const int st = w + 4 * i;
+            if (st < NST) {
+                const int ct = st / NJT_S, jj = st % NJT_S;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cp[(size_t)(ct * 16 + lg * 4 + e) * DV + col0 + jj * 16 + ln] = S[i][e];
+            }
+        }
+    }
     if (p.sT) {
 #pragma unroll
         for (int i = 0; i < STW; ++i) {
@@ -635,7 +660,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const int* order, hipStream
         (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((chunk_fwd_kernel<Tin, DK, DVT>), dim3((unsigned)grid), dim3(NTH),
-                       Lay::bytes, stream, p);
+                       Lay::bytes, stream, p, a.ckpt);
     return hipGetLastError();
 }
 
@@ -675,7 +700,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
     }
     int dvt = a.dvt > 0 ? a.dvt : plan_chunk_dvt(units, a.dv, a.bf16);
     if (dvt > a.dv) dvt = a.dv;
-    if (a.bf16 && !a.generic && chunk_bf16_supports(dvt)) {
+    if (a.bf16 && !a.generic && !a.ckpt && chunk_bf16_supports(dvt)) {
         KParams p;
         p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.beta = a.beta; p.s0 = a.s0;
         p.o = a.o; p.sT = a.sT; p.cu_seqlens = a.cu_seqlens; p.order = order;

@@ -201,7 +201,8 @@ size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_
     const long tokens = num_seqs > 0 ? (long)T : (long)B * T;
     const int nseq = num_seqs > 0 ? num_seqs : B;
     if (nseq == 0 || H == 0) return 0;
-    return kda::backward_workspace_bytes(tokens, nseq, H, dk, dv);
+    return dtype == KDA_DTYPE_BF16 ? kda::bwd_chunk_workspace_bytes(tokens, nseq, H, dk, dv)
+                                   : kda::backward_workspace_bytes(tokens, nseq, H, dk, dv);
 }
 
 kda_status kda_backward(const void* q, const void* k, const void* v, const float* alpha,
@@ -245,6 +246,9 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
         const void* elems[] = {q, k};
         for (const void* ptr : elems)
             if (!aligned(ptr, es)) return KDA_ERROR_MISALIGNED;
+        // the chunk form (bf16) reads q, k and alpha in pairs of channels
+        if (dtype == KDA_DTYPE_BF16 && (!aligned(q, 8) || !aligned(k, 8) || !aligned(alpha, 8)))
+            return KDA_ERROR_MISALIGNED;
         // v and dout are read as runs of four elements
         if (!aligned(v, 4 * es) || !aligned(dout, 4 * es)) return KDA_ERROR_MISALIGNED;
         const void* words[] = {alpha, beta, dq, dk, dv, dalpha, dbeta};
@@ -288,7 +292,9 @@ kda_status kda_backward(const void* q, const void* k, const void* v, const float
         a.num_seqs = varlen ? num_seqs : 0;
         a.scale = default_scale(scale, dk_dim);
         a.workspace = workspace;
-        return kda::launch_backward(a, stream) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+        const hipError_t e = a.bf16 ? kda::launch_bwd_chunk(a, stream)
+                                    : kda::launch_backward(a, stream);
+        return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
     } catch (...) {
         return KDA_ERROR_HIP;
     }

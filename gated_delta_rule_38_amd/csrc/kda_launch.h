@@ -40,6 +40,7 @@ struct ChunkArgs {
     float scale;
     int dvt;                // value columns per workgroup (0 = choose)
     bool generic;           // bf16 through the generic kernel (A/B checks)
+    float *ckpt = nullptr;  // chunk-start states for the backward (generic kernel), or NULL
 };
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
@@ -50,6 +51,10 @@ constexpr int NOALLOC_MAX_SEQS = 65536;
 // Device address of that array on the device of `stream` (looked up once per
 // device, then reused).  Every call on one device shares the array.
 hipError_t noalloc_order_buffer(hipStream_t stream, int **out);
+
+// longest-first order of packed sequences into `order` (num_seqs ints)
+hipError_t launch_order_sequences(const int *cu_seqlens, int num_seqs, int *order,
+                                  hipStream_t stream);
 
 // value-column tile the planner picks for a given number of units
 int plan_chunk_dvt(int units, int dv, bool bf16);
@@ -98,8 +103,14 @@ struct BwdArgs {
     void *workspace;
 };
 
+// float32 inputs: the token recurrence run backwards over 8-token checkpoints
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 // workspace of launch_backward: the state checkpoints of every unit
 size_t backward_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv);
+// bf16 inputs: the chunk form (a forward pass storing chunk-start states, then
+// the reverse sweep over chunks)
+hipError_t launch_bwd_chunk(const BwdArgs &a, hipStream_t stream);
+// workspace of launch_bwd_chunk: the state at every chunk start (and end) of every unit
+size_t bwd_chunk_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv);
 
 }  // namespace kda

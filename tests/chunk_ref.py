@@ -139,3 +139,81 @@ def gdn2_chunk_forward_unit(q, k, v, alpha, erase, write, s0, scale, bf16_ops=Fa
             S = f32(S)
         o[c0:c0 + n] = O[:n]
     return o, S
+
+
+def chunk_backward_unit(q, k, v, alpha, beta, s0, do, dsT, scale, bf16_ops=False):
+    """Gradients of one unit in the chunk form the HIP backward uses (fp64; the
+    decays referenced to the middle of each chunk as in the forward).
+
+    Per chunk, with the chunk-start states S0 of a forward sweep and dS the
+    gradient of the chunk-end state (from the next chunk, or dS_T):
+      T' = (I + Diag(beta) A)^{-1},  Y = beta X,  U = T' Y
+      dW   = (Pn/Pm) dS;            dU = scale M^T dO + Kc dW
+      dY   = T'^T dU;               dX = beta dY;  dV = dX
+      G    = dY U^T;  dA = -Diag(beta) G (strictly lower);  dM = scale dO U^T (lower)
+      dbeta = rowsum(dY X) - rowsum(G A)           (strictly lower part of G)
+      dQr  = scale dO SP^T + dM Kc;  dKr = -dX SP^T + dA Kc
+      dKc  = U dW^T + dA^T Kr + dM^T Qr
+      dq = dQr P/Pm,  dk = dKr P/Pm + dKc Pm/P
+      dlogP_r = dKr Kr - dKc Kc + dQr Qr  (+ rowsum(dS S_C) at the last row)
+      dalpha_t = (sum_{r >= t} dlogP_r) / alpha_t
+      dS0  = Pn dS + Pm (scale Qr^T dO - Kr^T dX)
+    Returns dq, dk, dv, dalpha, dbeta, dS0."""
+    rnd = bf16 if bf16_ops else (lambda x: x)
+    T_, dk = k.shape
+    dv = v.shape[1]
+    nch = (T_ + C - 1) // C
+    # forward sweep: chunk-start states
+    S = s0.astype(np.float64).copy()
+    starts = []
+    pieces = []
+    for ch in range(nch):
+        c0 = ch * C
+        n = min(C, T_ - c0)
+        Q = np.zeros((C, dk)); K = np.zeros((C, dk)); V = np.zeros((C, dv))
+        Al = np.ones((C, dk)); Be = np.zeros(C); dO = np.zeros((C, dv))
+        Q[:n], K[:n], V[:n], Al[:n], Be[:n], dO[:n] = q[c0:c0 + n], k[c0:c0 + n], \
+            v[c0:c0 + n], alpha[c0:c0 + n], beta[c0:c0 + n], do[c0:c0 + n]
+        P = np.cumprod(Al, axis=0)
+        Pm, Pn = P[31], P[C - 1]
+        Kr, Qr, Kc = K * P / Pm, Q * P / Pm, K * Pm / P
+        A = np.tril(rnd(Kr) @ rnd(Kc).T, -1)
+        M = np.tril(rnd(Qr) @ rnd(Kc).T, 0)
+        Tp = blocked_unit_lower_inverse(np.eye(C) + Be[:, None] * A, rnd)
+        starts.append(S.copy())
+        SP = rnd(Pm[:, None] * S)
+        X = V - rnd(Kr) @ SP
+        U = rnd(Tp) @ rnd(Be[:, None] * X)
+        S = Pn[:, None] * S + (Pn / Pm)[:, None] * (rnd(Kc).T @ rnd(U))
+        pieces.append((n, Q, K, V, Al, Be, dO, P, Pm, Pn, Kr, Qr, Kc, A, M, Tp, SP, X, U))
+    starts.append(S.copy())
+    g_q, g_k, g_v = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    g_a, g_b = np.zeros_like(alpha), np.zeros_like(beta)
+    dS = np.zeros((dk, dv)) if dsT is None else dsT.astype(np.float64).copy()
+    for ch in reversed(range(nch)):
+        n, Q, K, V, Al, Be, dO, P, Pm, Pn, Kr, Qr, Kc, A, M, Tp, SP, X, U = pieces[ch]
+        SC = starts[ch + 1]
+        dW = (Pn / Pm)[:, None] * dS
+        dU = scale * rnd(M).T @ rnd(dO) + rnd(Kc) @ rnd(dW)
+        dY = rnd(Tp).T @ rnd(dU)
+        dX = Be[:, None] * dY
+        G = rnd(dY) @ rnd(U).T
+        dA = -Be[:, None] * np.tril(G, -1)
+        dM = np.tril(scale * rnd(dO) @ rnd(U).T, 0)
+        db = np.sum(dY * X, axis=1) - np.sum(np.tril(G, -1) * A, axis=1)
+        dQr = scale * rnd(dO) @ SP.T + rnd(dM) @ rnd(Kc)
+        dKr = -rnd(dX) @ SP.T + rnd(dA) @ rnd(Kc)
+        dKc = rnd(U) @ rnd(dW).T + rnd(dA).T @ rnd(Kr) + rnd(dM).T @ rnd(Qr)
+        ratio = P / Pm
+        dlogP = dKr * Kr - dKc * Kc + dQr * Qr
+        dlogP[C - 1] += np.sum(dS * SC, axis=1)
+        dloga = np.cumsum(dlogP[::-1], axis=0)[::-1]
+        c0 = ch * C
+        g_q[c0:c0 + n] = (dQr * ratio)[:n]
+        g_k[c0:c0 + n] = (dKr * ratio + dKc / ratio)[:n]
+        g_v[c0:c0 + n] = dX[:n]
+        g_a[c0:c0 + n] = (dloga / Al)[:n]
+        g_b[c0:c0 + n] = db[:n]
+        dSP = scale * rnd(Qr).T @ rnd(dO) - rnd(Kr).T @ rnd(dX)
+        dS = Pn[:, None] * dS + Pm[:, None] * dSP
+    return g_q, g_k, g_v, g_a, g_b, dS

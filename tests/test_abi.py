@@ -328,12 +328,14 @@ def bwd_call(lib, **kw):
 
 
 def test_backward_workspace_size(lib):
-    # checkpoints every 8 tokens (+ one slot per sequence and one spare)
     B, T, H, d = 2, 100, 4, 128
-    slots = (B * T + 7) // 8 + B + 1
-    ck = slots * H * d * d * 4
     r = lambda x: (x + 255) // 256 * 256
-    assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 1) == r(ck)
+    # bf16 (chunk form): the state at every chunk start and end, two spare slots per sequence
+    slots = (B * T) // 64 + 2 * B + 1
+    assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 1) == r(slots * H * d * d * 4)
+    # float32 (token recurrence): checkpoints every 8 tokens (+ one slot per sequence and a spare)
+    slots = (B * T + 7) // 8 + B + 1
+    assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 0) == r(slots * H * d * d * 4)
     assert lib.kda_backward_workspace_size(B, T, H, 96, d, 0, 1) == 0
     assert lib.kda_backward_workspace_size(0, T, H, d, d, 0, 1) == 0
 
@@ -357,6 +359,8 @@ def test_backward_workspace_size(lib):
     (dict(v=fake(2, 2)), MISALIGNED),          # v and dout: runs of four elements
     (dict(do=fake(6, 4)), MISALIGNED),
     (dict(dt=0, v=fake(2, 8)), MISALIGNED),    # 16 bytes for float32
+    (dict(q=fake(0, 4)), MISALIGNED),          # bf16: q, k and alpha in pairs (8 bytes)
+    (dict(alpha=fake(3, 4)), MISALIGNED),
 ])
 def test_backward_rejects_before_any_hip_call(lib, kw, code):
     assert bwd_call(lib, **kw) == code

@@ -1,8 +1,9 @@
 """GPU parity of kda_backward (gradients of the chunk-wise forward) against
 the fp64 oracle's reverse sweep (oracle.backward, itself pinned by central
-differences of the oracle's forward).  The kernel works in fp32 on the
-stored inputs widened exactly, so every case, bf16 storage included, is held
-to the fp32 bound 1e-4 of max |g_gpu - g_ref| / max |g_ref| per gradient."""
+differences of the oracle's forward).  Error: max |g_gpu - g_ref| / max
+|g_ref| per gradient.  bf16 inputs take the chunk form on the matrix cores
+(bf16 operands, fp32 accumulation) and are held to the bf16 bound 2e-2;
+float32 inputs take the token recurrence in fp32 and are held to 1e-4."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +13,7 @@ from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-4
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 NAMES = ["dq", "dk", "dv", "dalpha", "dbeta", "dinitial_state"]
 
 
@@ -59,7 +60,7 @@ def check(kda, d, cu=None):
     errs = {n: rel(g, r) for n, g, r in zip(NAMES, got, ref)}
     print("errors", {n: "%.1e" % e for n, e in errs.items()}, flush=True)
     for n, e in errs.items():
-        assert e <= TOL, (n, e)
+        assert e <= TOL[d["q"].dtype], (n, e)
 
 
 CASES = [
@@ -71,6 +72,9 @@ CASES = [
     ("bf16", 1, 33, 3, 64, 128, 0.1, False),
     ("bf16", 1, 1, 2, 128, 128, 0.5, True),
     ("bf16", 1, 64, 2, 128, 128, None, True),
+    ("bf16", 1, 65, 2, 64, 64, 0.3, True),
+    ("bf16", 2, 190, 3, 128, 64, 0.2, True),
+    ("bf16", 1, 130, 2, 64, 128, 0.2, False),
 ]
 
 
@@ -158,4 +162,4 @@ def test_backward_full_B4_H16_T4096(kda):
     print("B4 H16 T4096 backward, all units:", {n: "%.1e" % e for n, e in errs.items()},
           flush=True)
     for n, e in errs.items():
-        assert e <= TOL, (n, e)
+        assert e <= TOL[torch.bfloat16], (n, e)

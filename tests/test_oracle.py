@@ -515,3 +515,20 @@ def test_step_in_place_matches_copy():
     o2, s3 = oracle.step(q, k, v, a, b, s2, in_place=True)
     assert np.array_equal(o1, o2) and np.array_equal(s1, s3) and np.array_equal(s2, s1)
     assert not np.array_equal(s, s1)  # the copying call left its input alone
+
+
+@pytest.mark.parametrize("T,dk,dv", [(64, 8, 4), (150, 16, 8), (1, 8, 8), (200, 32, 16)])
+def test_backward_chunk_algebra_matches_the_oracle(T, dk, dv):
+    """The chunk decomposition of the gradients the HIP backward uses
+    (tests/chunk_ref.py, fp64) equals the oracle's reverse token sweep."""
+    import chunk_ref
+    rng = np.random.default_rng(90 + T)
+    q, k, v, alpha, beta, s0 = draw(rng, T, dk, dv)
+    alpha = 1.0 / (1.0 + np.exp(-rng.normal(3.0, 1.0, (T, dk))))
+    do = rng.standard_normal((T, dv))
+    dsT = rng.standard_normal((dk, dv))
+    got = chunk_ref.chunk_backward_unit(q, k, v, alpha, beta, s0, do, dsT, 0.6)
+    ref = oracle.backward_units(q[None], k[None], v[None], alpha[None], beta[None], s0[None],
+                                do[None], dsT[None], scale=0.6)
+    for name, g, r in zip(["dq", "dk", "dv", "dalpha", "dbeta", "ds0"], got, ref):
+        assert rel(g, r[0]) < 1e-11, (name, rel(g, r[0]))
