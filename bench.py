@@ -54,10 +54,11 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_38_amd", "csrc")
 CHUNK = 64
 # the sources each timed kernel is compiled from (its counters go stale when any changes)
 KERNEL_SOURCES = {
-    "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "chunk_common.h", "kda_device.h"],
+    "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "chunk_walk.h", "chunk_common.h", "kda_device.h"],
     "recurrent_step_kernel": ["recurrent_step.hip", "kda_device.h"],
-    "backward_kernel": ["backward.hip", "kda_device.h"],
-    "gdn2_chunk_kernel": ["gdn2_chunk.hip", "chunk_common.h", "kda_device.h"],
+    "bwd_chunk_kernel": ["bwd_chunk.hip", "chunk_fwd.hip", "chunk_walk.h", "chunk_common.h",
+                         "kda_device.h"],
+    "gdn2_chunk_kernel": ["gdn2_chunk.hip", "chunk_walk.h", "chunk_common.h", "kda_device.h"],
     "gdn2_step_kernel": ["gdn2_step.hip", "kda_device.h"],
 }
 WORKLOADS = ["headline", "long_context", "varlen", "decode", "backward", "gdn2"]
@@ -153,6 +154,18 @@ def backward_bytes(tokens, H, dk, dv, nstates, es=2):
     once."""
     return (tokens * H * (2 * dk * es + dv * es + dk * 4 + 4 + dv * es
                           + 4 * (2 * dk + dv + dk) + 4) + 3 * nstates * H * dk * dv * 4)
+
+
+def backward_flops(tokens, H, dk, dv, C=CHUNK):
+    """Algorithmic matrix flops of one chunk-form backward call, triangle-aware,
+    per token and head: the forward that stores the chunk-start states
+    (chunk_flops) and the reverse sweep, 14 dk dv (seven state-sized products:
+    Kr SP, Kc dW, dO SP^T, dX SP^T, U dW^T, Qr^T dO, Kr^T dX) + C (6 dk + 5 dv)
+    (A and M again, dM Kc, dA Kc, dA^T Kr, dM^T Qr over the key channels;
+    M^T dO, T'^T dU, T' Y, dY U^T, dO U^T over the value columns, each over
+    half a chunk on average) + 2 C^2 / 3 (the triangular inverse again)."""
+    return (chunk_flops(tokens, H, dk, dv, C)
+            + tokens * H * (14 * dk * dv + C * (6 * dk + 5 * dv) + 2 * C * C / 3))
 
 
 def roofline(bytes_alg, ms, kernel, flops_alg=None):
@@ -404,7 +417,8 @@ def main():
             "workload": "kda_backward bf16 B4 H16 T4096 dk128 dv128 (per-channel gate), "
                         "fp32 gradients",
             "ms_per_step": bms, "tokens_per_s": B * T / (bms / 1e3),
-            "roofline": roofline(backward_bytes(B * T, H, dk, dv, B), bms, "backward_kernel")}
+            "roofline": roofline(backward_bytes(B * T, H, dk, dv, B), bms, "bwd_chunk_kernel",
+                                 backward_flops(B * T, H, dk, dv))}
         del dout, dsT, ws
 
     if run["decode"]:

@@ -37,13 +37,15 @@
 // overlay one another.
 #include <algorithm>
 
-#include "chunk_common.h"
+#include "chunk_walk.h"
 
 namespace kda {
 
 namespace {
 
 constexpr int BW_NTH = 256;
+// half-chunk decay product below which a chunk's gradients are taken token by token
+constexpr float BW_DECAY_FLOOR = 0x1p-12f;
 
 struct BwParams {
     KParams base;          // q, k, v, alpha, beta, cu_seqlens, order, B, T, H, dv, mapping, scale
@@ -148,6 +150,182 @@ __device__ __forceinline__ float row16_total(float x) {
     return x;
 }
 
+// Exact gradients of one chunk, token by token.  The reverse sweep switches to
+// this at the first chunk (from the end) that fails its range check (a
+// half-chunk product of alpha below 2^-12 in some key channel) and keeps it
+// down to the first chunk.  The checkpoints it starts from are exact or as
+// close as the chunk-wise forward (which redoes a unit token by token below
+// 2^-100).  The chain rule through one token's update
+//   S~ = Diag(alpha) S_,  vh = S~^T k,  u = beta (v - vh),  S = S~ + k u^T,  o = scale S^T q
+// with G = dS + scale q do^T (dS the gradient of S) gives
+//   dq = scale S do,  du = G^T k,  dv = beta du,  dbeta = du . (v - vh),
+//   dk = G u - beta S~ du,  dS~ = G - beta k du^T,
+//   dalpha = rowsum(dS~ * S_),  dS_ = Diag(alpha) dS~,
+// taken from the chunk's last token to its first.  The state before each token
+// is recomputed from the chunk-start checkpoint through eight snapshots (one
+// per 8 tokens) kept in LDS.  Thread (rg, c) holds rows rg*RPT.. of column c
+// of the slice; dS enters and leaves in the C-layout tiles of the chunk form.
+template <int DK, int DVT, int STW>
+__device__ __forceinline__ void bw_token_chunk(const BwParams& bp, int seq, int h, long t0, int len,
+                                               int ch, int col0, const float* ckpt, f32x4 (&dS)[STW],
+                                               float* lds) {
+    static_assert(DVT == 32 && BW_NTH == 256, "one 32-column slice over 256 threads");
+    constexpr int NJT = DVT / 16, NST = (DK / 16) * NJT;
+    constexpr int NRG = BW_NTH / DVT;  // 8 row groups
+    constexpr int RPT = DK / NRG;      // rows per thread (16 or 8)
+    constexpr int SNAP = 8;            // tokens per snapshot
+    const KParams& p = bp.base;
+    const int H = p.H, DV = p.dv;
+    const float scale = p.scale;
+    const bf16_t* __restrict__ gq = static_cast<const bf16_t*>(p.q);
+    const bf16_t* __restrict__ gk = static_cast<const bf16_t*>(p.k);
+    const bf16_t* __restrict__ gv = static_cast<const bf16_t*>(p.v);
+    const bf16_t* __restrict__ gdo = static_cast<const bf16_t*>(bp.dout);
+    const float* __restrict__ ga = static_cast<const float*>(p.alpha);
+    const float* __restrict__ gb = p.beta;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, ln = l & 15, lg = l >> 4;
+    const int c = tid % DVT, rg = tid / DVT, r0 = rg * RPT;
+    const int nt = min(CH, len - ch * CH);
+    float* snap = lds;                                     // [CH / SNAP][DK][DVT]
+    float* red = lds + (size_t)(CH / SNAP) * DK * DVT;     // [2][4 waves][DVT][2]
+    int par = 0;
+
+    // C-layout dS -> this thread's rows (through the first snapshot's space)
+    __syncthreads();  // every wave is past its reads of this chunk's LDS
+#pragma unroll
+    for (int i = 0; i < STW; ++i) {
+        const int st = w + 4 * i;
+        if (st < NST) {
+            const int ct = st / NJT, jj = st % NJT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lds[(ct * 16 + lg * 4 + e) * DVT + jj * 16 + ln] = dS[i][e];
+        }
+    }
+    __syncthreads();
+    float G[RPT], S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) G[i] = lds[(r0 + i) * DVT + c];
+
+    // sum of two per-column partials over the row groups (one barrier)
+    auto rows_total = [&](float& x0, float& x1) {
+        x0 += __shfl_xor(x0, 32, 64);
+        x1 += __shfl_xor(x1, 32, 64);
+        float* rb = red + (size_t)par * 4 * DVT * 2;
+        if (l < 32) { rb[(w * DVT + c) * 2] = x0; rb[(w * DVT + c) * 2 + 1] = x1; }
+        __syncthreads();
+        x0 = (rb[c * 2] + rb[(DVT + c) * 2]) + (rb[(2 * DVT + c) * 2] + rb[(3 * DVT + c) * 2]);
+        x1 = (rb[c * 2 + 1] + rb[(DVT + c) * 2 + 1]) + (rb[(2 * DVT + c) * 2 + 1] + rb[(3 * DVT + c) * 2 + 1]);
+        par ^= 1;
+    };
+    // token t of the chunk, forward: S <- S~ + k u^T
+    // (k and alpha are read again where used rather than held: they hit the
+    // cache, and the path keeps few registers)
+    auto fwd = [&](int t) {
+        const size_t tok = (size_t)(t0 + (long)ch * CH + t) * H + h;
+        float pv = 0.f, dummy = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const size_t e = tok * DK + r0 + i;
+            S[i] *= ga[e];
+            pv += to_f32(gk[e]) * S[i];
+        }
+        rows_total(pv, dummy);
+        const float u = gb[tok] * (to_f32(gv[tok * DV + col0 + c]) - pv);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) S[i] += to_f32(gk[tok * DK + r0 + i]) * u;
+    };
+    auto load_state = [&](const float* src, int pitch) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) S[i] = src[(size_t)(r0 + i) * pitch + c];
+    };
+    auto save_snap = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) snap[((size_t)j * DK + r0 + i) * DVT + c] = S[i];
+    };
+
+    // snapshots of the state before tokens 0, 8, 16, .. of the chunk
+    // (snapshot 0 overwrites the dS exchange, which every thread has read)
+    const int nsnap = (nt + SNAP - 1) / SNAP;
+    load_state(ckpt + col0, DV);
+    __syncthreads();
+    for (int j = 0; j < nsnap; ++j) {
+        save_snap(j);
+        if (j + 1 < nsnap)
+            for (int t = j * SNAP; t < (j + 1) * SNAP; ++t) fwd(t);
+    }
+
+    for (int t = nt - 1; t >= 0; --t) {
+        // the state before token t, from its snapshot
+        const int j = t / SNAP;
+        __syncthreads();  // snapshot writes (and the last token's reads) are done
+        load_state(snap + (size_t)j * DK * DVT, DVT);
+        for (int tt = j * SNAP; tt < t; ++tt) fwd(tt);
+
+        const size_t tok = (size_t)(t0 + (long)ch * CH + t) * H + h;
+        const float dov = to_f32(gdo[tok * DV + col0 + c]);
+        const float beta = gb[tok];
+        const float vv = to_f32(gv[tok * DV + col0 + c]);
+        float pv = 0.f, pu = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const size_t e = tok * DK + r0 + i;
+            const float kv = to_f32(gk[e]);
+            G[i] += scale * to_f32(gq[e]) * dov;
+            pv += kv * (ga[e] * S[i]);
+            pu += kv * G[i];
+        }
+        rows_total(pv, pu);  // vh, du
+        const float u = beta * (vv - pv);
+        // per row: the three column sums (over the 32 lanes of a half wave),
+        // added by one lane each
+        for (int i = 0; i < RPT; ++i) {
+            const size_t e = tok * DK + r0 + i;
+            const float al = ga[e], kv = to_f32(gk[e]);
+            const float st = al * S[i];                      // S~
+            const float sn = st + kv * u;                    // the state after token t
+            float gqv = scale * sn * dov;
+            float gkv = G[i] * u - beta * st * pu;
+            const float dst = G[i] - beta * kv * pu;         // dS~
+            float gav = dst * S[i];
+            G[i] = al * dst;
+#pragma unroll
+            for (int off = 1; off < 32; off *= 2) {
+                gqv += __shfl_xor(gqv, off, 64);
+                gkv += __shfl_xor(gkv, off, 64);
+                gav += __shfl_xor(gav, off, 64);
+            }
+            if (c == 0) atomicAdd(bp.dq + e, gqv);
+            else if (c == 1) atomicAdd(bp.dk + e, gkv);
+            else if (c == 2) atomicAdd(bp.dalpha + e, gav);
+        }
+        if (rg == 0) {
+            bp.dv[tok * DV + col0 + c] = beta * pu;
+            float db = pu * (vv - pv);
+#pragma unroll
+            for (int off = 1; off < 32; off *= 2) db += __shfl_xor(db, off, 64);
+            if (c == 0) atomicAdd(bp.dbeta + tok, db);
+        }
+    }
+
+    // this thread's rows of dS -> C-layout tiles
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) lds[(r0 + i) * DVT + c] = G[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < STW; ++i) {
+        const int st = w + 4 * i;
+        if (st < NST) {
+            const int ct = st / NJT, jj = st % NJT;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dS[i][e] = lds[(ct * 16 + lg * 4 + e) * DVT + jj * 16 + ln];
+        }
+    }
+    __syncthreads();  // the next chunk may overwrite this LDS
+}
+
 template <int DK, int DVT>
 __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
     using Top = bf16_t;
@@ -158,6 +336,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
     constexpr int NJT = L::NJT, NST = L::NST, STW = L::STW;
     using R = BwRow<CPT>;
     const KParams& p = bp.base;
+    static_assert((size_t)(8 * DK * DVT + 2 * 4 * DVT * 2) * 4 <= L::bytes, "token-chunk LDS");
 
     extern __shared__ __align__(16) unsigned char smem[];
     Top* sSPr = reinterpret_cast<Top*>(smem + L::oSPr);
@@ -273,6 +452,11 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
         for (int c = 0; c < CPT; ++c) run[c] *= (r < nvalid) ? a[c] : 1.f;
     };
 
+    // The sweep takes the chunk form until a chunk fails the range check; that
+    // chunk and every one before it then go through the token-by-token chain
+    // rule after the loop.  (The chunk form holds all 512 registers of a lane;
+    // the token path placed inside the loop would make it spill.)
+    int token_from = -1;
     for (int ch = nch - 1; ch >= 0; --ch) {
         load_rows(ch);
         load_vdo(ch);
@@ -299,14 +483,36 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
         }
         __syncthreads();  // B1
 
+        // Range check (every wave reads all channels' totals, so all waves
+        // take the same branch).  The backward's bound is tighter than the
+        // forward's: the gradient of the decays sums terms of every pair of
+        // rows, and those of pairs on the same side of a token cancel in exact
+        // arithmetic but leave bf16 rounding behind, which grows with the
+        // decay across the chunk; below a half-chunk product of 2^-12 the
+        // token-by-token path is the accurate one.
+        {
+            bool cbad = false;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const float h1 = sTot[c0 + c] * sTot[DK + c0 + c];
+                const float h2 = sTot[2 * DK + c0 + c] * sTot[3 * DK + c0 + c];
+                cbad |= h1 < BW_DECAY_FLOOR || h2 < BW_DECAY_FLOOR;
+            }
+            if (__builtin_amdgcn_ballot_w64(cbad) != 0) {
+                token_from = ch;
+                break;
+            }
+        }
+
         // ================= phase 1: operands =================================
-        float pre[CPT], ipm[CPT];
+        // P_row / P_31 = (running product inside row block w) * fw with
+        // fw = 1 / (t0 t1), 1 / t1, 1, t2 for w = 0..3 (t_b: row block b's product)
+        float fw[CPT];
         {
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
                 const float t0v = sTot[c0 + c], t1v = sTot[DK + c0 + c], t2v = sTot[2 * DK + c0 + c];
-                pre[c] = (w == 0) ? 1.f : (w == 1) ? t0v : (w == 2) ? t0v * t1v : t0v * t1v * t2v;
-                ipm[c] = fast_rcp(t0v * t1v);
+                fw[c] = (w == 0) ? fast_rcp(t0v * t1v) : (w == 1) ? fast_rcp(t1v) : (w == 2) ? 1.f : t2v;
             }
             float run[CPT];
 #pragma unroll
@@ -323,7 +529,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                 for (int c = 0; c < CPT; ++c) {
                     const float kv = (r < nvalid) ? kx[c] : 0.f;
                     const float qv = (r < nvalid) ? qx[c] : 0.f;
-                    const float ratio = pre[c] * run[c] * ipm[c];
+                    const float ratio = run[c] * fw[c];
                     kr[c] = from_f32<Top>(kv * ratio);
                     qr[c] = from_f32<Top>(qv * ratio);
                     kc[c] = from_f32<Top>(kv * fast_rcp(ratio));
@@ -646,7 +852,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                 for (int c = 0; c < CPT; ++c) {
                     const float kv = (r < nvalid) ? kx[c] : 0.f;
                     const float qv = (r < nvalid) ? qx[c] : 0.f;
-                    const float ratio = pre[c] * run[c] * ipm[c];
+                    const float ratio = run[c] * fw[c];
                     krt[c][r] = from_f32<Top>(kv * ratio);
                     qrt[c][r] = from_f32<Top>(qv * ratio);
                     kct[c][r] = from_f32<Top>(kv * fast_rcp(ratio));
@@ -747,7 +953,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     ac = M::k32(fdmt, fqr, ac);    // dM^T Qr
                 }
                 // P_r / Pm for the lane's four rows: prefix inside the lane, then
-                // the products of the earlier lane groups, the earlier row blocks
+                // the products of the earlier lane groups, the row block's factor
                 float pre4[4];
                 float run = 1.f;
 #pragma unroll
@@ -757,13 +963,13 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                 float excl = (lg >= 1) ? g1 : 1.f;
                 float g2 = __shfl_up(run * excl, 32, 64);  // groups lg-2, lg-3 combined
                 excl = (lg >= 2) ? excl * g2 : excl;
-                float pblk = 1.f;
-                for (int b = 0; b < w; ++b) pblk *= sTot[b * DK + c];
-                const float ipmc = fast_rcp(sTot[c] * sTot[DK + c]);
+                // the factor of row block w: 1 / (t0 t1), 1 / t1, 1, t2
+                const float fwc = (w == 0) ? fast_rcp(sTot[c] * sTot[DK + c])
+                                : (w == 1) ? fast_rcp(sTot[DK + c]) : (w == 2) ? 1.f : sTot[2 * DK + c];
                 float dl[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float ratio = pblk * excl * pre4[e] * ipmc;  // P_r / Pm
+                    const float ratio = fwc * excl * pre4[e];  // P_r / Pm
                     const float irat = fast_rcp(ratio);
                     const float gq = scale * aqo[e] + aq[e];
                     const float gkr = ak[e] - akx[e];
@@ -830,6 +1036,9 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
         }
         __syncthreads();  // B9: LDS reuse by the next chunk
     }
+    for (int ch = token_from; ch >= 0; --ch)
+        bw_token_chunk<DK, DVT, STW>(bp, seq, h, t0, len, ch, col0, ckpt_at(ch), dS,
+                                     reinterpret_cast<float*>(smem));
 
     // ---- the initial state's gradient: this slice's columns ----
 #pragma unroll

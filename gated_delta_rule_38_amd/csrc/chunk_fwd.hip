@@ -17,8 +17,9 @@
 //     O  = scale ((Q*P) S0 + M U),   M_ri = sum_c q_rc k_ic P_rc/P_ic (i<=r)
 //     S_C = Diag(P_63) S0 + (K * P_63/P)^T U.
 // Decay factors are referenced to the middle of the chunk (Pm = P_31) so that
-// the two Gram factors K*P/Pm and K*Pm/P stay within 2^{+-126} as long as
-// alpha's product over any half chunk does:
+// the two Gram factors K*P/Pm and K*Pm/P only span alpha's product over a half
+// chunk (a chunk whose half-chunk product falls below 2^-100 in some channel
+// sends its work item to the exact token walk of chunk_walk.h):
 //     Kr = K*P/Pm, Qr = Q*P/Pm, Kc = K*Pm/P,  A = tril_-1(Kr Kc^T), M = tril(Qr Kc^T)
 //     X = V - Kr (Pm*S0),  OI = Qr (Pm*S0),  U = T X
 //     O = scale (OI + M U),  S_C = Pn*S0 + (Pn/Pm) * (Kc^T U)
@@ -37,7 +38,7 @@
 // columns (decays, Gram matrices, T) is recomputed by every column tile of a
 // unit; tiles of one unit are placed on the same XCD so their shared q, k,
 // alpha reads hit the same L2.
-#include "chunk_common.h"
+#include "chunk_walk.h"
 
 #include <mutex>
 
@@ -82,7 +83,8 @@ struct ChunkLayout {
     static constexpr size_t oLd = oLo + (size_t)CH * LDC * ES;        // fp32 [4][16][LDL]
     static constexpr size_t oTot = oLd + (size_t)4 * 16 * LDL * 4;    // fp32 [4][DK]
     static constexpr size_t oBeta = oTot + (size_t)4 * DK * 4;        // fp32 [64]
-    static constexpr size_t bytes = oBeta + CH * 4;
+    static constexpr size_t oBad = oBeta + CH * 4;                    // u32 [4] out-of-range flags
+    static constexpr size_t bytes = oBad + 16;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -176,6 +178,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p, float* __r
     float* sLd = reinterpret_cast<float*>(smem + L::oLd);
     float* sTot = reinterpret_cast<float*>(smem + L::oTot);
     float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
+    uint32_t* sBad = reinterpret_cast<uint32_t*>(smem + L::oBad);
+    static_assert(WalkShape<DVT, NTH, false>::lds_bytes <= L::oBad, "walk LDS");
 
     const WorkItem wi = decode_work(p);
     if (!wi.valid) return;
@@ -270,6 +274,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p, float* __r
     if (nch > 0) { load_qka(0); load_v(0); }
 
     float pn_s[STW][4], pnm_s[STW][4];  // per owned state tile: Pn and Pn/Pm of its 4 rows
+    bool bad = false;  // a chunk's decays left the chunk form's range (wave 0 checks)
 
     for (int ch = 0; ch < nch; ++ch) {
         // ================= phase 0a: running products inside row block w ======
@@ -300,13 +305,16 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p, float* __r
 
         // ================= phase 0b: decayed operands ==========================
         {
-            float pre[CPT], ipm[CPT];
+            // P_row / P_31 = (running product inside row block w) * fw with
+            // fw = 1 / (t0 t1), 1 / t1, 1, t2 for w = 0..3 (t_b: row block b's
+            // product), which forms no product over more than half a chunk
+            float fw[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
                 const float t0v = sTot[0 * DK + c0 + c], t1v = sTot[1 * DK + c0 + c];
-                const float t2v = sTot[2 * DK + c0 + c];
-                pre[c] = (w == 0) ? 1.f : (w == 1) ? t0v : (w == 2) ? t0v * t1v : t0v * t1v * t2v;
-                ipm[c] = fast_rcp(t0v * t1v);  // 1 / P_31
+                const float t2v = sTot[2 * DK + c0 + c], t3v = sTot[3 * DK + c0 + c];
+                fw[c] = (w == 0) ? fast_rcp(t0v * t1v) : (w == 1) ? fast_rcp(t1v) : (w == 2) ? 1.f : t2v;
+                if (w == 0 && gate != 2) bad |= decay_out_of_range(t0v * t1v, t2v * t3v);
             }
             Top kct[CPT][16];
 #pragma unroll
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p, float* __r
                 for (int c = 0; c < CPT; ++c) {
                     const float kv = (r < nvalid) ? kx[c] : 0.f;
                     const float qv = (r < nvalid) ? qx[c] : 0.f;
-                    const float ratio = pre[c] * pr[r][c] * ipm[c];  // P_row / P_31
+                    const float ratio = pr[r][c] * fw[c];  // P_row / P_31
                     kr[c] = from_f32<Top>(kv * ratio);
                     qr[c] = from_f32<Top>(qv * ratio);
                     kc[c] = from_f32<Top>(kv * fast_rcp(ratio));
@@ -585,6 +593,24 @@ __global__ __launch_bounds__(NTH, 1) void chunk_fwd_kernel(KParams p, float* __r
                         S[i][e] = pn_s[i][e] * S[i][e] + pnm_s[i][e] * acc[e];
                 }
             }
+        }
+    }
+
+    // ---- a work item with a chunk out of range is redone token by token ----
+    {
+        const uint64_t b = __builtin_amdgcn_ballot_w64(bad);
+        __syncthreads();  // every wave is done with the last chunk's LDS
+        if (l == 0) sBad[w] = b != 0;
+        __syncthreads();
+        if (sBad[0] | sBad[1] | sBad[2] | sBad[3]) {
+            WalkArgs wa{};
+            wa.q = p.q; wa.k = p.k; wa.v = p.v; wa.alpha = p.alpha; wa.beta = p.beta;
+            wa.s0 = p.s0; wa.o = p.o; wa.sT = p.sT; wa.ckpt = ckpt;
+            wa.H = H; wa.dv = DV; wa.gate = gate; wa.fuse = p.fuse; wa.scale = p.scale;
+            __threadfence();  // this item's stores so far land before the walk's
+            __syncthreads();
+            token_walk<Tin, DK, DVT, NTH, false>(wa, seq, h, t0, len, col0, reinterpret_cast<float*>(smem));
+            return;
         }
     }
 

@@ -44,7 +44,7 @@
 // range ends with the sequence's last row in the chunk: rows past the end of
 // a sequence lie outside it, so their loads return zero and their stores are
 // dropped.
-#include "chunk_common.h"
+#include "chunk_walk.h"
 
 namespace kda {
 
@@ -283,7 +283,9 @@ struct Lay6 {
     // with in-kernel q/k normalisation: fp32 partial sums of squares
     // [parity][q, k][64 rows][4 producers]
     static constexpr size_t oPart = oD + (size_t)4 * BLK * 2;
-    static constexpr size_t bytes = oPart + (QN ? (size_t)2 * 2 * CH * 4 * 4 : 0);
+    // u32 [4]: a producer's chunks left the chunk form's range
+    static constexpr size_t oBad = oPart + (QN ? (size_t)2 * 2 * CH * 4 * 4 : 0);
+    static constexpr size_t bytes = oBad + 16;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -309,6 +311,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     float* sLd = reinterpret_cast<float*>(smem + L::oLd);
     bf16_t* sD = reinterpret_cast<bf16_t*>(smem + L::oD);
     float* sPart = reinterpret_cast<float*>(smem + L::oPart);
+    uint32_t* sBad = reinterpret_cast<uint32_t*>(smem + L::oBad);
+    static_assert(WalkShape<DVT, L::NTH, false>::lds_bytes <= L::oBad, "walk LDS");
 
     const WorkItem wi = decode_work(p);
     if (!wi.valid) return;
@@ -332,6 +336,26 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     const float* __restrict__ ga = static_cast<const float*>(p.alpha);
     const bf16_t* __restrict__ gg = static_cast<const bf16_t*>(p.alpha);  // gate logits
     const float* __restrict__ gb = p.beta;
+
+    // Every role ends in finish(): one barrier, after which the producers'
+    // flags tell whether a chunk of this work item left the chunk form's range
+    // (half-chunk decay product below 2^-100 in some key channel).  If one did,
+    // redo() recomputes the work item's outputs and final state exactly, token
+    // by token, with every wave of the workgroup.
+    auto finish = [&]() -> bool {
+        __syncthreads();
+        return (sBad[0] | sBad[1] | sBad[2] | sBad[3]) != 0;
+    };
+    auto redo = [&]() {
+        WalkArgs wa{};
+        wa.q = p.q; wa.k = p.k; wa.v = p.v; wa.alpha = p.alpha; wa.beta = p.beta;
+        wa.s0 = p.s0; wa.o = p.o; wa.sT = p.sT; wa.ckpt = nullptr;
+        wa.H = H; wa.dv = DV; wa.gate = GATE; wa.fuse = p.fuse; wa.scale = p.scale;
+        __threadfence();  // this item's stores so far land before the walk's
+        __syncthreads();
+        token_walk<bf16_t, DK, DVT, L::NTH, false>(wa, wi.seq, h, t0, len, jt * DVT,
+                                                   reinterpret_cast<float*>(smem));
+    };
 
     // ---------------------------------------------------------- Gram blocks
     // Blocks (a, b), b <= a, of chunk ch: lane holds A[16a + ln][16b + 4lg + e]
@@ -419,6 +443,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         uint32_t RT[2 * CPL];
 #pragma unroll
         for (int i = 0; i < 2 * CPL; ++i) { R0.q[i] = R0.k[i] = R1.q[i] = R1.k[i] = 0u; RT[i] = 0u; }
+        bool pbad = false;  // a chunk's half-chunk decay product left the range
 #pragma unroll
         for (int i = 0; i < 4 * NAW; ++i) R0.a[i] = R1.a[i] = 0u;
 
@@ -642,6 +667,13 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                     g[c] = fast_rcp(w[c] * f[c]);            // Pm / P through row pr0 + 3
                 }
                 mul_shr4_from(f, w);  // P through row pr0 - 1, over Pm
+                // range check on Pm (row 0) and Pn / Pm (row 3); the scan on
+                // 1 / alpha holds their inverses, which overflow instead
+                if ((lx >> 4) == 0 || (lx >> 4) == 3) {
+#pragma unroll
+                    for (int c = 0; c < NA; ++c)
+                        pbad |= INV ? u[c] > 1.f / DECAY_FLOOR : u[c] < DECAY_FLOOR;
+                }
             }
             // Pm from the first lanes of row 0, Pn / Pm from the first lanes of
             // row 3; the helper forms Pn from the two
@@ -759,6 +791,9 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             step(ch + 1, R0, R1);
         }
         if (ch < nch) step(ch, R1, R0);
+        const uint64_t bad = __builtin_amdgcn_ballot_w64(pbad);
+        if (l == 0) sBad[pw] = bad != 0;
+        if (finish()) redo();
         return;
     }
 
@@ -870,6 +905,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             gram_share(ch + 1, NP);
             __syncthreads();
         }
+        if (finish()) redo();
         return;
     }
 
@@ -932,6 +968,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         }
         asm volatile("" :: "v"(P0[0]), "v"(P0[1]), "v"(P0[2]), "v"(P0[3]), "v"(P1[0]), "v"(P1[1]), "v"(P1[2]),
                      "v"(P1[3]), "v"(P2[0]), "v"(P2[1]), "v"(P2[2]), "v"(P2[3]));
+        if (finish()) redo();
         return;
     }
 
@@ -1118,6 +1155,10 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     }
 
     if (nch > 0) c_out(nch - 1);
+    if (finish()) {
+        redo();
+        return;
+    }
     if (p.sT) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)

@@ -36,7 +36,7 @@
 // separated by workgroup barriers (decays; operands; Gram products and Kr SP,
 // Qr SP; Y and the inverse; the solve; outputs and the state update), with
 // the next chunk's inputs loaded into registers one chunk ahead.
-#include "chunk_common.h"
+#include "chunk_walk.h"
 
 namespace kda {
 
@@ -82,7 +82,8 @@ struct G2Layout {
     static constexpr size_t oAc = oZT + (size_t)DVT * LDC2 * ES;   // [CH][LDC]: L_c
     static constexpr size_t oLo = oAc + (size_t)CH * LDC * ES;     // [CH][LDC]: L_a off-diagonal
     static constexpr size_t oLd = oLo + (size_t)CH * LDC * ES;     // fp32 [4][16][LDL]
-    static constexpr size_t bytes = oLd + (size_t)4 * 16 * LDL * 4;
+    static constexpr size_t oBad = oLd + (size_t)4 * 16 * LDL * 4;   // u32 [4] out-of-range flags
+    static constexpr size_t bytes = oBad + 16;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -137,6 +138,8 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     Top* sAc = reinterpret_cast<Top*>(smem + L::oAc);
     Top* sLo = reinterpret_cast<Top*>(smem + L::oLo);
     float* sLd = reinterpret_cast<float*>(smem + L::oLd);
+    uint32_t* sBad = reinterpret_cast<uint32_t*>(smem + L::oBad);
+    static_assert(WalkShape<DVT, G2_NTH, true>::lds_bytes <= L::oBad, "walk LDS");
     // the decay total of row block b for channel c sits in the 16-byte pad of FT row c
     auto tot = [&](int b, int c) -> float& {
         return reinterpret_cast<float*>(sFT + (size_t)c * LDC2 + 2 * CH)[b];
@@ -220,6 +223,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     if (nch > 0) { load_rows(0); load_v(0); }
 
     float pn_s[STW][4], pnm_s[STW][4];
+    bool bad = false;  // a chunk's decays left the chunk form's range (wave 0 checks)
 
     for (int ch = 0; ch < nch; ++ch) {
         // ================= phase 0a: running products inside row block w ======
@@ -246,12 +250,16 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
 
         // ================= phase 0b: decayed operands ==========================
         {
-            float pre[CPT], ipm[CPT];
+            // P_row / P_31 = (running product inside row block w) * fw with
+            // fw = 1 / (t0 t1), 1 / t1, 1, t2 for w = 0..3 (t_b: row block b's
+            // product): no product over more than half a chunk is formed
+            float fw[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float t0v = tot(0, c0 + c), t1v = tot(1, c0 + c), t2v = tot(2, c0 + c);
-                pre[c] = (w == 0) ? 1.f : (w == 1) ? t0v : (w == 2) ? t0v * t1v : t0v * t1v * t2v;
-                ipm[c] = fast_rcp(t0v * t1v);  // 1 / P_31
+                const float t0v = tot(0, c0 + c), t1v = tot(1, c0 + c);
+                const float t2v = tot(2, c0 + c), t3v = tot(3, c0 + c);
+                fw[c] = (w == 0) ? fast_rcp(t0v * t1v) : (w == 1) ? fast_rcp(t1v) : (w == 2) ? 1.f : t2v;
+                if (w == 0) bad |= decay_out_of_range(t0v * t1v, t2v * t3v);
             }
             Top wct[CPT][16], ect[CPT][16];
 #pragma unroll
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 for (int c = 0; c < CPT; ++c) {
                     const float kv = ok ? kx[c] : 0.f;
                     const float qv = ok ? qx[c] : 0.f;
-                    const float ratio = pre[c] * pr[r][c] * ipm[c];  // P_row / P_31
+                    const float ratio = pr[r][c] * fw[c];  // P_row / P_31
                     const float inv = fast_rcp(ratio);
                     kr[c] = from_f32<Top>(kv * ratio);
                     qr[c] = from_f32<Top>(qv * ratio);
@@ -533,6 +541,26 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                         S[i][e] = pn_s[i][e] * S[i][e] + pnm_s[i][e] * acc[e];
                 }
             }
+        }
+    }
+
+    // ---- a work item with a chunk out of range is redone token by token ----
+    {
+        const uint64_t b = __builtin_amdgcn_ballot_w64(bad);
+        __syncthreads();  // every wave is done with the last chunk's LDS
+        if (l == 0) sBad[w] = b != 0;
+        __syncthreads();
+        if (sBad[0] | sBad[1] | sBad[2] | sBad[3]) {
+            WalkArgs wa{};
+            wa.q = p.q; wa.k = p.k; wa.v = p.v; wa.alpha = p.alpha;
+            wa.erase = gp.erase; wa.write = gp.write;
+            wa.s0 = p.s0; wa.o = p.o; wa.sT = p.sT; wa.ckpt = nullptr;
+            wa.H = H; wa.dv = DV; wa.gate = p.alpha ? 0 : 2; wa.fuse = 0; wa.scale = p.scale;
+            __threadfence();  // this item's stores so far land before the walk's
+            __syncthreads();
+            token_walk<bf16_t, DK, DVT, G2_NTH, true>(wa, seq, h, t0, len, col0,
+                                                      reinterpret_cast<float*>(smem));
+            return;
         }
     }
 

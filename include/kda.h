@@ -33,12 +33,19 @@
  *    The library never prints, throws across the ABI or aborts.
  *  - Thread safety.  Entry points are reentrant.
  *  - Supported shapes.  dk, dv in {64, 128}; chunk_size == 64.
- *  - Numerical domain.  alpha in (0, 1] (alpha = 1 is exact: DeltaNet).  The
- *    chunk-wise kernel scales keys by cumulative decays referenced to the
- *    middle of each 64-token chunk, so the product of alpha over any 32
- *    consecutive tokens of a chunk must stay above 2^-126 per channel
- *    (roughly: mean alpha above 0.066 over a half chunk); beyond that, results
- *    overflow.  The recurrent step has no such limit.  NaN/Inf propagate.
+ *  - Numerical domain.  Any alpha in [0, 1] (alpha = 1 is exact: DeltaNet).
+ *    The chunk-wise kernels scale keys and queries by cumulative decays
+ *    referenced to the middle of each 64-token chunk; a chunk whose product
+ *    of alpha over either half falls below 2^-100 in some key channel would
+ *    leave fp32's range there, so the kernel flags it and recomputes that
+ *    (sequence, head, value-column slice) token by token at the end of the
+ *    same launch, exactly and without ratios of decays.  Such work items run
+ *    one token per step (tens of times slower); the others are unaffected.
+ *    kda_backward (bf16) takes the token path from the last chunk whose
+ *    half-chunk product is below 2^-12 back to the sequence start: the chunk
+ *    form's decay gradient loses accuracy to cancellation as the decay across
+ *    a chunk grows.  The recurrent steps have no such case.  NaN/Inf
+ *    propagate.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -247,10 +254,12 @@ kda_status kda_recurrent_step_fused(const void *q, const void *k, const void *v,
                                     hipStream_t stream);
 
 /*
- * Device workspace (bytes) that kda_backward needs: a checkpoint of the
- * state every 8 tokens of every (sequence, head), (tokens/8 rounded up +
- * sequences + 1) * H * dk * dv * 4 bytes rounded up to 256.  Returns 0 for
- * arguments kda_backward would reject.
+ * Device workspace (bytes) that kda_backward needs: checkpoints of the
+ * float32 state of every (sequence, head).  bf16: one at the start of every
+ * 64-token chunk and one after the last, (tokens/64 + 2 * sequences + 1) *
+ * H * dk * dv * 4 bytes; float32: one every 8 tokens, (tokens/8 rounded up +
+ * sequences + 1) * H * dk * dv * 4 bytes; both rounded up to 256.  Returns
+ * 0 for arguments kda_backward would reject.
  */
 size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                    kda_dtype dtype);
@@ -261,8 +270,13 @@ size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_
  * dL/dalpha, dL/dbeta and dL/dS_0.
  * Source: the chain rule through the four steps of the update ("Kimi Delta
  * Attention", section "KDA 的更新式"; bugfactory.tech news 3610, second to
- * fourth paragraphs) taken token by token in reverse order; the fifth
- * paragraph there names training as the use of the chunk-wise mode.
+ * fourth paragraphs); the fifth paragraph there names training as the use of
+ * the chunk-wise mode.  bf16 inputs: a chunk-wise forward stores the state at
+ * every chunk start, then a reverse sweep over chunks applies the chain rule
+ * to the chunk form on the matrix cores (bf16 operands, fp32 accumulation;
+ * see the numerical domain above for the chunks it takes token by token).
+ * float32 inputs: the token recurrence run backwards from 8-token
+ * checkpoints, in fp32.
  *   q, k, v, alpha, beta, initial_state, B, T, H, dk, dv, dtype, cu_seqlens_*,
  *   num_seqs, scale: as for kda_chunk_fwd (the forward being differentiated)
  *   dout          [B, T, H, dv]  dtype
@@ -280,8 +294,9 @@ size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_
  * T == 0 (or varlen with every sequence empty) is valid: dinitial_state is
  * then dfinal_state (zero if NULL).
  * Determinism: dv and dinitial_state are bitwise reproducible; dq, dk,
- * dalpha and dbeta sum the contributions of the dv/16 column slices of a
- * unit with float atomics, so their last bits can differ from run to run.
+ * dalpha and dbeta sum the contributions of the value-column slices of a
+ * unit (dv/32 for bf16, dv/16 for float32) with float atomics, so their last
+ * bits can differ from run to run.
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const float *alpha,
                         const float *beta, const float *initial_state, const void *dout,
