@@ -430,10 +430,11 @@ def kda_backward_workspace_size(B, T, H, dk, dv, num_seqs, dtype=torch.bfloat16)
 
 
 def kda_backward(q, k, v, alpha, beta, initial_state, dout, dfinal_state=None,
-                 cu_seqlens=None, cu_seqlens_host=None, scale=None, workspace=None):
+                 cu_seqlens=None, cu_seqlens_host=None, scale=None, workspace=None, out=None):
     """Gradients of kda_chunk_fwd (per-channel gate): dout [B, T, H, dv] in the
     dtype of q, dfinal_state [B or N, H, dk, dv] float32 or None.  Returns
-    float32 (dq, dk, dv, dalpha, dbeta, dinitial_state)."""
+    float32 (dq, dk, dv, dalpha, dbeta, dinitial_state), written into ``out``
+    (a tuple of those six tensors, contiguous, float32) when given."""
     lib = load_library()
     dev = q.device
     dt = q.dtype
@@ -465,9 +466,16 @@ def kda_backward(q, k, v, alpha, beta, initial_state, dout, dfinal_state=None,
     if dfinal_state is not None:
         _check(dfinal_state, "dfinal_state", torch.float32, dev, sshape)
     f32 = dict(dtype=torch.float32, device=dev)
-    g = (torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32),
-         torch.empty((B, T, H, dv), **f32), torch.empty((B, T, H, dk), **f32),
-         torch.empty((B, T, H), **f32), torch.empty(sshape, **f32))
+    shapes = ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H, dk), (B, T, H), sshape)
+    if out is not None:
+        g = tuple(out)
+        names = ("dq", "dk", "dv", "dalpha", "dbeta", "dinitial_state")
+        if len(g) != 6:
+            raise ValueError("out holds %d tensors, kda_backward writes 6" % len(g))
+        for x, n, shp in zip(g, names, shapes):
+            _check(x, n, torch.float32, dev, shp)
+    else:
+        g = tuple(torch.empty(shp, **f32) for shp in shapes)
     ws_bytes = int(lib.kda_backward_workspace_size(B, T, H, dk, dv, num_seqs, code))
     if workspace is not None:
         _check(workspace, "workspace", torch.uint8, dev)

@@ -30,9 +30,10 @@
 // Work decomposition as in the forward: one workgroup of four waves owns one
 // (unit, 32-column value slice); the columns of dS evolve independently, so
 // the chain needs no exchange between slices.  dv and dS_0 are each slice's
-// own columns.  dq, dk, dalpha and dbeta sum over the value columns: each
-// slice adds its contribution with float atomics into the zeroed outputs (the
-// slices of a unit share an XCD, so the sums meet in its L2).  A chunk runs in
+// own columns.  dq, dk, dalpha and dbeta sum over the value columns: slice 0
+// writes its part into the outputs and every other slice into a plane of its
+// own in the workspace, each element once; a last pass adds the planes in
+// slice order, so the gradients are the same bit for bit from run to run.  A chunk runs in
 // eight phases separated by workgroup barriers; the LDS regions of the phases
 // overlay one another.
 #include <algorithm>
@@ -53,7 +54,22 @@ struct BwParams {
     const float* ckpt;     // chunk-start states (the forward with checkpoints)
     const float* dsT;      // [units, dk, dv] or NULL
     float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
+    // partial sums of value-column slices 1.. (slice 0 writes the outputs):
+    // slice j's dq, dk, dalpha ([tokens, H, dk] each) and dbeta ([tokens, H],
+    // padded to nb) start at part + (j - 1) * (3 nk + nb)
+    float* part;
+    size_t nk, nb;
 };
+
+// Where value-column slice jt writes its parts of dq, dk, dalpha and dbeta.
+struct GradOut {
+    float *dq, *dk, *da, *db;
+};
+__device__ __forceinline__ GradOut grad_out(const BwParams& bp, int jt) {
+    if (jt == 0) return {bp.dq, bp.dk, bp.dalpha, bp.dbeta};
+    float* b = bp.part + (size_t)(jt - 1) * (3 * bp.nk + bp.nb);
+    return {b, b + bp.nk, b + 2 * bp.nk, b + 3 * bp.nk};
+}
 
 template <int DK, int DVT>
 struct BwLayout {
@@ -188,6 +204,7 @@ __device__ __forceinline__ void bw_token_chunk(const BwParams& bp, int seq, int 
     const int w = tid >> 6, l = tid & 63, ln = l & 15, lg = l >> 4;
     const int c = tid % DVT, rg = tid / DVT, r0 = rg * RPT;
     const int nt = min(CH, len - ch * CH);
+    const GradOut go = grad_out(bp, col0 / DVT);
     float* snap = lds;                                     // [CH / SNAP][DK][DVT]
     float* red = lds + (size_t)(CH / SNAP) * DK * DVT;     // [2][4 waves][DVT][2]
     int par = 0;
@@ -296,16 +313,16 @@ __device__ __forceinline__ void bw_token_chunk(const BwParams& bp, int seq, int 
                 gkv += __shfl_xor(gkv, off, 64);
                 gav += __shfl_xor(gav, off, 64);
             }
-            if (c == 0) atomicAdd(bp.dq + e, gqv);
-            else if (c == 1) atomicAdd(bp.dk + e, gkv);
-            else if (c == 2) atomicAdd(bp.dalpha + e, gav);
+            if (c == 0) go.dq[e] = gqv;
+            else if (c == 1) go.dk[e] = gkv;
+            else if (c == 2) go.da[e] = gav;
         }
         if (rg == 0) {
             bp.dv[tok * DV + col0 + c] = beta * pu;
             float db = pu * (vv - pv);
 #pragma unroll
             for (int off = 1; off < 32; off *= 2) db += __shfl_xor(db, off, 64);
-            if (c == 0) atomicAdd(bp.dbeta + tok, db);
+            if (c == 0) go.db[tok] = db;
         }
     }
 
@@ -396,6 +413,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
     const int c0 = l * CPT;
     const size_t sbase = ((size_t)seq * H + h) * DK * DV;
     const long slot0 = t0 / CH + 2 * (long)seq;
+    const GradOut gout = grad_out(bp, jt);
     auto ckpt_at = [&](int ch) {
         return bp.ckpt + ((size_t)(slot0 + ch) * H + h) * DK * DV;
     };
@@ -977,8 +995,8 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     const int t = ch * CH + rowb + e;
                     if (t < len) {
                         const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                        atomicAdd(bp.dq + off, gq * ratio);
-                        atomicAdd(bp.dk + off, gkr * ratio + gkc * irat);
+                        gout.dq[off] = gq * ratio;
+                        gout.dk[off] = gkr * ratio + gkc * irat;
                     }
                     dl[e] = (gkr * ke[e] + gq * qe[e]) * ratio - gkc * ke[e] * irat;
                 }
@@ -1018,7 +1036,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     const int t = ch * CH + rowb + e;
                     if (t < len) {
                         const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                        atomicAdd(bp.dalpha + off, (dls[ct][e] + later) / ga[off]);
+                        gout.da[off] = (dls[ct][e] + later) / ga[off];
                     }
                 }
             }
@@ -1030,7 +1048,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     const int a = r >> 4;
                     float db = sDb1[r];
                     for (int b = 0; b <= a; ++b) db -= sDb2[(a * (a + 1) / 2 + b) * 16 + (r & 15)];
-                    atomicAdd(bp.dbeta + (size_t)(t0 + t) * H + h, db);
+                    gout.db[(size_t)(t0 + t) * H + h] = db;
                 }
             }
         }
@@ -1053,10 +1071,30 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
     }
 }
 
-__global__ void bw_zero_kernel(float* __restrict__ p, size_t n) {
+// out[i] = ((out[i] + p_1[i]) + p_2[i]) + ..., with p_j = part + (j - 1) * stride:
+// the slices' partial sums added in a fixed order, four elements per thread
+// (n4 float4 groups; out, part and stride keep 16-byte alignment)
+__global__ void bw_sum_planes_kernel(float* __restrict__ out, const float* __restrict__ part,
+                                     size_t n4, size_t stride, int nparts) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+         i += (size_t)gridDim.x * blockDim.x) {
+        float4 acc = reinterpret_cast<const float4*>(out)[i];
+        for (int j = 0; j < nparts; ++j) {
+            const float4 x = reinterpret_cast<const float4*>(part + (size_t)j * stride)[i];
+            acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+        }
+        reinterpret_cast<float4*>(out)[i] = acc;
+    }
+}
+// the same for a length that need not be a multiple of four
+__global__ void bw_sum_planes1_kernel(float* __restrict__ out, const float* __restrict__ part,
+                                      size_t n, size_t stride, int nparts) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0.f;
+         i += (size_t)gridDim.x * blockDim.x) {
+        float acc = out[i];
+        for (int j = 0; j < nparts; ++j) acc += part[(size_t)j * stride + i];
+        out[i] = acc;
+    }
 }
 
 template <int DK>
@@ -1076,9 +1114,18 @@ hipError_t launch_bw(const BwParams& bp, hipStream_t stream) {
 
 }  // namespace
 
-size_t bwd_chunk_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv) {
+// workspace: the checkpoints, then the partial sums of slices 1 .. dv/32 - 1
+static size_t bw_ckpt_bytes(long tokens_total, int nseq, int H, int dk, int dv) {
     const size_t slots = (size_t)(tokens_total / CH) + 2 * (size_t)nseq + 1;
     return (slots * H * dk * dv * 4 + 255) / 256 * 256;
+}
+static size_t bw_nb_padded(long tokens_total, int H) {
+    return ((size_t)tokens_total * H + 63) / 64 * 64;
+}
+
+size_t bwd_chunk_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv) {
+    const size_t nk = (size_t)tokens_total * H * dk, nb = bw_nb_padded(tokens_total, H);
+    return bw_ckpt_bytes(tokens_total, nseq, H, dk, dv) + (size_t)(dv / 32 - 1) * (3 * nk + nb) * 4;
 }
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
@@ -1087,6 +1134,8 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
     if (units == 0) return hipSuccess;
     const long tokens = a.cu_seqlens ? a.T : (long)a.B * a.T;
     float* ckpt = static_cast<float*>(a.workspace);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                           bw_ckpt_bytes(tokens, nseq, a.H, a.dk, a.dv));
     // 1. the forward with a checkpoint of the state at every chunk start
     ChunkArgs f;
     f.q = a.q; f.k = a.k; f.v = a.v; f.alpha = a.alpha; f.beta = a.beta;
@@ -1099,21 +1148,13 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
     f.num_seqs = a.num_seqs;
     f.order = nullptr;
     f.scale = a.scale;
-    f.dvt = 32;
-    f.generic = true;
+    f.dvt = 0;
+    f.generic = false;
     f.ckpt = ckpt;
     hipError_t e = launch_chunk_fwd(f, stream);
     if (e != hipSuccess) return e;
-    // 2. clear the column-summed gradients, then the reverse sweep
-    const size_t nk = (size_t)tokens * a.H * a.dk, nb = (size_t)tokens * a.H;
-    if (nk > 0) {
-        float* zs[] = {a.g_q, a.g_k, a.g_alpha};
-        for (float* z : zs)
-            hipLaunchKernelGGL(bw_zero_kernel, dim3((unsigned)std::min<size_t>((nk + 255) / 256, 4096)),
-                               dim3(256), 0, stream, z, nk);
-        hipLaunchKernelGGL(bw_zero_kernel, dim3((unsigned)std::min<size_t>((nb + 255) / 256, 4096)),
-                           dim3(256), 0, stream, a.g_beta, nb);
-    }
+    // 2. the reverse sweep; every slice writes each of its gradient elements once
+    const size_t nk = (size_t)tokens * a.H * a.dk, nb = bw_nb_padded(tokens, a.H);
     BwParams bp;
     KParams& p = bp.base;
     p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.beta = a.beta; p.s0 = a.s0;
@@ -1126,7 +1167,26 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
     bp.dout = a.dout; bp.ckpt = ckpt; bp.dsT = a.dsT;
     bp.dq = a.g_q; bp.dk = a.g_k; bp.dv = a.g_v; bp.dalpha = a.g_alpha; bp.dbeta = a.g_beta;
     bp.ds0 = a.g_s0;
-    return a.dk == 128 ? launch_bw<128>(bp, stream) : launch_bw<64>(bp, stream);
+    bp.part = part; bp.nk = nk; bp.nb = nb;
+    e = a.dk == 128 ? launch_bw<128>(bp, stream) : launch_bw<64>(bp, stream);
+    if (e != hipSuccess || tokens == 0) return e;
+    // 3. the slices' sums, in slice order
+    const int nparts = a.dv / 32 - 1;
+    const size_t stride = 3 * nk + nb;
+    const unsigned g4 = (unsigned)std::min<size_t>((nk / 4 + 255) / 256, 8192);
+    float* outs[] = {a.g_q, a.g_k, a.g_alpha};
+    for (int i = 0; i < 3; ++i) {
+        if (reinterpret_cast<uintptr_t>(outs[i]) % 16 == 0)
+            hipLaunchKernelGGL(bw_sum_planes_kernel, dim3(g4), dim3(256), 0, stream, outs[i],
+                               part + i * nk, nk / 4, stride, nparts);
+        else  // an output at an odd offset: element by element
+            hipLaunchKernelGGL(bw_sum_planes1_kernel, dim3(4 * g4), dim3(256), 0, stream, outs[i],
+                               part + i * nk, nk, stride, nparts);
+    }
+    const size_t ntb = (size_t)tokens * a.H;
+    hipLaunchKernelGGL(bw_sum_planes1_kernel, dim3((unsigned)std::min<size_t>((ntb + 255) / 256, 4096)),
+                       dim3(256), 0, stream, a.g_beta, part + 3 * nk, ntb, stride, nparts);
+    return hipGetLastError();
 }
 
 }  // namespace kda

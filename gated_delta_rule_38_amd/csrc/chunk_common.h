@@ -23,6 +23,9 @@ struct KParams {
     int gate;  // 0: alpha per key channel, 1: per head (Gated DeltaNet), 2: none (alpha = 1)
     int fuse;  // kda_fuse_flag bits (FUSE_*)
     float scale;
+    // the state at the start of every chunk and after the last one, for the
+    // chunk-form backward (slots as laid out in chunk_fwd.hip), or NULL
+    float *ckpt = nullptr;
 };
 
 struct WorkItem {

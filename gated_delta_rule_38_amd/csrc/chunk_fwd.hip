@@ -726,7 +726,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
     }
     int dvt = a.dvt > 0 ? a.dvt : plan_chunk_dvt(units, a.dv, a.bf16);
     if (dvt > a.dv) dvt = a.dv;
-    if (a.bf16 && !a.generic && !a.ckpt && chunk_bf16_supports(dvt)) {
+    if (a.bf16 && !a.generic && chunk_bf16_supports(dvt)) {
         KParams p;
         p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.beta = a.beta; p.s0 = a.s0;
         p.o = a.o; p.sT = a.sT; p.cu_seqlens = a.cu_seqlens; p.order = order;
@@ -736,6 +736,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
         p.gate = a.gate;
         p.fuse = a.fuse;
         p.scale = a.scale;
+        p.ckpt = a.ckpt;
         return launch_chunk_bf16(p, a.dk, dvt, stream);
     }
     if (a.bf16)

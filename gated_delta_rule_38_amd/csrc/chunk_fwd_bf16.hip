@@ -349,7 +349,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     auto redo = [&]() {
         WalkArgs wa{};
         wa.q = p.q; wa.k = p.k; wa.v = p.v; wa.alpha = p.alpha; wa.beta = p.beta;
-        wa.s0 = p.s0; wa.o = p.o; wa.sT = p.sT; wa.ckpt = nullptr;
+        wa.s0 = p.s0; wa.o = p.o; wa.sT = p.sT; wa.ckpt = p.ckpt;
         wa.H = H; wa.dv = DV; wa.gate = GATE; wa.fuse = p.fuse; wa.scale = p.scale;
         __threadfence();  // this item's stores so far land before the walk's
         __syncthreads();
@@ -988,6 +988,21 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     const size_t sbase = ((size_t)wi.seq * H + h) * DK * DV;
 
     f32x4 S[NT][NCT], Y[NT][4], OI[NT][4];  // state, beta-scaled X, (Qr (Pm S0))^T
+    // this wave's columns of the state into a float32 [dk][dv] block
+    // (lane offsets recomputed per call, so no per-element address stays live)
+    auto store_state = [&](float* dst) {
+        const int lx = (int)opaque((uint32_t)l);
+        float* base = dst + (size_t)(lx >> 4) * 8 * DV + colw + (lx & 15);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    base[(size_t)state_ch(ct, 0, e) * DV + 16 * j] = S[j][ct][e];
+    };
+    const size_t slot0 = (size_t)(t0 / CH + 2 * (long)wi.seq);
+    auto ckpt_at = [&](int ch) { return p.ckpt + ((slot0 + ch) * H + h) * DK * DV; };
     Mf::F16 UP[NT][4];                      // U of the last solved chunk (B operand layout)
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -1006,6 +1021,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // products are taken with their operands swapped, which yields O_a^T: lane
     // (n, g) then holds value columns 4g..4g+3 of token n, one 8-byte store.
     auto c_out = [&](int ch) {
+        if (!go) return;  // a call that only stores checkpoints
         const int lx = (int)opaque((uint32_t)l);
         const int ln = lx & 15, lg = lx >> 4;
         const bf16_t* m_b = reinterpret_cast<const bf16_t*>(buf(ch & 1, L::bM));
@@ -1054,6 +1070,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         {
             const int lx = (int)opaque((uint32_t)l);  // addresses recomputed per chunk
             const int ln = lx & 15, lg = lx >> 4;
+            if (p.ckpt) store_state(ckpt_at(ch));
             if (ch > 0) c_out(ch - 1);
             const bf16_t* kr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bKr));
             const bf16_t* qr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bQr));
@@ -1159,15 +1176,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         redo();
         return;
     }
-    if (p.sT) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    p.sT[sbase + (size_t)state_ch(ct, lg, e) * DV + col + 16 * j] = S[j][ct][e];
-    }
+    if (p.ckpt) store_state(ckpt_at(nch));
+    if (p.sT) store_state(p.sT + sbase);
 }
 
 template <int DK, int DVT, int GATE, int FE>

@@ -254,12 +254,14 @@ kda_status kda_recurrent_step_fused(const void *q, const void *k, const void *v,
                                     hipStream_t stream);
 
 /*
- * Device workspace (bytes) that kda_backward needs: checkpoints of the
- * float32 state of every (sequence, head).  bf16: one at the start of every
- * 64-token chunk and one after the last, (tokens/64 + 2 * sequences + 1) *
- * H * dk * dv * 4 bytes; float32: one every 8 tokens, (tokens/8 rounded up +
- * sequences + 1) * H * dk * dv * 4 bytes; both rounded up to 256.  Returns
- * 0 for arguments kda_backward would reject.
+ * Device workspace (bytes) that kda_backward needs.  bf16: the float32
+ * state of every (sequence, head) at the start of every 64-token chunk and
+ * after the last, (tokens/64 + 2 * sequences + 1) * H * dk * dv * 4 bytes
+ * rounded up to 256, then the partial gradients of value-column slices 1 ..
+ * dv/32 - 1, (dv/32 - 1) * (3 * tokens * H * dk + tokens * H rounded up to
+ * 64) * 4 bytes.  float32: a state checkpoint every 8 tokens, (tokens/8
+ * rounded up + sequences + 1) * H * dk * dv * 4 bytes rounded up to 256.
+ * Returns 0 for arguments kda_backward would reject.
  */
 size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                    kda_dtype dtype);
@@ -293,9 +295,11 @@ size_t kda_backward_workspace_size(int B, int T, int H, int dk, int dv, int num_
  * overlap inputs, each other or the workspace.  Errors as for kda_chunk_fwd.
  * T == 0 (or varlen with every sequence empty) is valid: dinitial_state is
  * then dfinal_state (zero if NULL).
- * Determinism: dv and dinitial_state are bitwise reproducible; dq, dk,
- * dalpha and dbeta sum the contributions of the value-column slices of a
- * unit (dv/32 for bf16, dv/16 for float32) with float atomics, so their last
+ * Determinism: bf16 gradients are bitwise reproducible (each of the dv/32
+ * value-column slices of a unit writes its part of dq, dk, dalpha and dbeta
+ * into a workspace plane of its own, and the planes are added in slice
+ * order).  float32: dv and dinitial_state are reproducible; dq, dk, dalpha
+ * and dbeta sum the dv/16 slices' parts with float atomics, so their last
  * bits can differ from run to run.
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const float *alpha,

@@ -330,9 +330,15 @@ def bwd_call(lib, **kw):
 def test_backward_workspace_size(lib):
     B, T, H, d = 2, 100, 4, 128
     r = lambda x: (x + 255) // 256 * 256
-    # bf16 (chunk form): the state at every chunk start and end, two spare slots per sequence
+    # bf16 (chunk form): the state at every chunk start and end, two spare slots per
+    # sequence; then, for each value-column slice but the first (dv / 32 of them),
+    # its partial dq, dk, dalpha (tokens * H * dk each) and dbeta (tokens * H,
+    # padded to 64) in float32
     slots = (B * T) // 64 + 2 * B + 1
-    assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 1) == r(slots * H * d * d * 4)
+    nk, nb = B * T * H * d, (B * T * H + 63) // 64 * 64
+    for dv in (64, 128):
+        assert lib.kda_backward_workspace_size(B, T, H, d, dv, 0, 1) == (
+            r(slots * H * d * dv * 4) + (dv // 32 - 1) * (3 * nk + nb) * 4)
     # float32 (token recurrence): checkpoints every 8 tokens (+ one slot per sequence and a spare)
     slots = (B * T + 7) // 8 + B + 1
     assert lib.kda_backward_workspace_size(B, T, H, d, d, 0, 0) == r(slots * H * d * d * 4)

@@ -129,6 +129,39 @@ def test_backward_no_tokens(kda):
     assert torch.equal(got[5], d["dsT"])
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_bitwise_reproducible(kda, dt):
+    """Two calls on the same inputs give the same gradients bit for bit (bf16:
+    the value-column slices' partial sums are added in a fixed order)."""
+    d = grads_inputs(dt, 2, 300 if dt == "bf16" else 70, 3, 128, 128, 0.1, True, seed=801)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"], d["dout"], d["dsT"])
+    a = kda.kda_backward(*args)
+    b = kda.kda_backward(*args)
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, a, b):
+        if dt == "bf16" or n in ("dv", "dinitial_state"):
+            assert torch.equal(x, y), n
+
+
+def test_backward_outputs_at_odd_offsets(kda):
+    """Gradient tensors that start 4 bytes past a 16-byte boundary (views into
+    larger buffers): the same values as freshly allocated outputs."""
+    d = grads_inputs("bf16", 1, 150, 2, 128, 128, 0.1, True, seed=803)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"], d["dout"], d["dsT"])
+    ref = kda.kda_backward(*args)
+    out = []
+    for i, x in enumerate(ref):
+        if i == 5:  # the state gradient keeps its 16-byte alignment
+            out.append(torch.empty_like(x))
+        else:
+            buf = torch.empty(x.numel() + 1, dtype=torch.float32, device=dev())
+            out.append(buf[1:].view(x.shape))
+    got = kda.kda_backward(*args, out=tuple(out))
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, got, ref):
+        assert torch.equal(x, y), n
+
+
 def test_backward_full_B4_H16_T4096(kda):
     """The benchmarked backward call (bf16 B4 H16 T4096 d128, S0 ~ N(0, 0.02),
     random dL/do and dL/dS_T): every (batch, head) unit compared with the
