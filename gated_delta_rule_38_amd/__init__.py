@@ -55,50 +55,54 @@ def load_library():
         if not os.path.exists(LIB_PATH):
             raise ImportError("libkda.so not found at %s; build it first "
                               "(python -c 'import __graft_entry__ as g; g.build()')" % LIB_PATH)
-        lib = ctypes.CDLL(LIB_PATH)
-        vp, fp = ctypes.c_void_p, ctypes.c_void_p
-        ip = ctypes.POINTER(ctypes.c_int)
-        i, f, sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        lib.kda_chunk_fwd.restype = i
-        lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
-                                      vp, ip, i, f, i, vp, sz, vp]
-        lib.kda_chunk_fwd_gated.restype = i
-        lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, i,
-                                            vp, ip, i, f, i, vp, sz, vp]
-        lib.kda_chunk_fwd_noalloc.restype = i
-        lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
-                                              vp, ip, i, f, i, vp]
-        lib.kda_gdn2_chunk_fwd.restype = i
-        lib.kda_gdn2_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
-                                           vp, ip, i, f, i, vp, sz, vp]
-        lib.kda_gdn2_recurrent_step.restype = i
-        lib.kda_gdn2_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, f,
-                                                vp]
-        lib.kda_recurrent_step.restype = i
-        lib.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, vp]
-        lib.kda_recurrent_step_gated.restype = i
-        lib.kda_recurrent_step_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i,
-                                                 f, vp]
-        u = ctypes.c_uint
-        lib.kda_chunk_fwd_fused.restype = i
-        lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i,
-                                            u, vp, ip, i, f, i, vp, sz, vp]
-        lib.kda_recurrent_step_fused.restype = i
-        lib.kda_recurrent_step_fused.argtypes = [vp, vp, vp, vp, fp, fp, vp, i, i, i, i, i, i,
-                                                 u, f, vp]
-        lib.kda_backward.restype = i
-        lib.kda_backward.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
-                                     i, i, i, i, i, i, vp, ip, i, f, vp, sz, vp]
-        lib.kda_backward_workspace_size.restype = sz
-        lib.kda_backward_workspace_size.argtypes = [i, i, i, i, i, i, i]
-        lib.kda_chunk_fwd_workspace_size.restype = sz
-        lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
-        lib.kda_status_string.restype = ctypes.c_char_p
-        lib.kda_status_string.argtypes = [i]
-        lib.kda_version.restype = i
-        lib.kda_version.argtypes = []
-        _lib = lib
+        _lib = _bind_signatures(ctypes.CDLL(LIB_PATH))
     return _lib
+
+
+def _bind_signatures(lib):
+    """Argument and result types of every entry point of kda.h on ``lib``."""
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    i, f, sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
+                                  vp, ip, i, f, i, vp, sz, vp]
+    lib.kda_chunk_fwd_gated.restype = i
+    lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, i,
+                                        vp, ip, i, f, i, vp, sz, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
+                                          vp, ip, i, f, i, vp]
+    lib.kda_gdn2_chunk_fwd.restype = i
+    lib.kda_gdn2_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp, i, i, i, i, i, i,
+                                       vp, ip, i, f, i, vp, sz, vp]
+    lib.kda_gdn2_recurrent_step.restype = i
+    lib.kda_gdn2_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, f,
+                                            vp]
+    lib.kda_recurrent_step.restype = i
+    lib.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, vp]
+    lib.kda_recurrent_step_gated.restype = i
+    lib.kda_recurrent_step_gated.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i,
+                                             f, vp]
+    u = ctypes.c_uint
+    lib.kda_chunk_fwd_fused.restype = i
+    lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i,
+                                        u, vp, ip, i, f, i, vp, sz, vp]
+    lib.kda_recurrent_step_fused.restype = i
+    lib.kda_recurrent_step_fused.argtypes = [vp, vp, vp, vp, fp, fp, vp, i, i, i, i, i, i,
+                                             u, f, vp]
+    lib.kda_backward.restype = i
+    lib.kda_backward.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                 i, i, i, i, i, i, vp, ip, i, f, vp, sz, vp]
+    lib.kda_backward_workspace_size.restype = sz
+    lib.kda_backward_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_version.restype = i
+    lib.kda_version.argtypes = []
+    return lib
 
 
 def kda_status_string(status):

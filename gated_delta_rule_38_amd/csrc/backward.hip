@@ -364,11 +364,6 @@ hipError_t launch_bwd_dt(const BwdParams& p, int dk, int dv, long tokens, hipStr
 
 }  // namespace
 
-size_t backward_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv) {
-    const size_t slots = (size_t)((tokens_total + BBLK - 1) / BBLK + nseq + 1);
-    return (slots * H * dk * dv * 4 + 255) / 256 * 256;
-}
-
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int nseq = a.cu_seqlens ? a.num_seqs : a.B;
     const int units = nseq * a.H;

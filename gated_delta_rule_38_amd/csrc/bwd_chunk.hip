@@ -1114,20 +1114,6 @@ hipError_t launch_bw(const BwParams& bp, hipStream_t stream) {
 
 }  // namespace
 
-// workspace: the checkpoints, then the partial sums of slices 1 .. dv/32 - 1
-static size_t bw_ckpt_bytes(long tokens_total, int nseq, int H, int dk, int dv) {
-    const size_t slots = (size_t)(tokens_total / CH) + 2 * (size_t)nseq + 1;
-    return (slots * H * dk * dv * 4 + 255) / 256 * 256;
-}
-static size_t bw_nb_padded(long tokens_total, int H) {
-    return ((size_t)tokens_total * H + 63) / 64 * 64;
-}
-
-size_t bwd_chunk_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv) {
-    const size_t nk = (size_t)tokens_total * H * dk, nb = bw_nb_padded(tokens_total, H);
-    return bw_ckpt_bytes(tokens_total, nseq, H, dk, dv) + (size_t)(dv / 32 - 1) * (3 * nk + nb) * 4;
-}
-
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
     const int nseq = a.cu_seqlens ? a.num_seqs : a.B;
     const int units = nseq * a.H;
@@ -1135,7 +1121,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
     const long tokens = a.cu_seqlens ? a.T : (long)a.B * a.T;
     float* ckpt = static_cast<float*>(a.workspace);
     float* part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
-                                           bw_ckpt_bytes(tokens, nseq, a.H, a.dk, a.dv));
+                                           bwd_chunk_ckpt_bytes(tokens, nseq, a.H, a.dk, a.dv));
     // 1. the forward with a checkpoint of the state at every chunk start
     ChunkArgs f;
     f.q = a.q; f.k = a.k; f.v = a.v; f.alpha = a.alpha; f.beta = a.beta;
@@ -1154,7 +1140,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = launch_chunk_fwd(f, stream);
     if (e != hipSuccess) return e;
     // 2. the reverse sweep; every slice writes each of its gradient elements once
-    const size_t nk = (size_t)tokens * a.H * a.dk, nb = bw_nb_padded(tokens, a.H);
+    const size_t nk = (size_t)tokens * a.H * a.dk, nb = bwd_chunk_beta_rows(tokens, a.H);
     BwParams bp;
     KParams& p = bp.base;
     p.q = a.q; p.k = a.k; p.v = a.v; p.alpha = a.alpha; p.beta = a.beta; p.s0 = a.s0;

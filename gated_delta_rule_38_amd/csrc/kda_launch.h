@@ -105,12 +105,19 @@ struct BwdArgs {
 
 // float32 inputs: the token recurrence run backwards over 8-token checkpoints
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
-// workspace of launch_backward: the state checkpoints of every unit
-size_t backward_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv);
 // bf16 inputs: the chunk form (a forward pass storing chunk-start states, then
 // the reverse sweep over chunks)
 hipError_t launch_bwd_chunk(const BwdArgs &a, hipStream_t stream);
-// workspace of launch_bwd_chunk: the state at every chunk start (and end) of every unit
+
+// Workspace layouts (kda_sizes.cpp, host code only).
+// launch_backward: the state every 8 tokens of every unit
+size_t backward_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv);
+// launch_bwd_chunk: the state at every chunk start and end of every unit
+// (bwd_chunk_ckpt_bytes, 256-byte multiple), then for each value-column slice
+// but the first its partial dq, dk, dalpha and dbeta, the last padded to
+// bwd_chunk_beta_rows floats
+size_t bwd_chunk_ckpt_bytes(long tokens_total, int nseq, int H, int dk, int dv);
+size_t bwd_chunk_beta_rows(long tokens_total, int H);
 size_t bwd_chunk_workspace_bytes(long tokens_total, int nseq, int H, int dk, int dv);
 
 }  // namespace kda

@@ -10,17 +10,21 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
-LIB = os.path.join(ROOT, "gated_delta_rule_38_amd", "libkda.so")
+# a host-only build of the argument checks may stand in (tests/test_sanitize.py)
+STAND_IN = os.environ.get("KDA_ABI_TEST_LIBRARY")
+LIB = STAND_IN or os.path.join(ROOT, "gated_delta_rule_38_amd", "libkda.so")
 
 SUCCESS, INVALID, NOT_SUPPORTED, MISALIGNED, WORKSPACE, HIP = range(6)
 
 
 @pytest.fixture(scope="module")
 def lib():
+    import gated_delta_rule_38_amd as kda
+    if STAND_IN:
+        return kda._bind_signatures(ctypes.CDLL(STAND_IN))
     if not os.path.exists(LIB):
         import __graft_entry__
         __graft_entry__.build()
-    import gated_delta_rule_38_amd as kda
     return kda.load_library()
 
 
@@ -393,3 +397,82 @@ def test_python_binding_checks_arguments():
     with pytest.raises(TypeError):  # gate logits come in the dtype of q (bf16 here)
         qb = q.to(torch.bfloat16)
         kda.kda_chunk_fwd_fused(qb, qb, qb, q, b)
+
+
+# ------------------------------------------------------- Gated DeltaNet-2
+
+def gdn2_chunk_call(lib, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), erase=fake(4), write=fake(9),
+             s0=fake(5), o=fake(6), sT=fake(7), B=2, T=100, H=4, dk=128, dv=128, dt=1,
+             cu_dev=None, cu_host=None, num_seqs=0, scale=0.0, chunk=64, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.kda_gdn2_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["erase"], a["write"],
+                                  a["s0"], a["o"], a["sT"], a["B"], a["T"], a["H"], a["dk"],
+                                  a["dv"], a["dt"], a["cu_dev"], a["cu_host"], a["num_seqs"],
+                                  a["scale"], a["chunk"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def gdn2_step_call(lib, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), alpha=fake(3), erase=fake(4), write=fake(9),
+             state=fake(5), o=fake(6), N=8, H=4, dk=128, dv=128, dt=1, scale=0.0, stream=None)
+    a.update(kw)
+    return lib.kda_gdn2_recurrent_step(a["q"], a["k"], a["v"], a["alpha"], a["erase"],
+                                       a["write"], a["state"], a["o"], a["N"], a["H"], a["dk"],
+                                       a["dv"], a["dt"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(dt=0), NOT_SUPPORTED),             # the chunk kernel takes bf16 q, k, v only
+    (dict(dk=96), NOT_SUPPORTED),
+    (dict(chunk=32), NOT_SUPPORTED),
+    (dict(erase=None), INVALID),
+    (dict(write=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(erase=fake(4, 4)), MISALIGNED),    # the gates are read in pairs of channels
+    (dict(write=fake(9, 4)), MISALIGNED),
+    (dict(alpha=fake(3, 4)), MISALIGNED),
+    (dict(q=fake(0, 4)), MISALIGNED),
+    (dict(o=fake(4, 64)), INVALID),          # output inside the erase gate
+    (dict(sT=fake(9, 256)), INVALID),        # final state inside the write gate
+    (dict(sT=fake(5, 256)), INVALID),        # partial overlap with the initial state
+    (dict(cu_dev=fake(8)), INVALID),         # cu_seqlens without num_seqs
+    (dict(B=1, T=10, num_seqs=2, cu_dev=fake(8), cu_host=host_cu([0, 4, 9])), INVALID),
+    (dict(B=1, T=10, num_seqs=2, cu_dev=fake(8), cu_host=host_cu([0, 6, 5])), INVALID),
+])
+def test_gdn2_chunk_rejects_before_any_hip_call(lib, kw, code):
+    assert gdn2_chunk_call(lib, **kw) == code
+
+
+def test_gdn2_chunk_workspace_and_empty(lib):
+    # packed sequences need the workspace of kda_chunk_fwd
+    cu = host_cu([0, 4, 10])
+    assert gdn2_chunk_call(lib, B=1, T=10, num_seqs=2, cu_dev=fake(8), cu_host=cu) == WORKSPACE
+    # no forget gate is allowed; no units is a no-op
+    assert gdn2_chunk_call(lib, alpha=None, H=0) == SUCCESS
+    assert gdn2_chunk_call(lib, B=0) == SUCCESS
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), INVALID),
+    (dict(N=-1), INVALID),
+    (dict(dv=32), NOT_SUPPORTED),
+    (dict(erase=None), INVALID),
+    (dict(write=None), INVALID),
+    (dict(state=None), INVALID),
+    (dict(state=fake(5, 8)), MISALIGNED),    # the state is read as float4
+    (dict(erase=fake(4, 2)), MISALIGNED),
+    (dict(write=fake(9, 2)), MISALIGNED),
+    (dict(dt=0, q=fake(0, 2)), MISALIGNED),  # float32 q: 4-byte elements
+    (dict(o=fake(5, 1024)), INVALID),        # output inside the state
+    (dict(state=fake(4, 0)), INVALID),       # state aliasing the erase gate
+])
+def test_gdn2_step_rejects_before_any_hip_call(lib, kw, code):
+    assert gdn2_step_call(lib, **kw) == code
+
+
+def test_gdn2_step_empty_is_a_noop(lib):
+    assert gdn2_step_call(lib, N=0) == SUCCESS
+    assert gdn2_step_call(lib, H=0, alpha=None) == SUCCESS
