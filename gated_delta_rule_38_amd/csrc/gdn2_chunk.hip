@@ -20,7 +20,9 @@
 // the state update are 128-deep products over the stacked rows F = [C~; A~]
 // and Z = [V; -Pred].  As in the KDA kernels, decays are referenced to the
 // middle of the chunk (Pm = P_31) so that both factors of every Gram product
-// stay within 2^{+-126} while alpha's product over half a chunk does:
+// span alpha's product over half a chunk only (a chunk where that product
+// falls below 2^-100 in some channel sends its work item to the exact token
+// walk of chunk_walk.h):
 //     Kr = K*P/Pm, Qr = Q*P/Pm, Ec = (e.K)*Pm/P, Wc = (w.K)*Pm/P,  SP = Pm*S0
 //     Y = Kr SP + tril_-1(Kr Wc^T) V,  Pred = (I + tril_-1(Kr Ec^T))^{-1} Y
 //     O = scale (Qr SP + [tril(Qr Wc^T) | tril(Qr Ec^T)] Z)
