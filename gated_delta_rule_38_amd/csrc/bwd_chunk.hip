@@ -478,6 +478,24 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
     for (int ch = nch - 1; ch >= 0; --ch) {
         load_rows(ch);
         load_vdo(ch);
+        // the chunk's start and end states, issued after the rows (phase 0 waits
+        // for those only) and used in phase 1
+        float s0v[STW][4], scv[STW][4];
+        {
+            const float* s0p = ckpt_at(ch);
+            const float* scp = ckpt_at(ch + 1);
+#pragma unroll
+            for (int i = 0; i < STW; ++i) {
+                const int st = w + 4 * i;
+                const int ct = st / NJT, jj = st % NJT;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const size_t si = (size_t)(ct * 16 + lg * 4 + e) * DV + col0 + jj * 16 + ln;
+                    s0v[i][e] = st < NST ? s0p[si] : 0.f;
+                    scv[i][e] = st < NST ? scp[si] : 0.f;
+                }
+            }
+        }
         // ================= phase 0: running products inside row block w ======
         typename R::B cq[16], ck[16];
         typename R::F ca[16];
@@ -558,8 +576,6 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
             }
             // SP = Pm S0 (both layouts), dW = (Pn/Pm) dS (both layouts), and the
             // slice's part of rowsum(dS S_C) for the last row's decay
-            const float* s0p = ckpt_at(ch);
-            const float* scp = ckpt_at(ch + 1);
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
                 const int st = w + 4 * i;
@@ -570,13 +586,12 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int c = ct * 16 + lg * 4 + e;
-                        const size_t si = (size_t)c * DV + col0 + jj * 16 + ln;
                         const float a0 = sTot[c], a1 = sTot[DK + c];
                         const float a2 = sTot[2 * DK + c], a3 = sTot[3 * DK + c];
                         const float pm = a0 * a1;
-                        sp[e] = pm * s0p[si];
+                        sp[e] = pm * s0v[i][e];
                         dw[e] = a2 * a3 * dS[i][e];
-                        dl[e] = row16_total(dS[i][e] * scp[si]);
+                        dl[e] = row16_total(dS[i][e] * scv[i][e]);
                     }
                     M::st4(sSPT + (jj * 16 + ln) * LDK + ct * 16 + lg * 4, sp);
                     M::st4(sdWT + (jj * 16 + ln) * LDK + ct * 16 + lg * 4, dw);
@@ -917,20 +932,32 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                 }
             }
             const int rowb = w * 16 + lg * 4;
+            // alpha, k and q of an element block in this layout (L2-resident: loaded in
+            // phase 0), read one block ahead of their use
+            float na[4], nk[4], nq[4];
+            auto ld_block = [&](int ct) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = min(ch * CH + rowb + e, len - 1);
+                    const size_t off = ((size_t)(t0 + t) * H + h) * DK + ct * 16 + ln;
+                    na[e] = ga[off];
+                    nk[e] = to_f32(gk[off]);
+                    nq[e] = to_f32(gq[off]);
+                }
+            };
+            ld_block(0);
 #pragma unroll
             for (int ct = 0; ct < DK / 16; ++ct) {
                 const int c = ct * 16 + ln;
-                // inputs of this element block (L2-resident: loaded in phase 0)
                 float ae[4], ke[4], qe[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = ch * CH + rowb + e;
-                    const bool ok = t < len;
-                    const size_t off = ((size_t)(t0 + min(t, len - 1)) * H + h) * DK + c;
-                    ae[e] = ok ? ga[off] : 1.f;
-                    ke[e] = ok ? to_f32(gk[off]) : 0.f;
-                    qe[e] = ok ? to_f32(gq[off]) : 0.f;
+                    const bool ok = ch * CH + rowb + e < len;
+                    ae[e] = ok ? na[e] : 1.f;
+                    ke[e] = ok ? nk[e] : 0.f;
+                    qe[e] = ok ? nq[e] : 0.f;
                 }
+                if (ct + 1 < DK / 16) ld_block(ct + 1);
                 f32x4 aq = zero4(), ak = zero4(), ac = zero4(), aqo = zero4(), akx = zero4();
                 // contractions over the slice's value columns
 #pragma unroll
@@ -1021,6 +1048,15 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
         // ================= phase 7: dalpha (suffix across row blocks), dbeta ==
         {
             const int rowb = w * 16 + lg * 4;
+            // alpha of the lane's elements, read before the barrier below
+            float av[DK / 16][4];
+#pragma unroll
+            for (int ct = 0; ct < DK / 16; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = min(ch * CH + rowb + e, len - 1);
+                    av[ct][e] = ga[((size_t)(t0 + t) * H + h) * DK + ct * 16 + ln];
+                }
             if (lg == 0) {  // block totals: the suffix at the block's first row
 #pragma unroll
                 for (int ct = 0; ct < DK / 16; ++ct) sTot[w * DK + ct * 16 + ln] = dls[ct][0];
@@ -1036,7 +1072,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     const int t = ch * CH + rowb + e;
                     if (t < len) {
                         const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                        gout.da[off] = (dls[ct][e] + later) / ga[off];
+                        gout.da[off] = (dls[ct][e] + later) / av[ct][e];
                     }
                 }
             }
