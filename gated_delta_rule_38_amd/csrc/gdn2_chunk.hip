@@ -198,10 +198,14 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     typename R::F pa[16], pe[16], pw[16];
     bf16_t pv[NJT][4];
     const int c0 = l * CPT;
-    auto load_rows = [&](int ch) {
+    // rows 4 part .. 4 part + 3 of the row block: the loads of the next chunk go
+    // out in four parts, at the end of the operand build and after each of the
+    // barriers B2..B4, where they overlap matrix-core work instead of stalling
+    // the operand build on their issue (80 load instructions per lane and chunk)
+    auto load_rows = [&](int ch, int part) {
         const int base_r = ch * CH + w * 16;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 4 * part; r < 4 * part + 4; ++r) {
             const int t = min(base_r + r, len - 1);  // rows past the end are replaced when used
             const size_t off = ((size_t)(t0 + t) * H + h) * DK + c0;
             pq[r] = R::ldb(gq + off);
@@ -222,7 +226,11 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     };
 
     const int nch = (len + CH - 1) / CH;
-    if (nch > 0) { load_rows(0); load_v(0); }
+    if (nch > 0) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) load_rows(0, part);
+        load_v(0);
+    }
 
     float pn_s[STW][4], pnm_s[STW][4];
     bool bad = false;  // a chunk's decays left the chunk form's range (wave 0 checks)
@@ -326,8 +334,9 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 }
             }
         }
-        if (ch + 1 < nch) load_rows(ch + 1);
+        if (ch + 1 < nch) load_rows(ch + 1, 0);
         __syncthreads();  // B2
+        if (ch + 1 < nch) load_rows(ch + 1, 1);
 
         // ================= phase 1: Gram blocks, X = Kr SP and OI = Qr SP =====
         f32x4 xr[NJT], oi[NJT];
@@ -392,6 +401,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
         }
         if (ch + 1 < nch) load_v(ch + 1);
         __syncthreads();  // B3
+        if (ch + 1 < nch) load_rows(ch + 1, 2);
 
         // ================= phase 2: Y = X + L_c V, T = (I + L_a)^{-1} ===========
         {
@@ -479,6 +489,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
             }
         }
         __syncthreads();  // B4
+        if (ch + 1 < nch) load_rows(ch + 1, 3);
 
         // ================= phase 3: Pred = T Y, stored as -Pred^T in Z ==========
         {
