@@ -294,7 +294,10 @@ struct Lay6 {
 // FE: in-kernel input preparation, FUSE_GATE_LOGITS (bf16 logits z in place
 // of alpha, alpha = sigmoid(z)) and FUSE_QK_L2NORM (q, k normalised per
 // token); beta logits (FUSE_BETA_LOGITS) are a run-time flag.
-template <int DK, int DVT, int GATE, int FE>
+// CKPT: the instance for the backward, which stores the state at every chunk
+// start (p.ckpt) and may form no output (p.o NULL); kept apart so that the
+// forward instances carry none of its code.
+template <int DK, int DVT, int GATE, int FE, bool CKPT = false>
 __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel(KParams p) {
     constexpr bool GL = (FE & FUSE_GATE_LOGITS) != 0, QN = (FE & FUSE_QK_L2NORM) != 0;
     static_assert(!(GL && GATE == 2), "gate logits need a gate");
@@ -1021,7 +1024,9 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // products are taken with their operands swapped, which yields O_a^T: lane
     // (n, g) then holds value columns 4g..4g+3 of token n, one 8-byte store.
     auto c_out = [&](int ch) {
-        if (!go) return;  // a call that only stores checkpoints
+        if constexpr (CKPT) {
+            if (!go) return;  // a call that only stores checkpoints
+        }
         const int lx = (int)opaque((uint32_t)l);
         const int ln = lx & 15, lg = lx >> 4;
         const bf16_t* m_b = reinterpret_cast<const bf16_t*>(buf(ch & 1, L::bM));
@@ -1070,7 +1075,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         {
             const int lx = (int)opaque((uint32_t)l);  // addresses recomputed per chunk
             const int ln = lx & 15, lg = lx >> 4;
-            if (p.ckpt) store_state(ckpt_at(ch));
+            if constexpr (CKPT) store_state(ckpt_at(ch));
             if (ch > 0) c_out(ch - 1);
             const bf16_t* kr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bKr));
             const bf16_t* qr_b = reinterpret_cast<const bf16_t*>(buf(par, L::bQr));
@@ -1176,19 +1181,19 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         redo();
         return;
     }
-    if (p.ckpt) store_state(ckpt_at(nch));
+    if constexpr (CKPT) store_state(ckpt_at(nch));
     if (p.sT) store_state(p.sT + sbase);
 }
 
-template <int DK, int DVT, int GATE, int FE>
+template <int DK, int DVT, int GATE, int FE, bool CKPT = false>
 static hipError_t launch_g(const KParams& p, hipStream_t stream) {
     using Lay = Lay6<DK, DVT, (FE & FUSE_QK_L2NORM) != 0>;
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)chunk_fwd_bf16_kernel<DK, DVT, GATE, FE>,
+        (const void*)chunk_fwd_bf16_kernel<DK, DVT, GATE, FE, CKPT>,
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
     const long grid = 8L * p.njt_all * ((p.units + 7) / 8);
-    hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVT, GATE, FE>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVT, GATE, FE, CKPT>), dim3((unsigned)grid),
                        dim3(Lay::NTH), Lay::bytes, stream, p);
     return hipGetLastError();
 }
@@ -1210,6 +1215,8 @@ static hipError_t launch_fe(const KParams& p, hipStream_t stream) {
 
 template <int DK, int DVT>
 static hipError_t launch_t(const KParams& p, hipStream_t stream) {
+    // the backward's forward: per-channel gate, no input preparation
+    if (p.ckpt) return launch_g<DK, DVT, 0, 0, true>(p, stream);
     return p.gate == 0 ? launch_fe<DK, DVT, 0>(p, stream)
          : p.gate == 1 ? launch_fe<DK, DVT, 1>(p, stream) : launch_fe<DK, DVT, 2>(p, stream);
 }
