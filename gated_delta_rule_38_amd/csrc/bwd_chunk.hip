@@ -1022,8 +1022,9 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     const int t = ch * CH + rowb + e;
                     if (t < len) {
                         const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                        gout.dq[off] = gq * ratio;
-                        gout.dk[off] = gkr * ratio + gkc * irat;
+                        // (non-temporal: the planes are read once, by the last pass)
+                        __builtin_nontemporal_store(gq * ratio, gout.dq + off);
+                        __builtin_nontemporal_store(gkr * ratio + gkc * irat, gout.dk + off);
                     }
                     dl[e] = (gkr * ke[e] + gq * qe[e]) * ratio - gkc * ke[e] * irat;
                 }
@@ -1072,7 +1073,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     const int t = ch * CH + rowb + e;
                     if (t < len) {
                         const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                        gout.da[off] = (dls[ct][e] + later) / av[ct][e];
+                        __builtin_nontemporal_store((dls[ct][e] + later) / av[ct][e], gout.da + off);
                     }
                 }
             }

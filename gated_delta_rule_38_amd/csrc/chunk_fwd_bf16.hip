@@ -992,7 +992,9 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 
     f32x4 S[NT][NCT], Y[NT][4], OI[NT][4];  // state, beta-scaled X, (Qr (Pm S0))^T
     // this wave's columns of the state into a float32 [dk][dv] block
-    // (lane offsets recomputed per call, so no per-element address stays live)
+    // (lane offsets recomputed per call, so no per-element address stays live;
+    // checkpoints are read back only by the reverse sweep, long after, so they
+    // are stored non-temporally)
     auto store_state = [&](float* dst) {
         const int lx = (int)opaque((uint32_t)l);
         float* base = dst + (size_t)(lx >> 4) * 8 * DV + colw + (lx & 15);
@@ -1001,8 +1003,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    base[(size_t)state_ch(ct, 0, e) * DV + 16 * j] = S[j][ct][e];
+                for (int e = 0; e < 4; ++e) {
+                    float* q = base + (size_t)state_ch(ct, 0, e) * DV + 16 * j;
+                    if constexpr (CKPT) __builtin_nontemporal_store(S[j][ct][e], q);
+                    else *q = S[j][ct][e];
+                }
     };
     const size_t slot0 = (size_t)(t0 / CH + 2 * (long)wi.seq);
     auto ckpt_at = [&](int ch) { return p.ckpt + ((slot0 + ch) * H + h) * DK * DV; };
