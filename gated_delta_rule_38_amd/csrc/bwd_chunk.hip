@@ -474,6 +474,14 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
     // chunk and every one before it then go through the token-by-token chain
     // rule after the loop.  (The chunk form holds all 512 registers of a lane;
     // the token path placed inside the loop would make it spill.)
+    // Descriptor over rows ch*CH .. of a [token][H][width] float tensor at
+    // head h, ending with the sequence's last row in the chunk: the stores
+    // of the rows past it are dropped.
+    auto chunk_rsrc = [&](float* base, int ch, int width) {
+        const int nrow = min(len - ch * CH, CH);
+        return make_rsrc(base + ((size_t)(t0 + (long)ch * CH) * H + h) * width, (uint32_t)(nrow * H * width * 4));
+    };
+
     int token_from = -1;
     for (int ch = nch - 1; ch >= 0; --ch) {
         load_rows(ch);
@@ -772,6 +780,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
 
         // ================= phase 4: U = T' Y, dY = T'^T dU, dX, dv ===========
         {
+            const Rsrc rdv = chunk_rsrc(bp.dv, ch, DV);
             const int ns = (w >= 2) ? 2 : 1;
             const int s_lo = (w >= 2) ? 1 : 0;
             const int rowb = w * 16 + lg * 4;
@@ -801,9 +810,10 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     sUr[r * LDV + jb * 16 + ln] = from_f32<Top>(cu[e]);
                     sdYr[r * LDV + jb * 16 + ln] = from_f32<Top>(cy[e]);
                     sdXr[r * LDV + jb * 16 + ln] = from_f32<Top>(dx[e]);
-                    const int t = ch * CH + r;
-                    if (t < len)
-                        bp.dv[((size_t)(t0 + t) * H + h) * DV + col0 + jb * 16 + ln] = dx[e];
+                    // lane part: row rowb, column col0 + ln; wave part: row e, column tile jb
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dx[e]), rdv,
+                                                          (uint32_t)((rowb * H * DV + col0 + ln) * 4),
+                                                          (e * H * DV + jb * 16) * 4, 0);
                 }
                 M::st4(sdXT + (jb * 16 + ln) * LDC + rowb, dx);
             }
@@ -905,6 +915,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
         // of channel 16 ct + ln.  The per-element decay factors are formed here
         // from alpha reloaded in this layout (prefix products inside the lane's
         // four rows, then across the four lane groups).
+        const Rsrc rdq = chunk_rsrc(gout.dq, ch, DK), rdk = chunk_rsrc(gout.dk, ch, DK);
         float dls[DK / 16][4];  // suffix sums of dlogP inside row block w
         {
 #pragma unroll
@@ -1019,13 +1030,13 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                     const float gq = scale * aqo[e] + aq[e];
                     const float gkr = ak[e] - akx[e];
                     const float gkc = ac[e];
-                    const int t = ch * CH + rowb + e;
-                    if (t < len) {
-                        const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                        // (non-temporal: the planes are read once, by the last pass)
-                        __builtin_nontemporal_store(gq * ratio, gout.dq + off);
-                        __builtin_nontemporal_store(gkr * ratio + gkc * irat, gout.dk + off);
-                    }
+                    // (non-temporal: the planes are read once, by the last pass)
+                    // lane part: row rowb, channel ln; wave part: row e, channel tile ct
+                    const uint32_t lo = (uint32_t)((rowb * H * DK + ln) * 4);
+                    const int so = (e * H * DK + ct * 16) * 4;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gq * ratio), rdq, lo, so, CPOL_NT);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gkr * ratio + gkc * irat), rdk, lo, so,
+                                                          CPOL_NT);
                     dl[e] = (gkr * ke[e] + gq * qe[e]) * ratio - gkc * ke[e] * irat;
                 }
                 if (w == 3 && lg == 3) {  // the last row also carries the chunk-end decay
@@ -1048,6 +1059,7 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
         __syncthreads();  // B7: everyone is done reading sTot
         // ================= phase 7: dalpha (suffix across row blocks), dbeta ==
         {
+            const Rsrc rda = chunk_rsrc(gout.da, ch, DK), rdb = chunk_rsrc(gout.db, ch, 1);
             const int rowb = w * 16 + lg * 4;
             // alpha of the lane's elements, read before the barrier below
             float av[DK / 16][4];
@@ -1069,24 +1081,18 @@ __global__ __launch_bounds__(BW_NTH, 1) void bwd_chunk_kernel(BwParams bp) {
                 float later = 0.f;
                 for (int b = w + 1; b < 4; ++b) later += sTot[b * DK + c];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = ch * CH + rowb + e;
-                    if (t < len) {
-                        const size_t off = ((size_t)(t0 + t) * H + h) * DK + c;
-                        __builtin_nontemporal_store((dls[ct][e] + later) / av[ct][e], gout.da + off);
-                    }
-                }
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((dls[ct][e] + later) / av[ct][e]), rda,
+                                                          (uint32_t)((rowb * H * DK + ln) * 4),
+                                                          (e * H * DK + ct * 16) * 4, CPOL_NT);
             }
             if (w == 0) {
                 const int r = l;
-                const int t = ch * CH + r;
-                if (t < len) {
-                    // jobs (a, b) of row block a = r / 16, in a fixed order
-                    const int a = r >> 4;
-                    float db = sDb1[r];
-                    for (int b = 0; b <= a; ++b) db -= sDb2[(a * (a + 1) / 2 + b) * 16 + (r & 15)];
-                    gout.db[(size_t)(t0 + t) * H + h] = db;
-                }
+                // jobs (a, b) of row block a = r / 16, in a fixed order
+                const int a = r >> 4;
+                float db = sDb1[r];
+                for (int b = 0; b <= a; ++b) db -= sDb2[(a * (a + 1) / 2 + b) * 16 + (r & 15)];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(db), rdb, (uint32_t)(r * H * 4), 0, 0);
             }
         }
         __syncthreads();  // B9: LDS reuse by the next chunk

@@ -63,6 +63,22 @@ __device__ __forceinline__ WorkItem decode_work(const KParams& p) {
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Raw buffer descriptor over [base, base + bytes).  Loads past the range
+// return zero and stores past it are dropped, so a chunk's tail rows need no
+// branch: a store that is issued on every path lets the compiler count the
+// memory operations in flight exactly (stores and loads share one counter),
+// where a store under a branch makes every later wait assume the shorter
+// path and so also wait for stores and loads that were issued after the one
+// it needs.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    // stride 0, num_records = bytes, dword 3 = 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// cache policy of a store that is read only much later (non-temporal)
+constexpr int CPOL_NT = 2;
+
 // Store N consecutive operand elements to LDS with the widest aligned writes.
 template <typename Top, int N>
 __device__ __forceinline__ void store_run(Top* p, const Top* v) {

@@ -48,15 +48,9 @@
 
 namespace kda {
 
-typedef __amdgpu_buffer_rsrc_t Rsrc;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-    // raw buffer: stride 0, num_records = bytes, dword 3 = 32-bit data format
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     bf16x2v h;

@@ -514,6 +514,8 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
         // ================= phase 4: outputs and the next state =================
         {
             const int ns = (w >= 2) ? 2 : 1;
+            const Rsrc ro = make_rsrc(go + ((size_t)(t0 + (long)ch * CH) * H + h) * DV,
+                                      (uint32_t)(min(len - ch * CH, CH) * H * DV * 2));
 #pragma unroll
             for (int jb = 0; jb < NJT; ++jb) {
                 f32x4 co = oi[jb];
@@ -529,13 +531,14 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                         }
                     }
                 }
+                // rows past the end of the sequence lie outside the descriptor
+                // (lane part: row 16w + 4lg, column col0 + ln; wave part: row e,
+                // column tile jb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = ch * CH + w * 16 + lg * 4 + e;
-                    if (t < len)
-                        go[((size_t)(t0 + t) * H + h) * DV + col0 + jb * 16 + ln] =
-                            from_f32<bf16_t>(p.scale * co[e]);
-                }
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        __builtin_bit_cast(unsigned short, from_f32<bf16_t>(p.scale * co[e])), ro,
+                        (uint32_t)(((w * 16 + lg * 4) * H * DV + col0 + ln) * 2), (e * H * DV + jb * 16) * 2, 0);
             }
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
