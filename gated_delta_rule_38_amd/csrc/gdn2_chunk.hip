@@ -158,6 +158,13 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     const float* __restrict__ ga = static_cast<const float*>(p.alpha);
     const float* __restrict__ ge = gp.erase;
     const float* __restrict__ gw = gp.write;
+    // Every load of the chunk loop is issued on every path (a load under a
+    // branch would make the compiler's waits for the loads in flight assume
+    // the path without it, and wait for more): without a forget gate the
+    // decay rows are read from the erase gate, an array of the same shape,
+    // and replaced by 1 where they are used.
+    const bool has_alpha = ga != nullptr;
+    const float* __restrict__ gsa = has_alpha ? ga : ge;
     bf16_t* __restrict__ go = static_cast<bf16_t*>(p.o);
 
     const int tid = threadIdx.x;
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
             const size_t off = ((size_t)(t0 + t) * H + h) * DK + c0;
             pq[r] = R::ldb(gq + off);
             pk[r] = R::ldb(gk + off);
-            pa[r] = ga ? R::ldf(ga + off) : R::one();
+            pa[r] = R::ldf(gsa + off);
             pe[r] = R::ldf(ge + off);
             pw[r] = R::ldf(gw + off);
         }
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 R::uf(pa[r], a);
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
-                    run[c] *= (r < nvalid) ? a[c] : 1.f;
+                    run[c] *= (r < nvalid && has_alpha) ? a[c] : 1.f;
                     pr[r][c] = run[c];
                 }
             }
@@ -334,9 +341,9 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 }
             }
         }
-        if (ch + 1 < nch) load_rows(ch + 1, 0);
+        load_rows(ch + 1, 0);  // (past the last chunk: rows clamped to the last, unused)
         __syncthreads();  // B2
-        if (ch + 1 < nch) load_rows(ch + 1, 1);
+        load_rows(ch + 1, 1);
 
         // ================= phase 1: Gram blocks, X = Kr SP and OI = Qr SP =====
         f32x4 xr[NJT], oi[NJT];
@@ -399,9 +406,9 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 oi[jb] = co;
             }
         }
-        if (ch + 1 < nch) load_v(ch + 1);
+        load_v(ch + 1);
         __syncthreads();  // B3
-        if (ch + 1 < nch) load_rows(ch + 1, 2);
+        load_rows(ch + 1, 2);
 
         // ================= phase 2: Y = X + L_c V, T = (I + L_a)^{-1} ===========
         {
@@ -489,7 +496,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
             }
         }
         __syncthreads();  // B4
-        if (ch + 1 < nch) load_rows(ch + 1, 3);
+        load_rows(ch + 1, 3);
 
         // ================= phase 3: Pred = T Y, stored as -Pred^T in Z ==========
         {
