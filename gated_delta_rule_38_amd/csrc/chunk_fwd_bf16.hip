@@ -64,14 +64,28 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-// Element offset of (row, channel) in a [64][LDK] token tile.  The 16-byte
-// column chunks of a row are XOR-swizzled by (row / 16) mod 4: a producer
-// lane writes rows 4 apart (16-byte stores), and unswizzled those rows would
-// share four bank groups; swizzled, the 16 lanes of a store and the 16 rows of
-// a matrix-core fragment read each hit distinct banks.
-template <int LDK>
+// Element offset of (row, channel) in a [64][LDK] token tile (LDK = dk + 8,
+// so rows are 16 bytes longer than the data).  Bank behaviour of gfx950's LDS,
+// measured with SQ_LDS_BANK_CONFLICT on probe kernels: a 16-byte read is served
+// 16 lanes at a time over 64 four-byte banks, lanes 0-7 together with 16-23
+// (and 8-15 with 24-31, ...); a 16-byte write, 16 consecutive lanes at a time.
+// A matrix-core fragment read takes 8 rows x 2 column chunks per pass, a
+// producer store 4 rows 4 apart x 4 chunks.  With dk = 128 (272-byte rows, 17
+// chunks of 16 bytes) the data chunk c of row r is placed at chunk
+// (c + 7 (r mod 2)) mod 16: row r then starts (in 16-byte bank groups) at
+// r + 7 (r mod 2) = the even values 0..14 over any 8 consecutive rows, so
+// both passes touch 16 distinct bank groups, where the plain layout gives every
+// fragment read a 2-way conflict.  The rotation's reads need per-lane chunk
+// offsets (formed once per wave where registers allow, ROT); otherwise (dk =
+// 64, or an instance with no registers to spare) the 16-byte chunks of a row
+// are XOR-swizzled by (row / 16) mod 4, which keeps the producers' stores
+// apart and leaves the reads 2-way.
+template <int LDK, bool ROT>
 __device__ __forceinline__ int tok_off(int row, int ch) {
-    return row * LDK + ((((ch >> 3) ^ (row >> 4)) & 3) | ((ch >> 3) & ~3)) * 8 + (ch & 7);
+    if constexpr (ROT)
+        return row * LDK + ((((ch >> 3) + 7 * (row & 1)) & 15) << 3) + (ch & 7);
+    else
+        return row * LDK + ((((ch >> 3) ^ (row >> 4)) & 3) | ((ch >> 3) & ~3)) * 8 + (ch & 7);
 }
 // Kc^T is kept with its rows (key channels) and columns (tokens) permuted
 // inside groups of 32 so that matrix-core operands can be taken straight from
@@ -322,6 +336,24 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
     const int ln = l & 15, lg = l >> 4;
+    // This lane's 16-byte chunk of row block rowblk at k-step s of a
+    // matrix-fragment read of a token tile.  With the rotated layout the chunk
+    // offsets within a row depend on the lane only (the row's parity is the
+    // lane's), so they are formed once per wave and the reads need no per-step
+    // address arithmetic; instances with in-kernel q/k normalisation have no
+    // registers to spare for them and keep the XOR layout.
+    constexpr bool ROT = DK == 128 && !QN;
+    int fco[DK / 32];
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) fco[s] = ROT ? tok_off<LDK, ROT>(ln, s * 32 + lg * 8) - ln * LDK : 0;
+    // (lane_n, lane_g: the caller's lane row and column group, used by the XOR
+    // layout's address)
+    auto frag_at = [&](const bf16_t* tile, int rowblk, int s, int lane_n, int lane_g) {
+        if constexpr (ROT)
+            return tile + (rowblk * 16 + ln) * LDK + fco[s];
+        else
+            return tile + tok_off<LDK, ROT>(rowblk * 16 + lane_n, s * 32 + lane_g * 8);
+    };
 
     // byte strides of one token row
     const uint32_t rsq = (uint32_t)H * DK * 2, rsa = (uint32_t)H * DK * (GL ? 2 : 4);
@@ -389,12 +421,12 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
         f32x4 cA[2] = {zero4(), zero4()}, cM[2] = {zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
-            const auto fk = Mf::ld32(kr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
-            const auto fq = Mf::ld32(qr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
+            const auto fk = Mf::ld32(frag_at(kr_b, a, s, ln, lg));
+            const auto fq = Mf::ld32(frag_at(qr_b, a, s, ln, lg));
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 if (j < nb) {
-                    const auto fa = Mf::ld32(sKc + tok_off<LDK>((b0 + j) * 16 + ln, s * 32 + lg * 8));
+                    const auto fa = Mf::ld32(frag_at(sKc, b0 + j, s, ln, lg));
                     cA[j] = Mf::k32(fa, fk, cA[j]);
                     cM[j] = Mf::k32(fa, fq, cM[j]);
                 }
@@ -737,7 +769,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                         RT[2 * c1 + (rr >> 1)] = __builtin_amdgcn_perm(kcp[i], kc[i], 0x07060302u);
                     }
                 }
-                const int to = tok_off<LDK>(pr0 + rr, pc0);
+                const int to = tok_off<LDK, ROT>(pr0 + rr, pc0);
                 if constexpr (CPL == 8) {
                     *reinterpret_cast<uint4*>(kr_b + to) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
                     *reinterpret_cast<uint4*>(qr_b + to) = make_uint4(qr[0], qr[1], qr[2], qr[3]);
@@ -1093,8 +1125,8 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
                 for (int j = 0; j < NT; ++j) cx[j] = co[j] = zero4();
 #pragma unroll
                 for (int s = 0; s < DK / 32; ++s) {
-                    const auto fk = Mf::ld32(kr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
-                    const auto fq = Mf::ld32(qr_b + tok_off<LDK>(a * 16 + ln, s * 32 + lg * 8));
+                    const auto fk = Mf::ld32(frag_at(kr_b, a, s, ln, lg));
+                    const auto fq = Mf::ld32(frag_at(qr_b, a, s, ln, lg));
 #pragma unroll
                     for (int j = 0; j < NT; ++j) {
                         cx[j] = Mf::k32(fk, fs[j][s], cx[j]);
