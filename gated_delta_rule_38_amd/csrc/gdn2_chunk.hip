@@ -30,21 +30,26 @@
 // Past the end of a sequence the chunk is padded with q = k = v = 0,
 // e = w = 0, alpha = 1, an exact no-op.
 //
-// Work decomposition as in the KDA kernels: one workgroup of four waves owns
-// one (unit, value-column slice) and walks the unit's chunks with its fp32
-// state slice in matrix-core accumulator registers; the column-independent
-// work (decays, Gram products, the triangular inverse) is recomputed per
-// slice, and the slices of a unit share an XCD.  A chunk runs in five phases
-// separated by workgroup barriers (decays; operands; Gram products and Kr SP,
-// Qr SP; Y and the inverse; the solve; outputs and the state update), with
-// the next chunk's inputs loaded into registers one chunk ahead.
+// Work decomposition as in the KDA kernels: one workgroup owns one (unit,
+// value-column slice) and walks the unit's chunks with its fp32 state slice
+// in matrix-core accumulator registers; the column-independent work (decays,
+// Gram products, the triangular inverse) is recomputed per slice, and the
+// slices of a unit share an XCD.  A chunk runs in five phases separated by
+// workgroup barriers (decays; operands; Gram products and Kr SP, Qr SP; Y and
+// the inverse; the solve; outputs and the state update), with the next
+// chunk's inputs loaded into registers one chunk ahead.  Wave w works on row
+// block w mod 4 of the chunk.  With dk = 128 and 32-column slices the
+// workgroup has eight waves, two per SIMD: the two waves of a row block split
+// its key channels in the operand build and its two value tiles in the
+// products, and each holds two state tiles; the phases are chains of
+// dependent matrix-core products and LDS round trips, which the second wave
+// on a SIMD overlaps.  Other shapes run four waves.
 #include "chunk_walk.h"
 
 namespace kda {
 
 namespace {
 
-constexpr int G2_NTH = 256;
 
 struct G2Params {
     KParams base;                // q, k, v, alpha (NULL: no forget gate), s0, o, sT, mapping
@@ -62,7 +67,6 @@ struct G2Layout {
     static constexpr int NJT = DVT / 16;
     static constexpr int NCT = DK / 16;
     static constexpr int NST = NCT * NJT;
-    static constexpr int STW = (NST + 3) / 4;
     // region A, phases 0b-1: chunk operands
     static constexpr size_t oKr = 0;
     static constexpr size_t oQr = oKr + (size_t)CH * LDK * ES;
@@ -84,8 +88,8 @@ struct G2Layout {
     static constexpr size_t oAc = oZT + (size_t)DVT * LDC2 * ES;   // [CH][LDC]: L_c
     static constexpr size_t oLo = oAc + (size_t)CH * LDC * ES;     // [CH][LDC]: L_a off-diagonal
     static constexpr size_t oLd = oLo + (size_t)CH * LDC * ES;     // fp32 [4][16][LDL]
-    static constexpr size_t oBad = oLd + (size_t)4 * 16 * LDL * 4;   // u32 [4] out-of-range flags
-    static constexpr size_t bytes = oBad + 16;
+    static constexpr size_t oBad = oLd + (size_t)4 * 16 * LDL * 4;   // u32 [8] out-of-range flags
+    static constexpr size_t bytes = oBad + 32;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -113,14 +117,19 @@ template <> struct G2Row<2> {
     static __device__ __forceinline__ F one() { return make_float2(1.f, 1.f); }
 };
 
-template <int DK, int DVT>
-__global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
+template <int DK, int DVT, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
     using Top = bf16_t;
     using L = G2Layout<DK, DVT>;
     using M = Mma<Top>;
-    constexpr int CPT = DK / 64;
+    constexpr int NTH = NW * 64;
+    constexpr int NH = NW / 4;          // waves per row block
+    constexpr int CPT = DK / 64 / NH;   // channels per lane in a row
     constexpr int LDK = L::LDK, LDC = L::LDC, LDC2 = L::LDC2, LDD = L::LDD, NJT = L::NJT;
-    constexpr int NST = L::NST, STW = L::STW;
+    constexpr int NJW = NJT / NH;       // value tiles per wave
+    constexpr int NST = L::NST, STW = (NST + NW - 1) / NW;
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    static_assert(CPT >= 1 && NJW >= 1, "a wave's share of a row block");
     using R = G2Row<CPT>;
     const KParams& p = gp.base;
 
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     Top* sLo = reinterpret_cast<Top*>(smem + L::oLo);
     float* sLd = reinterpret_cast<float*>(smem + L::oLd);
     uint32_t* sBad = reinterpret_cast<uint32_t*>(smem + L::oBad);
-    static_assert(WalkShape<DVT, G2_NTH, true>::lds_bytes <= L::oBad, "walk LDS");
+    static_assert(WalkShape<DVT, NTH, true>::lds_bytes <= L::oBad, "walk LDS");
     // the decay total of row block b for channel c sits in the 16-byte pad of FT row c
     auto tot = [&](int b, int c) -> float& {
         return reinterpret_cast<float*>(sFT + (size_t)c * LDC2 + 2 * CH)[b];
@@ -169,17 +178,20 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rb = w & 3;        // row block of the wave
+    const int hf = w >> 2;       // its share: channels hf*DK/NH.., value tiles hf*NJW..
+    const int jb0 = hf * NJW;
     const int l = tid & 63;
     const int ln = l & 15;
     const int lg = l >> 4;
     const int col0 = jt * DVT;
 
-    // ---- state slice in C-layout registers: wave w owns tiles w, w+4, ... ----
+    // ---- state slice in C-layout registers: wave w owns tiles w, w+NW, ... ----
     f32x4 S[STW];
     const size_t sbase = ((size_t)seq * H + h) * DK * DV;
 #pragma unroll
     for (int i = 0; i < STW; ++i) {
-        const int st = w + 4 * i;
+        const int st = w + NW * i;
         S[i] = zero4();
         if (st < NST && p.s0) {
             const int ct = st / NJT, jj = st % NJT;
@@ -191,26 +203,26 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
 
     // Blocks above the diagonal of M (both halves) and of L_c are read by the
     // 32-deep steps and must be zero; nothing else writes them.
-    for (int idx = tid; idx < CH * 2 * CH; idx += G2_NTH) {
+    for (int idx = tid; idx < CH * 2 * CH; idx += NTH) {
         const int r = idx / (2 * CH), c = idx % (2 * CH);
         if (((c & (CH - 1)) >> 4) > (r >> 4)) sM[r * LDC2 + c] = from_f32<Top>(0.f);
     }
-    for (int idx = tid; idx < CH * CH; idx += G2_NTH) {
+    for (int idx = tid; idx < CH * CH; idx += NTH) {
         const int r = idx / CH, c = idx % CH;
         if ((c >> 4) > (r >> 4)) sAc[r * LDC + c] = from_f32<Top>(0.f);
     }
 
-    // ---- register prefetch: row block w, channels l*CPT.. ----
+    // ---- register prefetch: row block rb, channels c0.. ----
     typename R::B pq[16], pk[16];
     typename R::F pa[16], pe[16], pw[16];
-    bf16_t pv[NJT][4];
-    const int c0 = l * CPT;
+    bf16_t pv[NJW][4];
+    const int c0 = hf * (DK / NH) + l * CPT;
     // rows 4 part .. 4 part + 3 of the row block: the loads of the next chunk go
     // out in four parts, at the end of the operand build and after each of the
     // barriers B2..B4, where they overlap matrix-core work instead of stalling
     // the operand build on their issue (80 load instructions per lane and chunk)
     auto load_rows = [&](int ch, int part) {
-        const int base_r = ch * CH + w * 16;
+        const int base_r = ch * CH + rb * 16;
 #pragma unroll
         for (int r = 4 * part; r < 4 * part + 4; ++r) {
             const int t = min(base_r + r, len - 1);  // rows past the end are replaced when used
@@ -224,11 +236,11 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     };
     auto load_v = [&](int ch) {
 #pragma unroll
-        for (int jb = 0; jb < NJT; ++jb)
+        for (int jj = 0; jj < NJW; ++jj)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = min(ch * CH + w * 16 + lg * 4 + e, len - 1);
-                pv[jb][e] = gv[((size_t)(t0 + t) * H + h) * DV + col0 + jb * 16 + ln];
+                const int t = min(ch * CH + rb * 16 + lg * 4 + e, len - 1);
+                pv[jj][e] = gv[((size_t)(t0 + t) * H + h) * DV + col0 + (jb0 + jj) * 16 + ln];
             }
     };
 
@@ -243,9 +255,9 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     bool bad = false;  // a chunk's decays left the chunk form's range (wave 0 checks)
 
     for (int ch = 0; ch < nch; ++ch) {
-        // ================= phase 0a: running products inside row block w ======
+        // ================= phase 0a: running products inside row block rb =====
         float pr[16][CPT];
-        const int nvalid = len - (ch * CH + w * 16);
+        const int nvalid = len - (ch * CH + rb * 16);
         {
             float run[CPT];
 #pragma unroll
@@ -261,27 +273,27 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 }
             }
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) tot(w, c0 + c) = run[c];
+            for (int c = 0; c < CPT; ++c) tot(rb, c0 + c) = run[c];
         }
         __syncthreads();  // B1
 
         // ================= phase 0b: decayed operands ==========================
         {
             // P_row / P_31 = (running product inside row block w) * fw with
-            // fw = 1 / (t0 t1), 1 / t1, 1, t2 for w = 0..3 (t_b: row block b's
+            // fw = 1 / (t0 t1), 1 / t1, 1, t2 for rb = 0..3 (t_b: row block b's
             // product): no product over more than half a chunk is formed
             float fw[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
                 const float t0v = tot(0, c0 + c), t1v = tot(1, c0 + c);
                 const float t2v = tot(2, c0 + c), t3v = tot(3, c0 + c);
-                fw[c] = (w == 0) ? fast_rcp(t0v * t1v) : (w == 1) ? fast_rcp(t1v) : (w == 2) ? 1.f : t2v;
-                if (w == 0) bad |= decay_out_of_range(t0v * t1v, t2v * t3v);
+                fw[c] = (rb == 0) ? fast_rcp(t0v * t1v) : (rb == 1) ? fast_rcp(t1v) : (rb == 2) ? 1.f : t2v;
+                if (rb == 0) bad |= decay_out_of_range(t0v * t1v, t2v * t3v);
             }
             Top wct[CPT][16], ect[CPT][16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = w * 16 + r;
+                const int row = rb * 16 + r;
                 const bool ok = r < nvalid;
                 float kx[CPT], qx[CPT], ex[CPT], wx[CPT];
                 R::ub(pk[r], kx);
@@ -309,22 +321,22 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
             }
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + w * 16, wct[c]);
-                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + CH + w * 16, ect[c]);
+                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + rb * 16, wct[c]);
+                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + CH + rb * 16, ect[c]);
             }
             // V^T into the first half of Z (4 consecutive tokens per lane)
 #pragma unroll
-            for (int jb = 0; jb < NJT; ++jb) {
+            for (int jj = 0; jj < NJW; ++jj) {
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    x[e] = (ch * CH + w * 16 + lg * 4 + e < len) ? to_f32(pv[jb][e]) : 0.f;
-                M::st4(sZT + (jb * 16 + ln) * LDC2 + w * 16 + lg * 4, x);
+                    x[e] = (ch * CH + rb * 16 + lg * 4 + e < len) ? to_f32(pv[jj][e]) : 0.f;
+                M::st4(sZT + ((jb0 + jj) * 16 + ln) * LDC2 + rb * 16 + lg * 4, x);
             }
             // SP = (Pm * S0)^T and the per-row decays kept for the state update
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
-                const int st = w + 4 * i;
+                const int st = w + NW * i;
                 if (st < NST) {
                     const int ct = st / NJT, jj = st % NJT;
                     f32x4 sp;
@@ -346,12 +358,12 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
         load_rows(ch + 1, 1);
 
         // ================= phase 1: Gram blocks, X = Kr SP and OI = Qr SP =====
-        f32x4 xr[NJT], oi[NJT];
+        f32x4 xr[NJW], oi[NJW];
         {
             // jobs (a, b), b <= a, round-robin over the waves; transposed tiles
             // F_b Kr_a^T give each lane 4 consecutive i of row r = 16a + ln
 #pragma unroll
-            for (int jn = w; jn < 10; jn += 4) {
+            for (int jn = w; jn < 10; jn += NW) {
                 const int a = (jn >= 6) ? 3 : (jn >= 3) ? 2 : (jn >= 1) ? 1 : 0;
                 const int b = jn - a * (a + 1) / 2;
                 f32x4 cLa = zero4(), cLc = zero4(), cMa = zero4(), cMc = zero4();
@@ -368,12 +380,10 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 }
                 const int r = a * 16 + ln;
                 if (a == b) {
-                    float4 ld;
-                    ld.x = (lg * 4 + 0 < ln) ? cLa[0] : 0.f;
-                    ld.y = (lg * 4 + 1 < ln) ? cLa[1] : 0.f;
-                    ld.z = (lg * 4 + 2 < ln) ? cLa[2] : 0.f;
-                    ld.w = (lg * 4 + 3 < ln) ? cLa[3] : 0.f;
-                    *reinterpret_cast<float4*>(sLd + (a * 16 + ln) * L::LDL + lg * 4) = ld;
+                    // the diagonal block, strictly lower, stored by columns
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sLd[(a * 16 + lg * 4 + e) * L::LDL + ln] = (lg * 4 + e < ln) ? cLa[e] : 0.f;
                     f32x4 lc, mc, ma;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -392,18 +402,19 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
                 }
             }
 #pragma unroll
-            for (int jb = 0; jb < NJT; ++jb) {
+            for (int jj = 0; jj < NJW; ++jj) {
+                const int jb = jb0 + jj;
                 f32x4 cx = zero4(), co = zero4();
 #pragma unroll
                 for (int s = 0; s < DK / 32; ++s) {
                     const auto fs = M::ld32(sSP + (jb * 16 + ln) * LDK + s * 32 + lg * 8);
-                    const auto fk = M::ld32(sKr + (w * 16 + ln) * LDK + s * 32 + lg * 8);
-                    const auto fq = M::ld32(sQr + (w * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fk = M::ld32(sKr + (rb * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fq = M::ld32(sQr + (rb * 16 + ln) * LDK + s * 32 + lg * 8);
                     cx = M::k32(fk, fs, cx);
                     co = M::k32(fq, fs, co);
                 }
-                xr[jb] = cx;
-                oi[jb] = co;
+                xr[jj] = cx;
+                oi[jj] = co;
             }
         }
         load_v(ch + 1);
@@ -412,87 +423,88 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
 
         // ================= phase 2: Y = X + L_c V, T = (I + L_a)^{-1} ===========
         {
-            const int ns = (w >= 2) ? 2 : 1;
+            const int ns = (rb >= 2) ? 2 : 1;
 #pragma unroll
-            for (int jb = 0; jb < NJT; ++jb) {
-                f32x4 cy = xr[jb];
+            for (int jj = 0; jj < NJW; ++jj) {
+                const int jb = jb0 + jj;
+                f32x4 cy = xr[jj];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     if (s < ns) {
-                        const auto fa = M::ld32(sAc + (w * 16 + ln) * LDC + s * 32 + lg * 8);
+                        const auto fa = M::ld32(sAc + (rb * 16 + ln) * LDC + s * 32 + lg * 8);
                         const auto fv = M::ld32(sZT + (jb * 16 + ln) * LDC2 + s * 32 + lg * 8);
                         cy = M::k32(fa, fv, cy);
                     }
                 }
-                M::st4(sYT + (jb * 16 + ln) * LDC + w * 16 + lg * 4, cy);
+                M::st4(sYT + (jb * 16 + ln) * LDC + rb * 16 + lg * 4, cy);
             }
-            // diagonal blocks: lane (block lg, column ln) solves L_aa x = e_ln
-            float x[16];
-            const float* La = sLd + lg * 16 * L::LDL;
-            float4 lrow[16][4];
+            // the first four waves form T's column blocks
+            if (hf == 0) {
+                // diagonal blocks: lane (block lg, column ln) solves L_aa x = e_ln
+                // (column i of the block: rows 0..15 at La + i LDL)
+                float x[16];
+                const float* La = sLd + lg * 16 * L::LDL;
 #pragma unroll
-            for (int r = 1; r < 16; ++r)
+                for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    if (q4 * 4 < r) lrow[r][q4] = *reinterpret_cast<const float4*>(La + r * L::LDL + q4 * 4);
+                for (int i = 0; i < 15; ++i) {
+                    float col[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < 15; ++i) {
-#pragma unroll
-                for (int r = i + 1; r < 16; ++r) {
-                    const float4 v4 = lrow[r][i / 4];
-                    const float lv = (i % 4 == 0) ? v4.x : (i % 4 == 1) ? v4.y : (i % 4 == 2) ? v4.z : v4.w;
-                    x[r] -= lv * x[i];
-                }
-            }
-            Top* Dr = sDr + (size_t)w * 4 * 16 * LDD;
-            Top* Dc = sDc + (size_t)w * 4 * 16 * LDD;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Dr[(lg * 16 + r) * LDD + ln] = from_f32<Top>(x[r]);
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                f32x4 t4 = {x[r4 * 4], x[r4 * 4 + 1], x[r4 * 4 + 2], x[r4 * 4 + 3]};
-                M::st4(Dc + (lg * 16 + ln) * LDD + r4 * 4, t4);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-            // column block b = w: T_bb = D_b, T_ab = -D_a sum_{j=b}^{a-1} L_aj T_jb
-            const int b = w;
-            f32x4 TB[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) TB[0][e] = to_f32(Dc[(b * 16 + ln) * LDD + lg * 4 + e]);
-#pragma unroll
-            for (int d = 1; d < 4; ++d) {
-                const int a = b + d;
-                if (a < 4) {
-                    f32x4 y = zero4();
-#pragma unroll
-                    for (int jd = 0; jd < d; ++jd) {
-                        const int j = b + jd;
-                        const auto fa = M::ld16(sLo + (a * 16 + ln) * LDC + j * 16 + lg * 4);
-                        y = M::k16(fa, M::pack16(TB[jd]), y);
+                    for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
+                        const float4 v4 = *reinterpret_cast<const float4*>(La + i * L::LDL + q4 * 4);
+                        col[q4 * 4] = v4.x; col[q4 * 4 + 1] = v4.y; col[q4 * 4 + 2] = v4.z; col[q4 * 4 + 3] = v4.w;
                     }
-                    const auto fd = M::ld16(Dr + (a * 16 + ln) * LDD + lg * 4);
-                    f32x4 t = M::k16(fd, M::pack16(y), zero4());
-                    TB[d][0] = -t[0]; TB[d][1] = -t[1]; TB[d][2] = -t[2]; TB[d][3] = -t[3];
-                }
-            }
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const int a = b + d;
-                if (a < 4) {
+                    for (int r = i + 1; r < 16; ++r) x[r] -= col[r] * x[i];
+                }
+                Top* Dr = sDr + (size_t)rb * 4 * 16 * LDD;
+                Top* Dc = sDc + (size_t)rb * 4 * 16 * LDD;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Dr[(lg * 16 + r) * LDD + ln] = from_f32<Top>(x[r]);
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 t4 = {x[r4 * 4], x[r4 * 4 + 1], x[r4 * 4 + 2], x[r4 * 4 + 3]};
+                    M::st4(Dc + (lg * 16 + ln) * LDD + r4 * 4, t4);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+                // column block b = rb: T_bb = D_b, T_ab = -D_a sum_{j=b}^{a-1} L_aj T_jb
+                const int b = rb;
+                f32x4 TB[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) TB[0][e] = to_f32(Dc[(b * 16 + ln) * LDD + lg * 4 + e]);
+#pragma unroll
+                for (int d = 1; d < 4; ++d) {
+                    const int a = b + d;
+                    if (a < 4) {
+                        f32x4 y = zero4();
+#pragma unroll
+                        for (int jd = 0; jd < d; ++jd) {
+                            const int j = b + jd;
+                            const auto fa = M::ld16(sLo + (a * 16 + ln) * LDC + j * 16 + lg * 4);
+                            y = M::k16(fa, M::pack16(TB[jd]), y);
+                        }
+                        const auto fd = M::ld16(Dr + (a * 16 + ln) * LDD + lg * 4);
+                        f32x4 t = M::k16(fd, M::pack16(y), zero4());
+                        TB[d][0] = -t[0]; TB[d][1] = -t[1]; TB[d][2] = -t[2]; TB[d][3] = -t[3];
+                    }
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const int a = b + d;
+                    if (a < 4) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(TB[d][e]);
+                    }
+                }
+                for (int a = 0; a < b; ++a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(TB[d][e]);
+                        sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(0.f);
                 }
-            }
-            for (int a = 0; a < b; ++a) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(0.f);
             }
         }
         __syncthreads();  // B4
@@ -500,56 +512,58 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
 
         // ================= phase 3: Pred = T Y, stored as -Pred^T in Z ==========
         {
-            const int ns = (w >= 2) ? 2 : 1;
+            const int ns = (rb >= 2) ? 2 : 1;
 #pragma unroll
-            for (int jb = 0; jb < NJT; ++jb) {
+            for (int jj = 0; jj < NJW; ++jj) {
+                const int jb = jb0 + jj;
                 f32x4 cp = zero4();
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     if (s < ns) {
-                        const auto ft = M::ld32(sTm + (w * 16 + ln) * LDC + s * 32 + lg * 8);
+                        const auto ft = M::ld32(sTm + (rb * 16 + ln) * LDC + s * 32 + lg * 8);
                         const auto fy = M::ld32(sYT + (jb * 16 + ln) * LDC + s * 32 + lg * 8);
                         cp = M::k32(ft, fy, cp);
                     }
                 }
                 f32x4 np = {-cp[0], -cp[1], -cp[2], -cp[3]};
-                M::st4(sZT + (jb * 16 + ln) * LDC2 + CH + w * 16 + lg * 4, np);
+                M::st4(sZT + (jb * 16 + ln) * LDC2 + CH + rb * 16 + lg * 4, np);
             }
         }
         __syncthreads();  // B5
 
         // ================= phase 4: outputs and the next state =================
         {
-            const int ns = (w >= 2) ? 2 : 1;
+            const int ns = (rb >= 2) ? 2 : 1;
             const Rsrc ro = make_rsrc(go + ((size_t)(t0 + (long)ch * CH) * H + h) * DV,
                                       (uint32_t)(min(len - ch * CH, CH) * H * DV * 2));
 #pragma unroll
-            for (int jb = 0; jb < NJT; ++jb) {
-                f32x4 co = oi[jb];
+            for (int jj = 0; jj < NJW; ++jj) {
+                const int jb = jb0 + jj;
+                f32x4 co = oi[jj];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         if (s < ns) {
                             const int k0 = half * CH + s * 32 + lg * 8;
-                            const auto fm = M::ld32(sM + (w * 16 + ln) * LDC2 + k0);
+                            const auto fm = M::ld32(sM + (rb * 16 + ln) * LDC2 + k0);
                             const auto fz = M::ld32(sZT + (jb * 16 + ln) * LDC2 + k0);
                             co = M::k32(fm, fz, co);
                         }
                     }
                 }
                 // rows past the end of the sequence lie outside the descriptor
-                // (lane part: row 16w + 4lg, column col0 + ln; wave part: row e,
+                // (lane part: row 16rb + 4lg, column col0 + ln; wave part: row e,
                 // column tile jb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     __builtin_amdgcn_raw_buffer_store_b16(
                         __builtin_bit_cast(unsigned short, from_f32<bf16_t>(p.scale * co[e])), ro,
-                        (uint32_t)(((w * 16 + lg * 4) * H * DV + col0 + ln) * 2), (e * H * DV + jb * 16) * 2, 0);
+                        (uint32_t)(((rb * 16 + lg * 4) * H * DV + col0 + ln) * 2), (e * H * DV + jb * 16) * 2, 0);
             }
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
-                const int st = w + 4 * i;
+                const int st = w + NW * i;
                 if (st < NST) {
                     const int ct = st / NJT, jj = st % NJT;
                     f32x4 acc = zero4();
@@ -573,7 +587,10 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
         __syncthreads();  // every wave is done with the last chunk's LDS
         if (l == 0) sBad[w] = b != 0;
         __syncthreads();
-        if (sBad[0] | sBad[1] | sBad[2] | sBad[3]) {
+        uint32_t any = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) any |= sBad[i];
+        if (any) {
             WalkArgs wa{};
             wa.q = p.q; wa.k = p.k; wa.v = p.v; wa.alpha = p.alpha;
             wa.erase = gp.erase; wa.write = gp.write;
@@ -581,7 +598,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
             wa.H = H; wa.dv = DV; wa.gate = p.alpha ? 0 : 2; wa.fuse = 0; wa.scale = p.scale;
             __threadfence();  // this item's stores so far land before the walk's
             __syncthreads();
-            token_walk<bf16_t, DK, DVT, G2_NTH, true>(wa, seq, h, t0, len, col0,
+            token_walk<bf16_t, DK, DVT, NTH, true>(wa, seq, h, t0, len, col0,
                                                       reinterpret_cast<float*>(smem));
             return;
         }
@@ -590,7 +607,7 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     if (p.sT) {
 #pragma unroll
         for (int i = 0; i < STW; ++i) {
-            const int st = w + 4 * i;
+            const int st = w + NW * i;
             if (st < NST) {
                 const int ct = st / NJT, jj = st % NJT;
 #pragma unroll
@@ -601,16 +618,16 @@ __global__ __launch_bounds__(G2_NTH, 1) void gdn2_chunk_kernel(G2Params gp) {
     }
 }
 
-template <int DK, int DVT>
+template <int DK, int DVT, int NW = 4>
 hipError_t launch_g2(const G2Params& gp, hipStream_t stream) {
     using Lay = G2Layout<DK, DVT>;
     const int groups = (gp.base.units + 7) / 8;
     const long grid = 8L * gp.base.njt_all * groups;
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)gdn2_chunk_kernel<DK, DVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (const void*)gdn2_chunk_kernel<DK, DVT, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
         (int)Lay::bytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gdn2_chunk_kernel<DK, DVT>), dim3((unsigned)grid), dim3(G2_NTH),
+    hipLaunchKernelGGL((gdn2_chunk_kernel<DK, DVT, NW>), dim3((unsigned)grid), dim3(NW * 64),
                        Lay::bytes, stream, gp);
     return hipGetLastError();
 }
@@ -652,7 +669,8 @@ hipError_t launch_gdn2_chunk_fwd(const Gdn2ChunkArgs& a, hipStream_t stream) {
     gp.erase = a.erase;
     gp.write = a.write;
     if (a.dk == 128) {
-        return dvt == 16 ? launch_g2<128, 16>(gp, stream) : launch_g2<128, 32>(gp, stream);
+        // eight waves where each wave still gets a whole channel and value tile
+        return dvt == 16 ? launch_g2<128, 16>(gp, stream) : launch_g2<128, 32, 8>(gp, stream);
     }
     switch (dvt) {
         case 16: return launch_g2<64, 16>(gp, stream);
