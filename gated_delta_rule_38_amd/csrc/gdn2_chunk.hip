@@ -40,8 +40,8 @@
 // chunk's inputs loaded into registers one chunk ahead.  Wave w works on row
 // block w mod 4 of the chunk.  With dk = 128 and 32-column slices the
 // workgroup has eight waves, two per SIMD: the two waves of a row block split
-// its key channels in the operand build and its two value tiles in the
-// products, and each holds two state tiles; the phases are chains of
+// its rows in the operand build and its two value tiles in the products, and
+// each holds two state tiles; the phases are chains of
 // dependent matrix-core products and LDS round trips, which the second wave
 // on a SIMD overlaps.  Other shapes run four waves.
 #include "chunk_walk.h"
@@ -61,7 +61,7 @@ struct G2Layout {
     static constexpr int ES = 2;                  // bf16 operands
     static constexpr int LDK = DK + 8;            // [token][channel] tiles
     static constexpr int LDC = CH + 8;            // [*][token] tiles
-    static constexpr int LDC2 = 2 * CH + 8;       // [*][stacked row] tiles (pad holds the decay totals)
+    static constexpr int LDC2 = 2 * CH + 8;       // [*][stacked row] tiles
     static constexpr int LDD = 16 + 8;            // 16x16 blocks
     static constexpr int LDL = 20;                // fp32 diagonal blocks of L_a
     static constexpr int NJT = DVT / 16;
@@ -124,12 +124,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
     using M = Mma<Top>;
     constexpr int NTH = NW * 64;
     constexpr int NH = NW / 4;          // waves per row block
-    constexpr int CPT = DK / 64 / NH;   // channels per lane in a row
+    constexpr int NSB = 4 * NH;         // operand-build row blocks, one per wave
+    constexpr int RPW = CH / NSB;       // rows of a wave's operand build
+    constexpr int CPT = DK / 64;        // channels per lane in a row
     constexpr int LDK = L::LDK, LDC = L::LDC, LDC2 = L::LDC2, LDD = L::LDD, NJT = L::NJT;
     constexpr int NJW = NJT / NH;       // value tiles per wave
     constexpr int NST = L::NST, STW = (NST + NW - 1) / NW;
     static_assert(NW == 4 || NW == 8, "four or eight waves");
-    static_assert(CPT >= 1 && NJW >= 1, "a wave's share of a row block");
+    static_assert(CPT >= 1 && NJW >= 1 && RPW % 4 == 0, "a wave's share of a row block");
     using R = G2Row<CPT>;
     const KParams& p = gp.base;
 
@@ -151,10 +153,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
     float* sLd = reinterpret_cast<float*>(smem + L::oLd);
     uint32_t* sBad = reinterpret_cast<uint32_t*>(smem + L::oBad);
     static_assert(WalkShape<DVT, NTH, true>::lds_bytes <= L::oBad, "walk LDS");
-    // the decay total of row block b for channel c sits in the 16-byte pad of FT row c
-    auto tot = [&](int b, int c) -> float& {
-        return reinterpret_cast<float*>(sFT + (size_t)c * LDC2 + 2 * CH)[b];
-    };
+    // the decay totals of the operand-build row blocks (phases 0a-0b) share
+    // the LDS of L_a's diagonal blocks (phases 1-2)
+    static_assert((size_t)NSB * DK * 4 <= (size_t)4 * 16 * L::LDL * 4, "decay totals");
+    auto tot = [&](int b, int c) -> float& { return sLd[b * DK + c]; };
 
     const WorkItem wi = decode_work(p);
     if (!wi.valid) return;
@@ -178,9 +180,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rb = w & 3;        // row block of the wave
-    const int hf = w >> 2;       // its share: channels hf*DK/NH.., value tiles hf*NJW..
+    const int rb = w & 3;        // row block of the wave's products
+    const int hf = w >> 2;       // its share of them: value tiles hf*NJW..
     const int jb0 = hf * NJW;
+    const int sb = rb * NH + hf; // operand build: rows sb*RPW .. sb*RPW + RPW - 1
     const int l = tid & 63;
     const int ln = l & 15;
     const int lg = l >> 4;
@@ -212,19 +215,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
         if ((c >> 4) > (r >> 4)) sAc[r * LDC + c] = from_f32<Top>(0.f);
     }
 
-    // ---- register prefetch: row block rb, channels c0.. ----
-    typename R::B pq[16], pk[16];
-    typename R::F pa[16], pe[16], pw[16];
+    // ---- register prefetch: rows of block sb, channels c0..; V of row block rb ----
+    typename R::B pq[RPW], pk[RPW];
+    typename R::F pa[RPW], pe[RPW], pw[RPW];
     bf16_t pv[NJW][4];
-    const int c0 = hf * (DK / NH) + l * CPT;
-    // rows 4 part .. 4 part + 3 of the row block: the loads of the next chunk go
+    const int c0 = l * CPT;
+    // a quarter of the rows per part: the loads of the next chunk go
     // out in four parts, at the end of the operand build and after each of the
     // barriers B2..B4, where they overlap matrix-core work instead of stalling
     // the operand build on their issue (80 load instructions per lane and chunk)
     auto load_rows = [&](int ch, int part) {
-        const int base_r = ch * CH + rb * 16;
+        const int base_r = ch * CH + sb * RPW;
 #pragma unroll
-        for (int r = 4 * part; r < 4 * part + 4; ++r) {
+        for (int r = part * RPW / 4; r < (part + 1) * RPW / 4; ++r) {
             const int t = min(base_r + r, len - 1);  // rows past the end are replaced when used
             const size_t off = ((size_t)(t0 + t) * H + h) * DK + c0;
             pq[r] = R::ldb(gq + off);
@@ -255,15 +258,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
     bool bad = false;  // a chunk's decays left the chunk form's range (wave 0 checks)
 
     for (int ch = 0; ch < nch; ++ch) {
-        // ================= phase 0a: running products inside row block rb =====
-        float pr[16][CPT];
-        const int nvalid = len - (ch * CH + rb * 16);
+        // ================= phase 0a: running products inside row block sb =====
+        float pr[RPW][CPT];
+        const int nvalid = len - (ch * CH + sb * RPW);
         {
             float run[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) run[c] = 1.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < RPW; ++r) {
                 float a[CPT];
                 R::uf(pa[r], a);
 #pragma unroll
@@ -273,27 +276,38 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                 }
             }
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) tot(rb, c0 + c) = run[c];
+            for (int c = 0; c < CPT; ++c) tot(sb, c0 + c) = run[c];
         }
         __syncthreads();  // B1
 
         // ================= phase 0b: decayed operands ==========================
         {
-            // P_row / P_31 = (running product inside row block w) * fw with
-            // fw = 1 / (t0 t1), 1 / t1, 1, t2 for rb = 0..3 (t_b: row block b's
-            // product): no product over more than half a chunk is formed
+            // P_row / P_31 = (running product inside row block sb) * fw with
+            // fw = 1 / (t_sb ... t_{h-1}) below the middle h = NSB/2 and
+            // t_h ... t_{sb-1} from it on (t_b: row block b's product): no
+            // product over more than half a chunk is formed
             float fw[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float t0v = tot(0, c0 + c), t1v = tot(1, c0 + c);
-                const float t2v = tot(2, c0 + c), t3v = tot(3, c0 + c);
-                fw[c] = (rb == 0) ? fast_rcp(t0v * t1v) : (rb == 1) ? fast_rcp(t1v) : (rb == 2) ? 1.f : t2v;
-                if (rb == 0) bad |= decay_out_of_range(t0v * t1v, t2v * t3v);
-            }
-            Top wct[CPT][16], ect[CPT][16];
+                float lo = 1.f, hi = 1.f, f = 1.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = rb * 16 + r;
+                for (int b = 0; b < NSB / 2; ++b) {
+                    lo *= tot(b, c0 + c);
+                    hi *= tot(NSB / 2 + b, c0 + c);
+                }
+                if (sb < NSB / 2) {
+                    for (int b = sb; b < NSB / 2; ++b) f *= tot(b, c0 + c);
+                    f = fast_rcp(f);
+                } else {
+                    for (int b = NSB / 2; b < sb; ++b) f *= tot(b, c0 + c);
+                }
+                fw[c] = f;
+                if (sb == 0) bad |= decay_out_of_range(lo, hi);
+            }
+            Top wct[CPT][RPW], ect[CPT][RPW];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int row = sb * RPW + r;
                 const bool ok = r < nvalid;
                 float kx[CPT], qx[CPT], ex[CPT], wx[CPT];
                 R::ub(pk[r], kx);
@@ -321,8 +335,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
             }
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + rb * 16, wct[c]);
-                store_run<Top, 16>(sFT + (c0 + c) * LDC2 + CH + rb * 16, ect[c]);
+                store_run<Top, RPW>(sFT + (c0 + c) * LDC2 + sb * RPW, wct[c]);
+                store_run<Top, RPW>(sFT + (c0 + c) * LDC2 + CH + sb * RPW, ect[c]);
             }
             // V^T into the first half of Z (4 consecutive tokens per lane)
 #pragma unroll
@@ -343,10 +357,17 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int c = ct * 16 + lg * 4 + e;
-                        const float a0 = tot(0, c), a1 = tot(1, c), a2 = tot(2, c), a3 = tot(3, c);
-                        const float pm = a0 * a1;
-                        pn_s[i][e] = pm * a2 * a3;
-                        pnm_s[i][e] = a2 * a3;  // Pn / Pm
+                        float pm = 1.f, pnm = 1.f;
+#pragma unroll
+                        for (int b = 0; b < NSB / 2; ++b) pm *= tot(b, c);
+                        float pn = pm;
+#pragma unroll
+                        for (int b = NSB / 2; b < NSB; ++b) {
+                            pn *= tot(b, c);
+                            pnm *= tot(b, c);
+                        }
+                        pn_s[i][e] = pn;
+                        pnm_s[i][e] = pnm;  // Pn / Pm
                         sp[e] = pm * S[i][e];
                     }
                     M::st4(sSP + (jj * 16 + ln) * LDK + ct * 16 + lg * 4, sp);
