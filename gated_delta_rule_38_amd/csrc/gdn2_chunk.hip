@@ -41,9 +41,11 @@
 // block w mod 4 of the chunk.  With dk = 128 and 32-column slices the
 // workgroup has eight waves, two per SIMD: the two waves of a row block split
 // its rows in the operand build and its two value tiles in the products, and
-// each holds two state tiles; the phases are chains of
-// dependent matrix-core products and LDS round trips, which the second wave
-// on a SIMD overlaps.  Other shapes run four waves.
+// each holds two state tiles; the phases are chains of dependent matrix-core
+// products and LDS round trips, which the second wave on a SIMD overlaps.
+// There the diagonal blocks of L_a are inverted in the Gram phase, each by
+// the wave that formed it, while the other four waves take the off-diagonal
+// Gram blocks.  Other shapes run four waves.
 #include "chunk_walk.h"
 
 namespace kda {
@@ -116,6 +118,25 @@ template <> struct G2Row<2> {
     static __device__ __forceinline__ void uf(F w, float* x) { x[0] = w.x; x[1] = w.y; }
     static __device__ __forceinline__ F one() { return make_float2(1.f, 1.f); }
 };
+
+// x = (I + L)^{-1} e_j for a strictly lower triangular 16x16 block L stored
+// by columns (column i: rows 0..15 at Lc + i ld, 16-byte aligned), by forward
+// substitution one column of L at a time
+__device__ __forceinline__ void unit_lower_solve(const float* Lc, int ld, int j, float (&x)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+        float col[16];
+#pragma unroll
+        for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(Lc + i * ld + q4 * 4);
+            col[q4 * 4] = v4.x; col[q4 * 4 + 1] = v4.y; col[q4 * 4 + 2] = v4.z; col[q4 * 4 + 3] = v4.w;
+        }
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) x[r] -= col[r] * x[i];
+    }
+}
 
 template <int DK, int DVT, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
@@ -286,14 +307,17 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
             // fw = 1 / (t_sb ... t_{h-1}) below the middle h = NSB/2 and
             // t_h ... t_{sb-1} from it on (t_b: row block b's product): no
             // product over more than half a chunk is formed
-            float fw[CPT];
+            // lo = Pm = P_31 and hi = Pn / Pm of the lane's channels
+            float fw[CPT], lo[CPT], hi[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                float lo = 1.f, hi = 1.f, f = 1.f;
+                float f = 1.f;
+                lo[c] = 1.f;
+                hi[c] = 1.f;
 #pragma unroll
                 for (int b = 0; b < NSB / 2; ++b) {
-                    lo *= tot(b, c0 + c);
-                    hi *= tot(NSB / 2 + b, c0 + c);
+                    lo[c] *= tot(b, c0 + c);
+                    hi[c] *= tot(NSB / 2 + b, c0 + c);
                 }
                 if (sb < NSB / 2) {
                     for (int b = sb; b < NSB / 2; ++b) f *= tot(b, c0 + c);
@@ -302,7 +326,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                     for (int b = NSB / 2; b < sb; ++b) f *= tot(b, c0 + c);
                 }
                 fw[c] = f;
-                if (sb == 0) bad |= decay_out_of_range(lo, hi);
+                if (sb == 0) bad |= decay_out_of_range(lo[c], hi[c]);
             }
             Top wct[CPT][RPW], ect[CPT][RPW];
 #pragma unroll
@@ -348,6 +372,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                 M::st4(sZT + ((jb0 + jj) * 16 + ln) * LDC2 + rb * 16 + lg * 4, x);
             }
             // SP = (Pm * S0)^T and the per-row decays kept for the state update
+            // (Pm and Pn / Pm of channel c come from lane c / CPT)
 #pragma unroll
             for (int i = 0; i < STW; ++i) {
                 const int st = w + NW * i;
@@ -356,17 +381,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                     f32x4 sp;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int c = ct * 16 + lg * 4 + e;
-                        float pm = 1.f, pnm = 1.f;
-#pragma unroll
-                        for (int b = 0; b < NSB / 2; ++b) pm *= tot(b, c);
-                        float pn = pm;
-#pragma unroll
-                        for (int b = NSB / 2; b < NSB; ++b) {
-                            pn *= tot(b, c);
-                            pnm *= tot(b, c);
-                        }
-                        pn_s[i][e] = pn;
+                        const int src = (ct * 16 + lg * 4 + e) / CPT;
+                        const float pm = __shfl(lo[e % CPT], src, 64);
+                        const float pnm = __shfl(hi[e % CPT], src, 64);
+                        pn_s[i][e] = pm * pnm;
                         pnm_s[i][e] = pnm;  // Pn / Pm
                         sp[e] = pm * S[i][e];
                     }
@@ -381,10 +399,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
         // ================= phase 1: Gram blocks, X = Kr SP and OI = Qr SP =====
         f32x4 xr[NJW], oi[NJW];
         {
-            // jobs (a, b), b <= a, round-robin over the waves; transposed tiles
-            // F_b Kr_a^T give each lane 4 consecutive i of row r = 16a + ln
-#pragma unroll
-            for (int jn = w; jn < 10; jn += NW) {
+            // Gram jobs (a, b), b <= a; transposed tiles F_b Kr_a^T give each
+            // lane 4 consecutive i of row r = 16a + ln.  A job forms the L part
+            // (L_a, L_c from Kr) and the M part (M_a, M_c from Qr), or one of them.
+            auto gram = [&](int jn, bool doL, bool doM) {
                 const int a = (jn >= 6) ? 3 : (jn >= 3) ? 2 : (jn >= 1) ? 1 : 0;
                 const int b = jn - a * (a + 1) / 2;
                 f32x4 cLa = zero4(), cLc = zero4(), cMa = zero4(), cMc = zero4();
@@ -392,35 +410,77 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                 for (int s = 0; s < DK / 32; ++s) {
                     const auto fe = M::ld32(sEc + (b * 16 + ln) * LDK + s * 32 + lg * 8);
                     const auto fw = M::ld32(sWc + (b * 16 + ln) * LDK + s * 32 + lg * 8);
-                    const auto fk = M::ld32(sKr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
-                    const auto fq = M::ld32(sQr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
-                    cLa = M::k32(fe, fk, cLa);
-                    cLc = M::k32(fw, fk, cLc);
-                    cMa = M::k32(fe, fq, cMa);
-                    cMc = M::k32(fw, fq, cMc);
+                    if (doL) {
+                        const auto fk = M::ld32(sKr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
+                        cLa = M::k32(fe, fk, cLa);
+                        cLc = M::k32(fw, fk, cLc);
+                    }
+                    if (doM) {
+                        const auto fq = M::ld32(sQr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
+                        cMa = M::k32(fe, fq, cMa);
+                        cMc = M::k32(fw, fq, cMc);
+                    }
                 }
                 const int r = a * 16 + ln;
                 if (a == b) {
-                    // the diagonal block, strictly lower, stored by columns
+                    if (doL) {
+                        // the diagonal block, strictly lower, stored by columns
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sLd[(a * 16 + lg * 4 + e) * L::LDL + ln] = (lg * 4 + e < ln) ? cLa[e] : 0.f;
-                    f32x4 lc, mc, ma;
+                        for (int e = 0; e < 4; ++e)
+                            sLd[(a * 16 + lg * 4 + e) * L::LDL + ln] = (lg * 4 + e < ln) ? cLa[e] : 0.f;
+                        f32x4 lc;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lc[e] = (lg * 4 + e < ln) ? cLc[e] : 0.f;
-                        mc[e] = (lg * 4 + e <= ln) ? cMc[e] : 0.f;
-                        ma[e] = (lg * 4 + e <= ln) ? cMa[e] : 0.f;
+                        for (int e = 0; e < 4; ++e) lc[e] = (lg * 4 + e < ln) ? cLc[e] : 0.f;
+                        M::st4(sAc + r * LDC + b * 16 + lg * 4, lc);
                     }
-                    M::st4(sAc + r * LDC + b * 16 + lg * 4, lc);
-                    M::st4(sM + r * LDC2 + b * 16 + lg * 4, mc);
-                    M::st4(sM + r * LDC2 + CH + b * 16 + lg * 4, ma);
+                    if (doM) {
+                        f32x4 mc, ma;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            mc[e] = (lg * 4 + e <= ln) ? cMc[e] : 0.f;
+                            ma[e] = (lg * 4 + e <= ln) ? cMa[e] : 0.f;
+                        }
+                        M::st4(sM + r * LDC2 + b * 16 + lg * 4, mc);
+                        M::st4(sM + r * LDC2 + CH + b * 16 + lg * 4, ma);
+                    }
                 } else {
-                    M::st4(sLo + r * LDC + b * 16 + lg * 4, cLa);
-                    M::st4(sAc + r * LDC + b * 16 + lg * 4, cLc);
-                    M::st4(sM + r * LDC2 + b * 16 + lg * 4, cMc);
-                    M::st4(sM + r * LDC2 + CH + b * 16 + lg * 4, cMa);
+                    if (doL) {
+                        M::st4(sLo + r * LDC + b * 16 + lg * 4, cLa);
+                        M::st4(sAc + r * LDC + b * 16 + lg * 4, cLc);
+                    }
+                    if (doM) {
+                        M::st4(sM + r * LDC2 + b * 16 + lg * 4, cMc);
+                        M::st4(sM + r * LDC2 + CH + b * 16 + lg * 4, cMa);
+                    }
                 }
+            };
+            if constexpr (NW == 8) {
+                if (hf == 0) {
+                    // diagonal block rb, then its inverse D = (I + L_aa)^{-1}
+                    // (lane (ln, any lg) forms column ln), which replaces
+                    // L_aa in LDS, by columns
+                    gram(rb * (rb + 3) / 2, true, true);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    float* La = sLd + rb * 16 * L::LDL;
+                    float x[16];
+                    unit_lower_solve(La, L::LDL, ln, x);
+                    if (lg == 0) {
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4)
+                            *reinterpret_cast<float4*>(La + ln * L::LDL + r4 * 4) =
+                                make_float4(x[r4 * 4], x[r4 * 4 + 1], x[r4 * 4 + 2], x[r4 * 4 + 3]);
+                    }
+                } else {
+                    // the six off-diagonal jobs: (1,0) or (2,0) or (2,1) or
+                    // (3,0) whole, and half of (3,2) or (3,1)
+                    gram(rb == 0 ? 1 : rb == 1 ? 3 : rb == 2 ? 4 : 6, true, true);
+                    gram(rb < 2 ? 8 : 7, (rb & 1) == 0, (rb & 1) != 0);
+                }
+            } else {
+#pragma unroll
+                for (int jn = w; jn < 10; jn += NW) gram(jn, true, true);
             }
 #pragma unroll
             for (int jj = 0; jj < NJW; ++jj) {
@@ -459,72 +519,106 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                 }
                 M::st4(sYT + (jb * 16 + ln) * LDC + rb * 16 + lg * 4, cy);
             }
-            // the first four waves form T's column blocks
-            if (hf == 0) {
-                // diagonal blocks: lane (block lg, column ln) solves L_aa x = e_ln
-                // (column i of the block: rows 0..15 at La + i LDL)
-                float x[16];
-                const float* La = sLd + lg * 16 * L::LDL;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 0; i < 15; ++i) {
-                    float col[16];
-#pragma unroll
-                    for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
-                        const float4 v4 = *reinterpret_cast<const float4*>(La + i * L::LDL + q4 * 4);
-                        col[q4 * 4] = v4.x; col[q4 * 4 + 1] = v4.y; col[q4 * 4 + 2] = v4.z; col[q4 * 4 + 3] = v4.w;
+            if constexpr (NW == 8) {
+                // the first four waves form T's column blocks from the
+                // inverses D_a left in LDS by columns (rounded to the operand
+                // type where they are used)
+                if (hf == 0) {
+                    const int b = rb;
+                    f32x4 TB[4];
+                    {
+                        const float4 d4 = *reinterpret_cast<const float4*>(sLd + (b * 16 + ln) * L::LDL + lg * 4);
+                        TB[0][0] = to_f32(from_f32<Top>(d4.x)); TB[0][1] = to_f32(from_f32<Top>(d4.y));
+                        TB[0][2] = to_f32(from_f32<Top>(d4.z)); TB[0][3] = to_f32(from_f32<Top>(d4.w));
                     }
 #pragma unroll
-                    for (int r = i + 1; r < 16; ++r) x[r] -= col[r] * x[i];
-                }
-                Top* Dr = sDr + (size_t)rb * 4 * 16 * LDD;
-                Top* Dc = sDc + (size_t)rb * 4 * 16 * LDD;
+                    for (int d = 1; d < 4; ++d) {
+                        const int a = b + d;
+                        if (a < 4) {
+                            f32x4 y = zero4();
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Dr[(lg * 16 + r) * LDD + ln] = from_f32<Top>(x[r]);
+                            for (int jd = 0; jd < d; ++jd) {
+                                const int j = b + jd;
+                                const auto fa = M::ld16(sLo + (a * 16 + ln) * LDC + j * 16 + lg * 4);
+                                y = M::k16(fa, M::pack16(TB[jd]), y);
+                            }
+                            f32x4 dr;
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    f32x4 t4 = {x[r4 * 4], x[r4 * 4 + 1], x[r4 * 4 + 2], x[r4 * 4 + 3]};
-                    M::st4(Dc + (lg * 16 + ln) * LDD + r4 * 4, t4);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-                // column block b = rb: T_bb = D_b, T_ab = -D_a sum_{j=b}^{a-1} L_aj T_jb
-                const int b = rb;
-                f32x4 TB[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) TB[0][e] = to_f32(Dc[(b * 16 + ln) * LDD + lg * 4 + e]);
-#pragma unroll
-                for (int d = 1; d < 4; ++d) {
-                    const int a = b + d;
-                    if (a < 4) {
-                        f32x4 y = zero4();
-#pragma unroll
-                        for (int jd = 0; jd < d; ++jd) {
-                            const int j = b + jd;
-                            const auto fa = M::ld16(sLo + (a * 16 + ln) * LDC + j * 16 + lg * 4);
-                            y = M::k16(fa, M::pack16(TB[jd]), y);
+                            for (int e = 0; e < 4; ++e) dr[e] = sLd[(a * 16 + lg * 4 + e) * L::LDL + ln];
+                            f32x4 t = M::k16(M::pack16(dr), M::pack16(y), zero4());
+                            TB[d][0] = -t[0]; TB[d][1] = -t[1]; TB[d][2] = -t[2]; TB[d][3] = -t[3];
                         }
-                        const auto fd = M::ld16(Dr + (a * 16 + ln) * LDD + lg * 4);
-                        f32x4 t = M::k16(fd, M::pack16(y), zero4());
-                        TB[d][0] = -t[0]; TB[d][1] = -t[1]; TB[d][2] = -t[2]; TB[d][3] = -t[3];
                     }
-                }
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const int a = b + d;
-                    if (a < 4) {
+                    for (int d = 0; d < 4; ++d) {
+                        const int a = b + d;
+                        if (a < 4) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(TB[d][e]);
+                        }
+                    }
+                    for (int a = 0; a < b; ++a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(TB[d][e]);
+                            sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(0.f);
                     }
                 }
-                for (int a = 0; a < b; ++a) {
+            } else {
+                // the first four waves form T's column blocks
+                if (hf == 0) {
+                    // diagonal blocks: lane (block lg, column ln) forms column ln
+                    // of D_lg = (I + L_aa)^{-1}
+                    float x[16];
+                    unit_lower_solve(sLd + lg * 16 * L::LDL, L::LDL, ln, x);
+                    Top* Dr = sDr + (size_t)rb * 4 * 16 * LDD;
+                    Top* Dc = sDc + (size_t)rb * 4 * 16 * LDD;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(0.f);
+                    for (int r = 0; r < 16; ++r) Dr[(lg * 16 + r) * LDD + ln] = from_f32<Top>(x[r]);
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        f32x4 t4 = {x[r4 * 4], x[r4 * 4 + 1], x[r4 * 4 + 2], x[r4 * 4 + 3]};
+                        M::st4(Dc + (lg * 16 + ln) * LDD + r4 * 4, t4);
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+                    // column block b = rb: T_bb = D_b, T_ab = -D_a sum_{j=b}^{a-1} L_aj T_jb
+                    const int b = rb;
+                    f32x4 TB[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) TB[0][e] = to_f32(Dc[(b * 16 + ln) * LDD + lg * 4 + e]);
+#pragma unroll
+                    for (int d = 1; d < 4; ++d) {
+                        const int a = b + d;
+                        if (a < 4) {
+                            f32x4 y = zero4();
+#pragma unroll
+                            for (int jd = 0; jd < d; ++jd) {
+                                const int j = b + jd;
+                                const auto fa = M::ld16(sLo + (a * 16 + ln) * LDC + j * 16 + lg * 4);
+                                y = M::k16(fa, M::pack16(TB[jd]), y);
+                            }
+                            const auto fd = M::ld16(Dr + (a * 16 + ln) * LDD + lg * 4);
+                            f32x4 t = M::k16(fd, M::pack16(y), zero4());
+                            TB[d][0] = -t[0]; TB[d][1] = -t[1]; TB[d][2] = -t[2]; TB[d][3] = -t[3];
+                        }
+                    }
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const int a = b + d;
+                        if (a < 4) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(TB[d][e]);
+                        }
+                    }
+                    for (int a = 0; a < b; ++a) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sTm[(a * 16 + lg * 4 + e) * LDC + b * 16 + ln] = from_f32<Top>(0.f);
+                    }
                 }
             }
         }
