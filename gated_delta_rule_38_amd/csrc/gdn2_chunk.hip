@@ -44,7 +44,7 @@
 // each holds two state tiles; the phases are chains of dependent matrix-core
 // products and LDS round trips, which the second wave on a SIMD overlaps.
 // There the diagonal blocks of L_a are inverted in the Gram phase, each by
-// the wave that formed it, while the other four waves take the off-diagonal
+// the wave that formed it, while the other four waves take the rest of the
 // Gram blocks.  Other shapes run four waves.
 #include "chunk_walk.h"
 
@@ -456,10 +456,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
             };
             if constexpr (NW == 8) {
                 if (hf == 0) {
-                    // diagonal block rb, then its inverse D = (I + L_aa)^{-1}
-                    // (lane (ln, any lg) forms column ln), which replaces
-                    // L_aa in LDS, by columns
-                    gram(rb * (rb + 3) / 2, true, true);
+                    // the L part of diagonal block rb, then its inverse
+                    // D = (I + L_aa)^{-1} (lane (ln, any lg) forms column ln),
+                    // which replaces L_aa in LDS, by columns
+                    gram(rb * (rb + 3) / 2, true, false);
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -474,9 +474,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                     }
                 } else {
                     // the six off-diagonal jobs: (1,0) or (2,0) or (2,1) or
-                    // (3,0) whole, and half of (3,2) or (3,1)
+                    // (3,0) whole, and half of (3,2) or (3,1); and the M part
+                    // of diagonal block rb
                     gram(rb == 0 ? 1 : rb == 1 ? 3 : rb == 2 ? 4 : 6, true, true);
                     gram(rb < 2 ? 8 : 7, (rb & 1) == 0, (rb & 1) != 0);
+                    gram(rb * (rb + 3) / 2, false, true);
                 }
             } else {
 #pragma unroll
