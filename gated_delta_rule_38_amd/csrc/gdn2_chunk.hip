@@ -178,6 +178,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
     // the LDS of L_a's diagonal blocks (phases 1-2)
     static_assert((size_t)NSB * DK * 4 <= (size_t)4 * 16 * L::LDL * 4, "decay totals");
     auto tot = [&](int b, int c) -> float& { return sLd[b * DK + c]; };
+    // [row][channel] tiles at dk = 128: the 16-byte chunk c of row r sits at
+    // chunk (c + 7 (r mod 2)) mod 16, which spreads fragment reads of 16 rows
+    // over all LDS banks (the plain 272-byte rows pair them two by two)
+    auto tk = [&](int row, int ch) -> int {
+        if constexpr (DK == 128) return row * LDK + ((((ch >> 3) + 7 * (row & 1)) & 15) << 3) + (ch & 7);
+        else return row * LDK + ch;
+    };
 
     const WorkItem wi = decode_work(p);
     if (!wi.valid) return;
@@ -352,10 +359,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                     ect[c][r] = ec[c];
                     wct[c][r] = wc[c];
                 }
-                store_run<Top, CPT>(sKr + row * LDK + c0, kr);
-                store_run<Top, CPT>(sQr + row * LDK + c0, qr);
-                store_run<Top, CPT>(sEc + row * LDK + c0, ec);
-                store_run<Top, CPT>(sWc + row * LDK + c0, wc);
+                store_run<Top, CPT>(sKr + tk(row, c0), kr);
+                store_run<Top, CPT>(sQr + tk(row, c0), qr);
+                store_run<Top, CPT>(sEc + tk(row, c0), ec);
+                store_run<Top, CPT>(sWc + tk(row, c0), wc);
             }
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                         pnm_s[i][e] = pnm;  // Pn / Pm
                         sp[e] = pm * S[i][e];
                     }
-                    M::st4(sSP + (jj * 16 + ln) * LDK + ct * 16 + lg * 4, sp);
+                    M::st4(sSP + tk(jj * 16 + ln, ct * 16 + lg * 4), sp);
                 }
             }
         }
@@ -408,15 +415,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                 f32x4 cLa = zero4(), cLc = zero4(), cMa = zero4(), cMc = zero4();
 #pragma unroll
                 for (int s = 0; s < DK / 32; ++s) {
-                    const auto fe = M::ld32(sEc + (b * 16 + ln) * LDK + s * 32 + lg * 8);
-                    const auto fw = M::ld32(sWc + (b * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fe = M::ld32(sEc + tk(b * 16 + ln, s * 32 + lg * 8));
+                    const auto fw = M::ld32(sWc + tk(b * 16 + ln, s * 32 + lg * 8));
                     if (doL) {
-                        const auto fk = M::ld32(sKr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
+                        const auto fk = M::ld32(sKr + tk(a * 16 + ln, s * 32 + lg * 8));
                         cLa = M::k32(fe, fk, cLa);
                         cLc = M::k32(fw, fk, cLc);
                     }
                     if (doM) {
-                        const auto fq = M::ld32(sQr + (a * 16 + ln) * LDK + s * 32 + lg * 8);
+                        const auto fq = M::ld32(sQr + tk(a * 16 + ln, s * 32 + lg * 8));
                         cMa = M::k32(fe, fq, cMa);
                         cMc = M::k32(fw, fq, cMc);
                     }
@@ -490,9 +497,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gdn2_chunk_kernel(G2Params gp) {
                 f32x4 cx = zero4(), co = zero4();
 #pragma unroll
                 for (int s = 0; s < DK / 32; ++s) {
-                    const auto fs = M::ld32(sSP + (jb * 16 + ln) * LDK + s * 32 + lg * 8);
-                    const auto fk = M::ld32(sKr + (rb * 16 + ln) * LDK + s * 32 + lg * 8);
-                    const auto fq = M::ld32(sQr + (rb * 16 + ln) * LDK + s * 32 + lg * 8);
+                    const auto fs = M::ld32(sSP + tk(jb * 16 + ln, s * 32 + lg * 8));
+                    const auto fk = M::ld32(sKr + tk(rb * 16 + ln, s * 32 + lg * 8));
+                    const auto fq = M::ld32(sQr + tk(rb * 16 + ln, s * 32 + lg * 8));
                     cx = M::k32(fk, fs, cx);
                     co = M::k32(fq, fs, co);
                 }
