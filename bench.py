@@ -388,9 +388,13 @@ def main():
         nst = dd["cu_seqlens"].numel() - 1 if dd["cu_seqlens"] is not None else c.B
         ol = torch.empty_like(dd["v"])
         fl_ = torch.empty((nst, c.H, c.dk, c.dv), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(1, kda.kda_chunk_fwd_workspace_size(
-            1, toks, c.H, c.dk, c.dv, nst if dd["cu_seqlens"] is not None else 0)),
-            dtype=torch.uint8, device=dev)
+        wsb = kda.kda_chunk_fwd_workspace_size(1, toks, c.H, c.dk, c.dv,
+                                               nst if dd["cu_seqlens"] is not None else 0)
+        # dense shapes with few units and long sequences take the two-segment
+        # path when the workspace holds its buffers
+        split_b = 0 if dd["cu_seqlens"] is not None else kda.kda_chunk_fwd_split_workspace_size(
+            c.B, c.T, c.H, c.dk, c.dv)
+        ws = torch.empty(max(1, wsb, split_b), dtype=torch.uint8, device=dev)
 
         def lstep():
             kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"],
@@ -403,6 +407,7 @@ def main():
                 "kda_chunk_fwd bf16 varlen: 64 packed sequences, lengths U{128..8192} "
                 "(%d tokens), H16 dk128 dv128, initial states N(0,0.02)" % toks)
         out[name] = {"workload": desc, "ms_per_step": lms, "tokens_per_s": toks / (lms / 1e3),
+                     "path": "two time segments at once" if split_b else "single pass",
                      "roofline": roofline(chunk_bytes(toks, c.H, c.dk, c.dv, nst,
                                                       initial=dd["initial_state"] is not None),
                                           lms,

@@ -18,7 +18,8 @@ __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused",
            "kda_gdn2_recurrent_step", "kda_recurrent_step",
            "kda_recurrent_step_gated", "kda_recurrent_step_fused", "kda_backward",
            "kda_backward_workspace_size", "kda_chunk_fwd_workspace_size",
-           "kda_status_string", "kda_version", "KDAError", "LIB_PATH", "load_library"]
+           "kda_chunk_fwd_split_workspace_size", "kda_status_string", "kda_version",
+           "KDAError", "LIB_PATH", "load_library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -98,6 +99,8 @@ def _bind_signatures(lib):
     lib.kda_backward_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_chunk_fwd_split_workspace_size.restype = sz
+    lib.kda_chunk_fwd_split_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i]
     lib.kda_version.restype = i
@@ -149,6 +152,13 @@ def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype=torch.bfloat16
     return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, code))
 
 
+def kda_chunk_fwd_split_workspace_size(B, T, H, dk, dv, dtype=torch.bfloat16):
+    """Workspace bytes with which a dense call runs in two time segments (0: the
+    shape does not qualify)."""
+    code = KDA_DTYPE_BF16 if dtype == torch.bfloat16 else KDA_DTYPE_F32
+    return int(load_library().kda_chunk_fwd_split_workspace_size(B, T, H, dk, dv, code))
+
+
 def _gate_code(gate):
     if isinstance(gate, str):
         if gate not in _GATES:
@@ -176,7 +186,7 @@ def _fuse_flags(gate_logits, beta_logits, qk_l2norm):
 
 def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
                   cu_seqlens_host=None, scale=None, output_final_state=True,
-                  final_state=None, o=None, chunk_size=64, workspace=None):
+                  final_state=None, o=None, chunk_size=64, workspace=None, split=True):
     """Chunk-wise KDA forward.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype);
@@ -188,39 +198,47 @@ def kda_chunk_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
     in-place update); o may be passed as a preallocated output, and
     workspace as a uint8 device tensor of at least
     kda_chunk_fwd_workspace_size() bytes (else one is allocated per call).
+    With split (the default), a dense call allocates the workspace of the
+    two-segment path when the shape qualifies
+    (kda_chunk_fwd_split_workspace_size); split=False keeps the single pass
+    (a passed workspace is then announced with its minimum size only).
     Returns (o, final_state or None).
     """
     return _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
-                      output_final_state, final_state, o, chunk_size, workspace, None)
+                      output_final_state, final_state, o, chunk_size, workspace, None,
+                      split=split)
 
 
 def kda_chunk_fwd_gated(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
                         cu_seqlens_host=None, scale=None, output_final_state=True,
                         final_state=None, o=None, chunk_size=64, workspace=None,
-                        gate="channel"):
+                        gate="channel", split=True):
     """kda_chunk_fwd with the forget gate's granularity chosen by ``gate``:
     "channel" (alpha [B, T, H, dk], KDA), "head" (alpha [B, T, H], Gated
     DeltaNet) or "none" (alpha None, DeltaNet)."""
     return _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
-                      output_final_state, final_state, o, chunk_size, workspace, _gate_code(gate))
+                      output_final_state, final_state, o, chunk_size, workspace, _gate_code(gate),
+                      split=split)
 
 
 def kda_chunk_fwd_fused(q, k, v, gate, beta, initial_state=None, cu_seqlens=None,
                         cu_seqlens_host=None, scale=None, output_final_state=True,
                         final_state=None, o=None, chunk_size=64, workspace=None,
                         gate_kind="channel", gate_logits=True, beta_logits=True,
-                        qk_l2norm=True):
+                        qk_l2norm=True, split=True):
     """kda_chunk_fwd_gated with the inputs prepared in the kernel: ``gate``
     holds logits (dtype of q, alpha = sigmoid) when gate_logits, else float32
     alpha; ``beta`` holds logits (beta = sigmoid) when beta_logits; q and k
     are L2-normalised per token and head when qk_l2norm."""
     return _chunk_fwd(q, k, v, gate, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
                       output_final_state, final_state, o, chunk_size, workspace,
-                      _gate_code(gate_kind), _fuse_flags(gate_logits, beta_logits, qk_l2norm))
+                      _gate_code(gate_kind), _fuse_flags(gate_logits, beta_logits, qk_l2norm),
+                      split=split)
 
 
 def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host, scale,
-               output_final_state, final_state, o, chunk_size, workspace, gate, flags=None):
+               output_final_state, final_state, o, chunk_size, workspace, gate, flags=None,
+               split=True):
     lib = load_library()
     dev = q.device
     dt = q.dtype
@@ -265,8 +283,11 @@ def _chunk_fwd(q, k, v, alpha, beta, initial_state, cu_seqlens, cu_seqlens_host,
         if workspace.numel() < ws_bytes:
             raise ValueError("workspace holds %d bytes, the call needs %d" % (workspace.numel(), ws_bytes))
         ws = workspace
-        ws_bytes = workspace.numel()
+        ws_bytes = workspace.numel() if split else ws_bytes
     else:
+        if split and num_seqs == 0:
+            ws_bytes = max(ws_bytes, int(lib.kda_chunk_fwd_split_workspace_size(B, T, H, dk, dv,
+                                                                                code)))
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     common = (float(scale) if scale is not None else 0.0, int(chunk_size), _ptr(ws), ws_bytes,
               _stream(dev))

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_sizes.cpp", "chunk_fwd.hip", "chunk_fwd_bf16.hip",
            "recurrent_step.hip", "backward.hip", "bwd_chunk.hip", "gdn2_step.hip",
-           "gdn2_chunk.hip"]
+           "gdn2_chunk.hip", "chunk_split.hip"]
 ARCH = "gfx950"
 
 

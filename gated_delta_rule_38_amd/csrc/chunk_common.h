@@ -26,6 +26,12 @@ struct KParams {
     // the state at the start of every chunk and after the last one, for the
     // chunk-form backward (slots as laid out in chunk_fwd.hip), or NULL
     float *ckpt = nullptr;
+    // dense calls: tokens taken from each sequence, the first t_len of its T
+    // rows from the base pointers (-1: all T)
+    int t_len = -1;
+    // the transition part of a time segment: the same recurrence started from
+    // the identity (dv == dk) with every value read as zero (s0 unused)
+    bool ident = false;
 };
 
 struct WorkItem {
@@ -56,7 +62,7 @@ __device__ __forceinline__ WorkItem decode_work(const KParams& p) {
         wi.len = p.cu_seqlens[wi.seq + 1] - (int)wi.t0;
     } else {
         wi.t0 = (long)wi.seq * p.T;
-        wi.len = p.T;
+        wi.len = p.t_len >= 0 ? p.t_len : p.T;
     }
     return wi;
 }

@@ -718,6 +718,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
     const int nseq = a.cu_seqlens ? a.num_seqs : a.B;
     const int units = nseq * a.H;
     if (units == 0) return hipSuccess;
+    if (a.split_ws) return launch_chunk_split(a, a.split_ws, stream);
     const int* order = nullptr;
     if (a.cu_seqlens && a.order) {
         hipError_t e = launch_order_sequences(a.cu_seqlens, a.num_seqs, a.order, stream);

@@ -358,6 +358,9 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     // byte strides of one token row
     const uint32_t rsq = (uint32_t)H * DK * 2, rsa = (uint32_t)H * DK * (GL ? 2 : 4);
     const uint32_t rsb = (uint32_t)H * 4, rsv = (uint32_t)H * DV * 2;
+    // The transition part of a time segment (p.ident) reads no values: its
+    // value descriptors get an empty range, so every load of v returns zero.
+    const uint32_t vlim = p.ident ? 0u : ~0u;
 
     const bf16_t* __restrict__ gq = static_cast<const bf16_t*>(p.q);
     const bf16_t* __restrict__ gk = static_cast<const bf16_t*>(p.k);
@@ -378,7 +381,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
     auto redo = [&]() {
         WalkArgs wa{};
         wa.q = p.q; wa.k = p.k; wa.v = p.v; wa.alpha = p.alpha; wa.beta = p.beta;
-        wa.s0 = p.s0; wa.o = p.o; wa.sT = p.sT; wa.ckpt = p.ckpt;
+        wa.s0 = p.s0; wa.o = p.o; wa.sT = p.sT; wa.ckpt = p.ckpt; wa.ident = p.ident;
         wa.H = H; wa.dv = DV; wa.gate = GATE; wa.fuse = p.fuse; wa.scale = p.scale;
         __threadfence();  // this item's stores so far land before the walk's
         __syncthreads();
@@ -842,7 +845,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const size_t tok = (size_t)(t0 + (long)ch * CH) * H + h;
             const Rsrc rb = make_rsrc(gb + tok, (uint32_t)nr * rsb);
             HB = __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lx * rsb, 0, 0);
-            const Rsrc rv = make_rsrc(gv + tok * DV + jt * DVT, (uint32_t)nr * rsv);
+            const Rsrc rv = make_rsrc(gv + tok * DV + jt * DVT, ((uint32_t)nr * rsv) & vlim);
             const uint32_t vo = (uint32_t)(RPV * rq) * rsv + (uint32_t)cg * 16;
 #pragma unroll
             for (int i = 0; i < RPV; ++i) {
@@ -957,7 +960,7 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
             const uint32_t row = (uint32_t)(jt * (CH / njt) + lx / njt), sub = (uint32_t)(lx % njt);
             const Rsrc rq = make_rsrc(gq + tok * DK, (uint32_t)nr * rsq);
             const Rsrc rk = make_rsrc(gk + tok * DK, (uint32_t)nr * rsq);
-            const Rsrc rv = make_rsrc(gv + tok * DV, (uint32_t)nr * rsv);
+            const Rsrc rv = make_rsrc(gv + tok * DV, ((uint32_t)nr * rsv) & vlim);
             r[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, row * rsq + (sub & 1) * 128, 0, 0);
             r[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, row * rsq + (sub & 1) * 128, 0, 0);
             if constexpr (GATE == 0) {  // 512-byte rows (256 with bf16 logits)
@@ -1043,7 +1046,11 @@ __global__ __launch_bounds__((Lay6<DK, DVT>::NTH), 1) void chunk_fwd_bf16_kernel
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             S[j][ct] = zero4();
-            if (p.s0) {
+            if (p.ident) {  // the identity's columns (dv == dk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[j][ct][e] = state_ch(ct, lg, e) == col + 16 * j ? 1.f : 0.f;
+            } else if (p.s0) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     S[j][ct][e] = p.s0[sbase + (size_t)state_ch(ct, lg, e) * DV + col + 16 * j];

@@ -43,6 +43,7 @@ struct WalkArgs {
     int gate;     // 0 per key channel, 1 per head, 2 none (alpha NULL in Gated DeltaNet-2)
     int fuse;     // FUSE_* bits (KDA only)
     float scale;
+    bool ident = false;  // start from the identity (dv == dk) with every value zero
 };
 
 template <int DVT, int NTHR, bool GDN2>
@@ -63,8 +64,9 @@ struct WalkShape {
 //   KDA:       u = beta (v - vh),  S = S~ + k u^T,  o = scale (p + (k.q) u)
 //   DeltaNet-2: S = S~ - (e k) vh^T + (w k) v^T,    o = scale (p - ((e k).q) vh + ((w k).q) v)
 // (with FUSE_QK_L2NORM, k and q are first divided by their norms; every sum
-// over the key channels is formed once per token).  lds: lds_bytes of
-// WalkShape, free for the walk.
+// over the key channels is formed once per token).  With a.ident the walk
+// starts from the identity instead of a.s0 and reads every value as zero.
+// lds: lds_bytes of WalkShape, free for the walk.
 template <typename Tin, int DK, int DVT, int NTHR, bool GDN2>
 __device__ __forceinline__ void token_walk(const WalkArgs& a, int seq, int h, long t0, int len,
                                            int col0, float* lds) {
@@ -95,7 +97,9 @@ __device__ __forceinline__ void token_walk(const WalkArgs& a, int seq, int h, lo
     float S[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        S[i] = (act && a.s0) ? a.s0[sbase + (size_t)(r0 + i) * DV + col0 + c] : 0.f;
+        S[i] = !act ? 0.f
+             : a.ident ? (r0 + i == col0 + c ? 1.f : 0.f)
+             : a.s0 ? a.s0[sbase + (size_t)(r0 + i) * DV + col0 + c] : 0.f;
     auto store_state = [&](float* dst) {
         if (!act) return;
 #pragma unroll
@@ -158,7 +162,7 @@ __device__ __forceinline__ void token_walk(const WalkArgs& a, int seq, int h, lo
             for (int s = 0; s < NSLOT; ++s)
 #pragma unroll
                 for (int j = 0; j < NR; ++j) tot[j] += red[(s * DVT + c) * NR + j];
-            const float vv = to_f32(gv[tok * DV + col0 + c]);
+            const float vv = a.ident ? 0.f : to_f32(gv[tok * DV + col0 + c]);
             float ov;
             if constexpr (GDN2) {
                 const float vh = tot[0];

@@ -121,6 +121,12 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int num
     return ((size_t)num_seqs * 4 + 255) / 256 * 256;
 }
 
+size_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int dk, int dv,
+                                          kda_dtype dtype) {
+    if (B < 0 || T < 0 || H < 0 || dtype != KDA_DTYPE_BF16) return 0;
+    return kda::chunk_split_plan(B, T, H, dk, dv).bytes;
+}
+
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                          const float* beta, const float* initial_state, void* o,
                          float* final_state, int B, int T, int H, int dk, int dv,
@@ -358,10 +364,18 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
         for (const void* ptr : words)
             if (!aligned(ptr, 4)) return KDA_ERROR_MISALIGNED;
 
-        const size_t need_ws =
+        const size_t min_ws =
             noalloc ? 0 : kda_chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, dtype);
-        if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+        if (min_ws > 0 && (!workspace || workspace_bytes < min_ws))
             return KDA_ERROR_INSUFFICIENT_WORKSPACE;
+        // Dense bf16 calls whose workspace holds the two-segment path's
+        // buffers (256-byte aligned) take that path when o allows its 8-byte
+        // accesses; overrides of the kernel choice keep the single pass.
+        const size_t split_ws = (noalloc || varlen || env_generic() || env_dvt())
+                                    ? 0 : kda_chunk_fwd_split_workspace_size(B, T, H, dk, dv, dtype);
+        const bool split = split_ws > 0 && workspace && workspace_bytes >= split_ws &&
+                           aligned(workspace, 256) && aligned(o, 8);
+        const size_t need_ws = split ? split_ws : min_ws;
 
         // outputs must not overlap inputs, each other or the workspace; the one
         // allowed alias is an in-place state (final_state == initial_state)
@@ -393,6 +407,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
         a.cu_seqlens = varlen ? cu_seqlens_dev : nullptr;
         a.num_seqs = varlen ? num_seqs : 0;
         a.order = (varlen && num_seqs <= 65536) ? static_cast<int*>(workspace) : nullptr;
+        a.split_ws = split ? workspace : nullptr;
         if (noalloc && varlen) {
             int* order = nullptr;
             if (kda::noalloc_order_buffer(stream, &order) != hipSuccess) return KDA_ERROR_HIP;

@@ -41,9 +41,22 @@ struct ChunkArgs {
     int dvt;                // value columns per workgroup (0 = choose)
     bool generic;           // bf16 through the generic kernel (A/B checks)
     float *ckpt = nullptr;  // chunk-start states for the backward (generic kernel), or NULL
+    void *split_ws = nullptr;  // workspace of the two-segment path (chunk_split_plan), or NULL
 };
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
+
+// Dense bf16 calls with few (sequence, head) units and long sequences run in
+// two time segments at once (chunk_split.hip).  The plan: the first segment's
+// tokens per sequence (a multiple of the chunk), the second's, and the
+// workspace layout; bytes == 0 when the shape does not qualify.
+struct SplitPlan {
+    int l0 = 0, l1 = 0;
+    size_t off_sm = 0, off_phi = 0, off_r = 0, off_z = 0, bytes = 0;
+};
+SplitPlan chunk_split_plan(int B, int T, int H, int dk, int dv);
+// the chunk-wise forward in two time segments; ws holds chunk_split_plan().bytes
+hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t stream);
 
 // Sequences a call of kda_chunk_fwd_noalloc may pack: the size of the device
 // array that holds their order in place of a caller workspace.

@@ -35,4 +35,30 @@ size_t bwd_chunk_workspace_bytes(long tokens_total, int nseq, int H, int dk, int
            (size_t)(dv / 32 - 1) * (3 * nk + nb) * 4;
 }
 
+// The two-segment path (chunk_split.hip) pays when the single pass cannot give
+// the chip wide slices: eight workgroups per unit (four 32-column slices of the
+// first segment, two 64-column slices each of the second segment's transition
+// and zero-start parts) must fit the 256 compute units of one MI355X, and the
+// sequences must be long enough for the added output pass.  The first segment
+// takes 59.5 % of the chunks: a 32-column chunk costs a workgroup about
+// 2.38 us and a 64-column one 3.41 us, so both segments then end together.
+SplitPlan chunk_split_plan(int B, int T, int H, int dk, int dv) {
+    SplitPlan sp;
+    const long units = (long)B * H;
+    const long nch = (T + kChunk - 1) / kChunk;
+    if (dk != 128 || dv != 128 || units <= 0 || units * 8 > 256 || nch < 64) return sp;
+    const long c0 = (nch * 595 + 500) / 1000;
+    sp.l0 = (int)(c0 * kChunk);
+    sp.l1 = T - sp.l0;
+    const size_t st = round256((size_t)units * dk * dv * 4);
+    sp.off_sm = 0;
+    sp.off_phi = st;
+    sp.off_r = 2 * st;
+    sp.off_z = 3 * st;
+    // transition-part outputs: rows seq * T + tau, tau < l1, of dk bf16 per head
+    const size_t zrows = (size_t)(B - 1) * T + sp.l1;
+    sp.bytes = sp.off_z + round256(zrows * H * dk * 2);
+    return sp;
+}
+
 }  // namespace kda

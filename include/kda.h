@@ -124,6 +124,32 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int num
                                     kda_dtype dtype);
 
 /*
+ * Device workspace (bytes) with which a dense bf16 call of kda_chunk_fwd,
+ * kda_chunk_fwd_gated or kda_chunk_fwd_fused runs each sequence in two time
+ * segments at once; 0 when the shape does not qualify (it needs
+ * dk = dv = 128, at most 32 (batch, head) units and T >= 4033, i.e. at least
+ * 64 chunks).
+ * Source: the update of "Kimi Delta Attention", section "KDA 的更新式", is
+ * affine in the state, so the second segment's states are Phi_t X + R_t for
+ * the unknown start X, and the chunk-parallel state passing of the
+ * kongchang.com page, section "硬件效率的优化策略", then applies inside one
+ * sequence: the first segment (from initial_state) and the second segment's
+ * transition part Phi (from the identity, zero values) and zero-start part R
+ * run concurrently (two more streams of the library's own, forked from and
+ * joined back to `stream` with events), and a last pass forms
+ * o_t = o^R_t + Sm^T z_t and the final state Phi_T Sm + R_T from the first
+ * segment's final state Sm.
+ * A call whose workspace holds at least this many bytes, 256-byte aligned,
+ * with o 8-byte aligned, takes that path; otherwise (and for
+ * kda_chunk_fwd_noalloc) the single pass.
+ * The two agree up to rounding (z_t = scale Phi_t^T q_t is kept in bf16, Sm
+ * enters the output products as two bf16 parts with fp32 accumulation); each
+ * is deterministic.  Concurrent calls on one device share those streams and
+ * serialise their second-segment kernels on them.
+ */
+size_t kda_chunk_fwd_split_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dtype);
+
+/*
  * Chunk-wise forward (64-token chunks) over whole sequences.
  * Source: the chunk-wise mode of bugfactory.tech news 3610, fifth paragraph,
  * and the chunk-parallel scheme on the kongchang.com page, section
@@ -195,8 +221,10 @@ kda_status kda_chunk_fwd_fused(const void *q, const void *k, const void *v, cons
 /*
  * kda_chunk_fwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
- * the same arguments without the workspace, and the same results bit for bit.
- * It calls no hipMalloc, hipFree or allocating library routine.  The only
+ * the same arguments without the workspace, and the same results bit for bit
+ * as kda_chunk_fwd's single pass (a dense call that takes kda_chunk_fwd's
+ * two-segment path, see kda_chunk_fwd_split_workspace_size, agrees with it up
+ * to rounding).  It calls no hipMalloc, hipFree or allocating library routine.  The only
  * scratch, the longest-first order of the packed sequences, lives in a
  * fixed device array of KDA_NOALLOC_MAX_SEQS ints (256 KiB) that each GPU
  * the library runs on holds until the process ends; the order is rewritten

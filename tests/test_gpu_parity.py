@@ -233,27 +233,32 @@ def _heads(d, heads):
 
 
 def test_chunk_full_T65536_all_heads(kda):
-    """The long-context workload, every head compared over all 65536 tokens;
-    the oracle runs 8 heads at a time to bound host memory."""
+    """The long-context workload, every head compared over all 65536 tokens,
+    through both the two-segment path (the binding's default for this shape)
+    and the single pass; the oracle runs 8 heads at a time to bound host
+    memory."""
     d = gen.chunk_inputs(CONFIGS[2], device=dev())
-    o, s = run(kda, d)
+    B, T, H, dk = d["q"].shape
+    assert kda.kda_chunk_fwd_split_workspace_size(B, T, H, dk, d["v"].shape[-1]) > 0
+    outs = {"split": run(kda, d), "single": run(kda, d, split=False)}
     torch.cuda.synchronize()
-    num_o = num_s = 0.0
+    num = {p: [0.0, 0.0] for p in outs}
     den_o = den_s = 0.0
-    H = d["q"].shape[2]
     for h0 in range(0, H, 8):
         heads = list(range(h0, min(H, h0 + 8)))
         ro, rs = ref(_heads(d, heads))
-        go = o[:, :, heads].double().cpu().numpy()
-        gs = s[:, heads].double().cpu().numpy()
-        assert not np.isnan(go).any() and not np.isnan(gs).any()
-        num_o = max(num_o, float(np.max(np.abs(go - ro))))
-        num_s = max(num_s, float(np.max(np.abs(gs - rs))))
         den_o = max(den_o, float(np.max(np.abs(ro))))
         den_s = max(den_s, float(np.max(np.abs(rs))))
-    eo, es = num_o / den_o, num_s / den_s
-    print("B1 H32 T65536 all heads: err o %.2e state %.2e" % (eo, es))
-    assert eo <= 2e-2 and es <= 2e-2
+        for p, (o, s) in outs.items():
+            go = o[:, :, heads].double().cpu().numpy()
+            gs = s[:, heads].double().cpu().numpy()
+            assert not np.isnan(go).any() and not np.isnan(gs).any()
+            num[p][0] = max(num[p][0], float(np.max(np.abs(go - ro))))
+            num[p][1] = max(num[p][1], float(np.max(np.abs(gs - rs))))
+    for p in outs:
+        eo, es = num[p][0] / den_o, num[p][1] / den_s
+        print("B1 H32 T65536 all heads, %s: err o %.2e state %.2e" % (p, eo, es))
+        assert eo <= 2e-2 and es <= 2e-2
 
 
 def test_chunk_full_varlen_all_units(kda):
