@@ -22,6 +22,11 @@ some 25 ms of chunk-kernel work, and the other legs' kernels leave it at its
 steady value, so the headline's K timed steps after its W warm-up steps run at
 the clock a busy GPU holds whatever W is.
 
+Before the legs it measures what this GPU reaches on the roofline's two
+resources with its own kernels (libkda_peaks.so): a streaming copy, a
+read-only stream and a loop of bf16 matrix-core products ("achievable"); the
+headline also reports its rates as fractions of those.
+
 Each workload reports a roofline: algorithmic bytes (every input read once,
 every output written once) and, for the chunk forward, algorithmic matrix
 flops, divided by the measured launch time, against the published MI355X
@@ -39,7 +44,7 @@ entry points prepare them in the kernel.  --only runs a single workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--gate channel|head|none] [--fused] [--only NAME] [--no-flush]
-                       [--calib-copy] [--prep-baseline]
+                       [--calib-copy] [--prep-baseline] [--no-peaks]
 """
 import argparse
 import hashlib
@@ -197,6 +202,59 @@ def roofline(bytes_alg, ms, kernel, flops_alg=None):
     return r
 
 
+def achievable_peaks(torch, dev, stream):
+    """What this GPU reaches on the two roofline resources, measured with the
+    benchmark's own kernels (libkda_peaks.so): a streaming 1 GiB copy and a
+    1 GiB read-only stream (HBM GB/s; the copy counts its reads and writes)
+    and independent chains of bf16 16x16x32 matrix-core products on every
+    SIMD (TFLOP/s).  Each is the best of 5 timed launches after 2 warm-ups."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_delta_rule_38_amd", "libkda_peaks.so"))
+    vp, sz, i, u32, f = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32,
+                         ctypes.c_float)
+    lib.kda_peak_copy.argtypes = [vp, vp, sz, i, vp]
+    lib.kda_peak_read.argtypes = [vp, sz, u32, vp, i, vp]
+    lib.kda_peak_mfma.argtypes = [i, f, vp, i, vp]
+    st = ctypes.c_void_p(stream.cuda_stream)
+    blocks = 256 * 8
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def best(launch):
+        for _ in range(2):
+            launch()
+        ts = []
+        for _ in range(5):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return min(ts)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("peak probe failed with hipError %d" % rc)
+    t_copy = best(lambda: ok(lib.kda_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks,
+                                               st)))
+    t_read = best(lambda: ok(lib.kda_peak_read(src.data_ptr(), nbytes, 0x9E3779B9,
+                                               sink.data_ptr(), blocks, st)))
+    iters = 20000
+    chains = lib.kda_peak_mfma_chains()
+    t_mfma = best(lambda: ok(lib.kda_peak_mfma(iters, 12345.678, sink.data_ptr(), blocks, st)))
+    flops = blocks * 4 * chains * iters * 2 * 16 * 16 * 32
+    del src, dst, sink
+    return {"hbm_copy_GBs": 2 * nbytes / t_copy / 1e9, "hbm_read_GBs": nbytes / t_read / 1e9,
+            "mfma_bf16_TFs": flops / t_mfma / 1e12,
+            "how": "libkda_peaks.so: 1 GiB streaming copy (reads + writes counted), 1 GiB "
+                   "read-only stream, %d workgroups x 4 waves x %d chains of %d bf16 "
+                   "16x16x32 MFMA; best of 5 launches" % (blocks, chains, iters)}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -218,6 +276,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the achievable HBM and matrix-core rates")
     ap.add_argument("--only", choices=WORKLOADS, default=None,
                     help="run one workload only (profiling runs)")
     ap.add_argument("--no-flush", action="store_true",
@@ -296,6 +356,8 @@ def main():
         return {"median_ms": ts[len(ts) // 2], "min_ms": ts[0], "launches": n}
 
     out = {}
+    if not args.no_peaks:
+        out["achievable"] = achievable_peaks(torch, dev, stream)
     cfg = CONFIGS[1]
     B, T, H, dk, dv = cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv
     d = None
@@ -354,6 +416,12 @@ def main():
                 "timed_after": [w for w in ("long_context", "varlen", "backward", "decode",
                                             "gdn2") if run[w]],
             })
+            if "achievable" in out:
+                rf = out["roofline"]
+                rf["frac_of_achievable_read"] = rf["achieved"] / out["achievable"]["hbm_read_GBs"]
+                if "mfma" in rf:
+                    rf["mfma"]["frac_of_achievable"] = (rf["mfma"]["achieved"] /
+                                                        out["achievable"]["mfma_bf16_TFs"])
             if not args.no_flush:
                 out["roofline"]["hbm_cold"] = flushed(step, 20)
 

@@ -31,7 +31,7 @@ namespace kda {
 
 namespace {
 constexpr int SD = 128;  // dk = dv of the split path
-constexpr int OUT_TOKENS = 256;  // second-segment tokens per workgroup of split_out_kernel
+constexpr int OUT_TOKENS = 512;  // second-segment tokens per workgroup of split_out_kernel
 }  // namespace
 
 // Final states: sT[u] = Phi[u] Sm[u] + R[u] (fp32, 128 x 128 per unit).
@@ -72,20 +72,30 @@ __global__ __launch_bounds__(256) void split_state_kernel(const float* __restric
 
 // Second-segment outputs: o_t += Sm^T z_t, in place over o^R_t.
 // Block (u, tb): unit u = seq * H + h, second-segment tokens
-// tb * OUT_TOKENS .. of it.  Wave w owns value columns 32 w .. 32 w + 31 as
-// two 16-row tiles of C^T = Sm^T Z^T (rows: value columns j, columns: tokens),
-// so that a lane holds four adjacent value columns of one token and writes
-// them with one 8-byte store.  The A fragments (Sm^T, split in bf16 hi and lo
-// parts) stay in registers for all the block's tokens.
+// tb * OUT_TOKENS .. of it, in tiles of 16 tokens.  Wave w owns value columns
+// 32 w .. 32 w + 31 as two 16-row tiles of C^T = Sm^T Z^T (rows: value
+// columns j, columns: tokens), so that a lane holds four adjacent value
+// columns of one token and writes them with one 8-byte store.  The A
+// fragments (Sm^T, split in bf16 hi and lo parts, each with its own
+// accumulator chain) stay in registers for all the block's tokens.  Each z
+// tile (16 rows of 256 bytes) is loaded once per block, one 16-byte word per
+// thread, and handed to the waves through LDS (rows 288 bytes apart, so the
+// fragment reads are free of bank conflicts); z and o^R are loaded OUT_AHEAD
+// tiles before their use.
 //   o: the caller's output, rows seq * T + L0 + tau; z: rows seq * T + tau.
+constexpr int OUT_AHEAD = 4;
+constexpr int ZPITCH = SD + 16;  // bf16 elements per LDS row of a z tile
 __global__ __launch_bounds__(256) void split_out_kernel(const float* __restrict__ sm,
                                                         const bf16_t* __restrict__ z,
                                                         bf16_t* __restrict__ o, int H, int T,
                                                         int L0, int L1) {
     using Mf = Mma<bf16_t>;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ __align__(16) bf16_t zs[2][16 * ZPITCH];
     const int u = blockIdx.x, seq = u / H, h = u % H;
     const int tb0 = blockIdx.y * OUT_TOKENS;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, ln = l & 15, lg = l >> 4;
+    const int t = threadIdx.x;
+    const int w = t >> 6, l = t & 63, ln = l & 15, lg = l >> 4;
     const float* smu = sm + (size_t)u * SD * SD;
 
     Mf::F32 ahi[2][4], alo[2][4];
@@ -105,41 +115,62 @@ __global__ __launch_bounds__(256) void split_out_kernel(const float* __restrict_
     }
 
     const size_t rs = (size_t)H * SD;  // elements per token row
-    const bf16_t* zu = z + (size_t)seq * T * rs + (size_t)h * SD;
-    bf16_t* ou = o + ((size_t)seq * T + L0) * rs + (size_t)h * SD;
+    const int zr = t >> 4, zc = t & 15;  // this thread's row and 16-byte word of a z tile
+    const bf16_t* zu = z + (size_t)seq * T * rs + (size_t)h * SD + 8 * zc;
+    bf16_t* ou = o + ((size_t)seq * T + L0) * rs + (size_t)h * SD + 32 * w + 4 * lg;
     const int tend = min(L1, tb0 + OUT_TOKENS);
-    for (int tau0 = tb0; tau0 < tend; tau0 += 16) {
-        const int tau = tau0 + ln;  // this lane's token (column of the product)
-        const bool ok = tau < tend;
-        Mf::F32 bz[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (ok) {
-                bz[s] = Mf::ld32(zu + (size_t)tau * rs + 32 * s + 8 * lg);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bz[s].v[e] = (bf16_t)0.f;
-            }
-        }
+    const int ntiles = (tend - tb0 + 15) / 16;
+
+    u32x4 zw[OUT_AHEAD];       // z words in flight
+    bf16x4 rw[OUT_AHEAD][2];   // o^R of the lane's token, both column tiles
+    auto load = [&](int n, int slot) __attribute__((always_inline)) {
+        const int tau0 = tb0 + 16 * n;
+        const int tz = tau0 + zr, to = tau0 + ln;
+        if (tz < tend) zw[slot] = *reinterpret_cast<const u32x4*>(zu + (size_t)tz * rs);
+        else zw[slot] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
-            bf16_t* op = ou + (size_t)tau * rs + 32 * w + 16 * jt + 4 * lg;
-            f32x4 acc = zero4();
-            if (ok) {
-                const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(op);
+            if (to < tend) {
+                rw[slot][jt] = *reinterpret_cast<const bf16x4*>(ou + (size_t)to * rs + 16 * jt);
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = to_f32(r4[e]);
+                for (int e = 0; e < 4; ++e) rw[slot][jt][e] = (bf16_t)0.f;
             }
+        }
+    };
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                acc = Mf::k32(ahi[jt][s], bz[s], acc);
-                acc = Mf::k32(alo[jt][s], bz[s], acc);
-            }
-            if (ok) {
-                bf16x4 r4;
+    for (int k = 0; k < OUT_AHEAD; ++k) load(k, k);
+
+    for (int n0 = 0; n0 < ntiles; n0 += OUT_AHEAD) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r4[e] = (bf16_t)acc[e];
-                *reinterpret_cast<bf16x4*>(op) = r4;
+        for (int k = 0; k < OUT_AHEAD; ++k) {
+            const int n = n0 + k;
+            if (n < ntiles) {  // the same for every thread of the block
+                bf16_t* zb = zs[n & 1];
+                *reinterpret_cast<u32x4*>(zb + zr * ZPITCH + 8 * zc) = zw[k];
+                __syncthreads();
+                Mf::F32 bz[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) bz[s] = Mf::ld32(zb + ln * ZPITCH + 32 * s + 8 * lg);
+                const int tau = tb0 + 16 * n + ln;
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    f32x4 a0, a1 = zero4();
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a0[e] = to_f32(rw[k][jt][e]);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        a0 = Mf::k32(ahi[jt][s], bz[s], a0);
+                        a1 = Mf::k32(alo[jt][s], bz[s], a1);
+                    }
+                    if (tau < tend) {
+                        bf16x4 r4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) r4[e] = (bf16_t)(a0[e] + a1[e]);
+                        *reinterpret_cast<bf16x4*>(ou + (size_t)tau * rs + 16 * jt) = r4;
+                    }
+                }
+                if (n + OUT_AHEAD < ntiles) load(n + OUT_AHEAD, k);
             }
         }
     }

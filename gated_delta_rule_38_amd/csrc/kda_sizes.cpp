@@ -40,14 +40,15 @@ size_t bwd_chunk_workspace_bytes(long tokens_total, int nseq, int H, int dk, int
 // first segment, two 64-column slices each of the second segment's transition
 // and zero-start parts) must fit the 256 compute units of one MI355X, and the
 // sequences must be long enough for the added output pass.  The first segment
-// takes 59.5 % of the chunks: a 32-column chunk costs a workgroup about
-// 2.38 us and a 64-column one 3.41 us, so both segments then end together.
+// takes 58.3 % of the chunks: with all three parts running, a 32-column chunk
+// costs a workgroup about 2.52 us and a 64-column one 3.52 us, so both
+// segments then end together.
 SplitPlan chunk_split_plan(int B, int T, int H, int dk, int dv) {
     SplitPlan sp;
     const long units = (long)B * H;
     const long nch = (T + kChunk - 1) / kChunk;
     if (dk != 128 || dv != 128 || units <= 0 || units * 8 > 256 || nch < 64) return sp;
-    const long c0 = (nch * 595 + 500) / 1000;
+    const long c0 = (nch * 583 + 500) / 1000;
     sp.l0 = (int)(c0 * kChunk);
     sp.l1 = T - sp.l0;
     const size_t st = round256((size_t)units * dk * dv * 4);

@@ -75,15 +75,15 @@ def lib():
 def test_split_plan_sizes(lib):
     import torch
     f = lib.kda_chunk_fwd_split_workspace_size
-    # the long-context workload: 1024 chunks, 609 in the first segment
-    l0 = 609 * 64
+    # the long-context workload: 1024 chunks, 597 in the first segment
+    l0 = 597 * 64
     l1 = 65536 - l0
     st = 32 * 128 * 128 * 4
     assert f(1, 65536, 32, 128, 128) == 3 * st + l1 * 32 * 128 * 2
     # two sequences: the transition outputs of both, rows seq * T + tau
     T = 5000
     nch = (T + 63) // 64
-    l0 = (nch * 595 + 500) // 1000 * 64
+    l0 = (nch * 583 + 500) // 1000 * 64
     zrows = T + (T - l0)
     z = (zrows * 3 * 128 * 2 + 255) // 256 * 256
     assert f(2, T, 3, 128, 128) == 3 * ((6 * 128 * 128 * 4 + 255) // 256 * 256) + z
