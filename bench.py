@@ -65,6 +65,10 @@ CHUNK = 64
 # the sources each timed kernel is compiled from (its counters go stale when any changes)
 KERNEL_SOURCES = {
     "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "chunk_walk.h", "chunk_common.h", "kda_device.h"],
+    # the two-segment path of long dense sequences: its three chunk-kernel
+    # launches, the final states and the output correction, and its plan
+    "chunk_split_path": ["chunk_split.hip", "chunk_fwd_bf16.hip", "chunk_walk.h", "chunk_common.h",
+                         "kda_device.h", "kda_sizes.cpp"],
     "recurrent_step_kernel": ["recurrent_step.hip", "kda_device.h"],
     "bwd_chunk_kernel": ["bwd_chunk.hip", "chunk_fwd.hip", "chunk_walk.h", "chunk_common.h",
                          "kda_device.h"],
@@ -479,7 +483,8 @@ def main():
                      "roofline": roofline(chunk_bytes(toks, c.H, c.dk, c.dv, nst,
                                                       initial=dd["initial_state"] is not None),
                                           lms,
-                                          "chunk_fwd_bf16_kernel[%s]" % name,
+                                          ("chunk_split_path[%s]" if split_b else
+                                           "chunk_fwd_bf16_kernel[%s]") % name,
                                           chunk_flops(toks, c.H, c.dk, c.dv))}
         del dd, ol, fl_, ws
 
