@@ -31,20 +31,22 @@ namespace kda {
 
 namespace {
 constexpr int SD = 128;  // dk = dv of the split path
-constexpr int OUT_TOKENS = 512;  // second-segment tokens per workgroup of split_out_kernel
+// second-segment tokens per output block: 36 tiles of 16, which deal the long-context
+// workload's blocks (32 units x 48) to 256 compute units, three at a time, in two whole rounds
+constexpr int OUT_TOKENS = 576;
 }  // namespace
 
 // Final states: sT[u] = Phi[u] Sm[u] + R[u] (fp32, 128 x 128 per unit).
-// Block (u, cb) forms columns 16 cb .. 16 cb + 15; thread t row t / 2 and
+// State block (u, cb) forms columns 16 cb .. 16 cb + 15; thread t row t / 2 and
 // eight of those columns.  Sm and sT may not overlap, but sT may be the
 // caller's initial state (read by the first segment, which has ended).
-__global__ __launch_bounds__(256) void split_state_kernel(const float* __restrict__ phi,
-                                                          const float* __restrict__ sm,
-                                                          const float* __restrict__ r,
-                                                          float* __restrict__ sT) {
+__device__ __forceinline__ void split_state_block(const float* __restrict__ phi,
+                                                  const float* __restrict__ sm,
+                                                  const float* __restrict__ r,
+                                                  float* __restrict__ sT, int u, int cb) {
     __shared__ float tile[SD][16];
-    const size_t ub = (size_t)blockIdx.x * SD * SD;
-    const int c0 = blockIdx.y * 16;
+    const size_t ub = (size_t)u * SD * SD;
+    const int c0 = cb * 16;
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void split_state_kernel(const float* __restric
 }
 
 // Second-segment outputs: o_t += Sm^T z_t, in place over o^R_t.
-// Block (u, tb): unit u = seq * H + h, second-segment tokens
+// Output block (u, tb): unit u = seq * H + h, second-segment tokens
 // tb * OUT_TOKENS .. of it, in tiles of 16 tokens.  Wave w owns value columns
 // 32 w .. 32 w + 31 as two 16-row tiles of C^T = Sm^T Z^T (rows: value
 // columns j, columns: tokens), so that a lane holds four adjacent value
@@ -83,17 +85,17 @@ __global__ __launch_bounds__(256) void split_state_kernel(const float* __restric
 // fragment reads are free of bank conflicts); z and o^R are loaded OUT_AHEAD
 // tiles before their use.
 //   o: the caller's output, rows seq * T + L0 + tau; z: rows seq * T + tau.
-constexpr int OUT_AHEAD = 4;
+constexpr int OUT_AHEAD = 6;
 constexpr int ZPITCH = SD + 16;  // bf16 elements per LDS row of a z tile
-__global__ __launch_bounds__(256) void split_out_kernel(const float* __restrict__ sm,
-                                                        const bf16_t* __restrict__ z,
-                                                        bf16_t* __restrict__ o, int H, int T,
-                                                        int L0, int L1) {
+__device__ __forceinline__ void split_out_block(const float* __restrict__ sm,
+                                                const bf16_t* __restrict__ z,
+                                                bf16_t* __restrict__ o, int H, int T, int L0,
+                                                int L1, int u, int tb) {
     using Mf = Mma<bf16_t>;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __shared__ __align__(16) bf16_t zs[2][16 * ZPITCH];
-    const int u = blockIdx.x, seq = u / H, h = u % H;
-    const int tb0 = blockIdx.y * OUT_TOKENS;
+    const int seq = u / H, h = u % H;
+    const int tb0 = tb * OUT_TOKENS;
     const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63, ln = l & 15, lg = l >> 4;
     const float* smu = sm + (size_t)u * SD * SD;
@@ -174,6 +176,22 @@ __global__ __launch_bounds__(256) void split_out_kernel(const float* __restrict_
             }
         }
     }
+}
+
+// The last step of a call, one launch: blocks (u, y) with y < nblk form
+// second-segment outputs, y = nblk + cb (when the final state is wanted) the
+// final state's columns 16 cb ...
+__global__ __launch_bounds__(256) void split_finish_kernel(const float* __restrict__ phi,
+                                                           const float* __restrict__ sm,
+                                                           const float* __restrict__ r,
+                                                           float* __restrict__ sT,
+                                                           const bf16_t* __restrict__ z,
+                                                           bf16_t* __restrict__ o, int H, int T,
+                                                           int L0, int L1, int nblk) {
+    if ((int)blockIdx.y < nblk)
+        split_out_block(sm, z, o, H, T, L0, L1, blockIdx.x, blockIdx.y);
+    else
+        split_state_block(phi, sm, r, sT, blockIdx.x, blockIdx.y - nblk);
 }
 
 namespace {
@@ -282,14 +300,10 @@ hipError_t launch_chunk_split(const ChunkArgs& a, void* ws, hipStream_t stream) 
             if ((e = hipStreamWaitEvent(stream, ax->join[i], 0)) != hipSuccess) return e;
         }
     }
-    if (a.sT) {
-        hipLaunchKernelGGL(split_state_kernel, dim3((unsigned)units, SD / 16), dim3(256), 0,
-                           stream, phi, sm, rr, a.sT);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    const unsigned nblk = (unsigned)((sp.l1 + OUT_TOKENS - 1) / OUT_TOKENS);
-    hipLaunchKernelGGL(split_out_kernel, dim3((unsigned)units, nblk), dim3(256), 0, stream, sm,
-                       zz, static_cast<bf16_t*>(a.o), a.H, a.T, sp.l0, sp.l1);
+    const int nblk = (sp.l1 + OUT_TOKENS - 1) / OUT_TOKENS;
+    hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)units, nblk + (a.sT ? SD / 16 : 0)),
+                       dim3(256), 0, stream, phi, sm, rr, a.sT, zz, static_cast<bf16_t*>(a.o),
+                       a.H, a.T, sp.l0, sp.l1, nblk);
     return hipGetLastError();
 }
 
