@@ -476,3 +476,15 @@ def test_gdn2_step_rejects_before_any_hip_call(lib, kw, code):
 def test_gdn2_step_empty_is_a_noop(lib):
     assert gdn2_step_call(lib, N=0) == SUCCESS
     assert gdn2_step_call(lib, H=0, alpha=None) == SUCCESS
+
+
+def test_chunk_split_workspace_is_range_checked(lib):
+    """A dense call whose workspace holds the two-segment path's buffers takes
+    that path, so the workspace must then not overlap an input or an output
+    (every case here is refused before any HIP call)."""
+    big = dict(B=1, T=65536, H=32, s0=None, sT=fake(7))
+    n = lib.kda_chunk_fwd_split_workspace_size(1, 65536, 32, 128, 128, 1)
+    assert n > 0
+    assert chunk_call(lib, **big, ws=fake(0), ws_bytes=n) == INVALID            # inside q
+    assert chunk_call(lib, **big, ws=fake(6, 1 << 20), ws_bytes=n) == INVALID  # inside o
+    assert chunk_call(lib, **big, ws=fake(7), ws_bytes=n) == INVALID           # is the final state
