@@ -17,10 +17,11 @@ launches that each follow a 1 GiB read (the 256 MB last-level cache then
 holds none of the launch's inputs): the HBM-cold figure beside the
 back-to-back one.
 
-The headline is timed last, after the other legs: the shader clock climbs for
-some 25 ms of chunk-kernel work, and the other legs' kernels leave it at its
-steady value, so the headline's K timed steps after its W warm-up steps run at
-the clock a busy GPU holds whatever W is.
+The headline is timed last, after the other legs, the chunk-kernel legs (long
+context, varlen) just before it: the shader clock climbs for some 25 ms of
+chunk-kernel work (and the memory-bound decode steps leave it lower), so the
+headline's K timed steps after its W warm-up steps run at the clock a busy GPU
+holds for this kernel whatever W is.
 
 Before the legs it measures what this GPU reaches on the roofline's two
 resources with its own kernels (libkda_peaks.so): a streaming copy, a
@@ -417,8 +418,8 @@ def main():
                 "roofline": roofline(chunk_bytes(B * T, H, dk, dv, B, gate=gate, ges=ges), ms, kname,
                                      chunk_flops(B * T, H, dk, dv)),
                 "timed_wall_s": wall,
-                "timed_after": [w for w in ("long_context", "varlen", "backward", "decode",
-                                            "gdn2") if run[w]],
+                "timed_after": [w for w in ("decode", "gdn2", "backward", "long_context",
+                                            "varlen") if run[w]],
             })
             if "achievable" in out:
                 rf = out["roofline"]
@@ -450,64 +451,6 @@ def main():
                     "fused_ms": ms}
             del o, fs
 
-
-    for name, ci in (("long_context", 2), ("varlen", 4)):
-        if not run[name]:
-            continue
-        c = CONFIGS[ci]
-        dd = gen.chunk_inputs(c, device=dev)
-        toks = dd["q"].shape[0] * dd["q"].shape[1]
-        nst = dd["cu_seqlens"].numel() - 1 if dd["cu_seqlens"] is not None else c.B
-        ol = torch.empty_like(dd["v"])
-        fl_ = torch.empty((nst, c.H, c.dk, c.dv), dtype=torch.float32, device=dev)
-        wsb = kda.kda_chunk_fwd_workspace_size(1, toks, c.H, c.dk, c.dv,
-                                               nst if dd["cu_seqlens"] is not None else 0)
-        # dense shapes with few units and long sequences take the two-segment
-        # path when the workspace holds its buffers
-        split_b = 0 if dd["cu_seqlens"] is not None else kda.kda_chunk_fwd_split_workspace_size(
-            c.B, c.T, c.H, c.dk, c.dv)
-        ws = torch.empty(max(1, wsb, split_b), dtype=torch.uint8, device=dev)
-
-        def lstep():
-            kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"],
-                              dd["initial_state"], cu_seqlens=dd["cu_seqlens"],
-                              cu_seqlens_host=dd["cu_seqlens_host"], o=ol, final_state=fl_,
-                              workspace=ws)
-        lms = timed(lstep, args.steps, args.warmup if args.only else max(5, args.warmup // 10))
-        desc = ("kda_chunk_fwd bf16 B1 H32 T65536 dk128 dv128 chunk64, zero initial state, "
-                "alpha = sigmoid(N(5,1))" if name == "long_context" else
-                "kda_chunk_fwd bf16 varlen: 64 packed sequences, lengths U{128..8192} "
-                "(%d tokens), H16 dk128 dv128, initial states N(0,0.02)" % toks)
-        out[name] = {"workload": desc, "ms_per_step": lms, "tokens_per_s": toks / (lms / 1e3),
-                     "path": "two time segments at once" if split_b else "single pass",
-                     "roofline": roofline(chunk_bytes(toks, c.H, c.dk, c.dv, nst,
-                                                      initial=dd["initial_state"] is not None),
-                                          lms,
-                                          ("chunk_split_path[%s]" if split_b else
-                                           "chunk_fwd_bf16_kernel[%s]") % name,
-                                          chunk_flops(toks, c.H, c.dk, c.dv))}
-        del dd, ol, fl_, ws
-
-    if run["backward"]:
-        gg = torch.Generator(device=dev)
-        gg.manual_seed(11)
-        dout = torch.randn((B, T, H, dv), generator=gg, device=dev).to(d["q"].dtype)
-        dsT = torch.randn((B, H, dk, dv), generator=gg, device=dev)
-        ws = torch.empty(max(1, kda.kda_backward_workspace_size(B, T, H, dk, dv, 0)),
-                         dtype=torch.uint8, device=dev)
-
-        def bstep():
-            return kda.kda_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                    d["initial_state"], dout, dsT, workspace=ws)
-        nb = max(2, args.steps // 20)
-        bms = timed(bstep, nb, 2)
-        out["backward"] = {
-            "workload": "kda_backward bf16 B4 H16 T4096 dk128 dv128 (per-channel gate), "
-                        "fp32 gradients",
-            "ms_per_step": bms, "tokens_per_s": B * T / (bms / 1e3),
-            "roofline": roofline(backward_bytes(B * T, H, dk, dv, B), bms, "bwd_chunk_kernel",
-                                 backward_flops(B * T, H, dk, dv))}
-        del dout, dsT, ws
 
     if run["decode"]:
         dc = CONFIGS[3]
@@ -584,6 +527,8 @@ def main():
             "ms_per_step": gms, "tokens_per_s": B * T / (gms / 1e3),
             "roofline": roofline(gdn2_chunk_bytes(B * T, H, dk, dv, B), gms, "gdn2_chunk_kernel",
                                  gdn2_chunk_flops(B * T, H, dk, dv))}
+        if not args.no_flush:
+            out["gdn2"]["roofline"]["hbm_cold"] = flushed(gstep, 10)
         del g2, og, fg
         dc = CONFIGS[3]
         g = torch.Generator(device=dev)
@@ -609,9 +554,70 @@ def main():
             "roofline": roofline(gb, gus / 1e3, "gdn2_step_kernel")}
         del gst, steps_in, sin, ogd
 
-    # The headline leg runs after the other legs: their kernels bring the shader clock to its
-    # steady value (it climbs for some 25 ms of chunk-kernel work), so the headline's timed
-    # steps run at that clock whatever the warm-up count.  With --only headline the default
+    if run["backward"]:
+        gg = torch.Generator(device=dev)
+        gg.manual_seed(11)
+        dout = torch.randn((B, T, H, dv), generator=gg, device=dev).to(d["q"].dtype)
+        dsT = torch.randn((B, H, dk, dv), generator=gg, device=dev)
+        ws = torch.empty(max(1, kda.kda_backward_workspace_size(B, T, H, dk, dv, 0)),
+                         dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return kda.kda_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                    d["initial_state"], dout, dsT, workspace=ws)
+        nb = max(2, args.steps // 20)
+        bms = timed(bstep, nb, 2)
+        out["backward"] = {
+            "workload": "kda_backward bf16 B4 H16 T4096 dk128 dv128 (per-channel gate), "
+                        "fp32 gradients",
+            "ms_per_step": bms, "tokens_per_s": B * T / (bms / 1e3),
+            "roofline": roofline(backward_bytes(B * T, H, dk, dv, B), bms, "bwd_chunk_kernel",
+                                 backward_flops(B * T, H, dk, dv))}
+        del dout, dsT, ws
+
+    for name, ci in (("long_context", 2), ("varlen", 4)):
+        if not run[name]:
+            continue
+        c = CONFIGS[ci]
+        dd = gen.chunk_inputs(c, device=dev)
+        toks = dd["q"].shape[0] * dd["q"].shape[1]
+        nst = dd["cu_seqlens"].numel() - 1 if dd["cu_seqlens"] is not None else c.B
+        ol = torch.empty_like(dd["v"])
+        fl_ = torch.empty((nst, c.H, c.dk, c.dv), dtype=torch.float32, device=dev)
+        wsb = kda.kda_chunk_fwd_workspace_size(1, toks, c.H, c.dk, c.dv,
+                                               nst if dd["cu_seqlens"] is not None else 0)
+        # dense shapes with few units and long sequences take the two-segment
+        # path when the workspace holds its buffers
+        split_b = 0 if dd["cu_seqlens"] is not None else kda.kda_chunk_fwd_split_workspace_size(
+            c.B, c.T, c.H, c.dk, c.dv)
+        ws = torch.empty(max(1, wsb, split_b), dtype=torch.uint8, device=dev)
+
+        def lstep():
+            kda.kda_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"],
+                              dd["initial_state"], cu_seqlens=dd["cu_seqlens"],
+                              cu_seqlens_host=dd["cu_seqlens_host"], o=ol, final_state=fl_,
+                              workspace=ws)
+        lms = timed(lstep, args.steps, args.warmup if args.only else max(5, args.warmup // 10))
+        desc = ("kda_chunk_fwd bf16 B1 H32 T65536 dk128 dv128 chunk64, zero initial state, "
+                "alpha = sigmoid(N(5,1))" if name == "long_context" else
+                "kda_chunk_fwd bf16 varlen: 64 packed sequences, lengths U{128..8192} "
+                "(%d tokens), H16 dk128 dv128, initial states N(0,0.02)" % toks)
+        out[name] = {"workload": desc, "ms_per_step": lms, "tokens_per_s": toks / (lms / 1e3),
+                     "path": "two time segments at once" if split_b else "single pass",
+                     "roofline": roofline(chunk_bytes(toks, c.H, c.dk, c.dv, nst,
+                                                      initial=dd["initial_state"] is not None),
+                                          lms,
+                                          ("chunk_split_path[%s]" if split_b else
+                                           "chunk_fwd_bf16_kernel[%s]") % name,
+                                          chunk_flops(toks, c.H, c.dk, c.dv))}
+        if not args.no_flush:
+            out[name]["roofline"]["hbm_cold"] = flushed(lstep, 5)
+        del dd, ol, fl_, ws
+
+    # The headline leg runs after the other legs, the chunk-kernel legs (long context,
+    # varlen) last: they bring the shader clock to the chunk kernel's steady value (it climbs
+    # for some 25 ms of chunk-kernel work, and memory-bound decode steps leave it lower), so
+    # the headline's timed steps run at that clock whatever the warm-up count.  With --only headline the default
     # 200 warm-up steps do the same.
     headline_leg()
 
