@@ -45,7 +45,7 @@ entry points prepare them in the kernel.  --only runs a single workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--gate channel|head|none] [--fused] [--only NAME] [--no-flush]
-                       [--calib-copy] [--prep-baseline] [--no-peaks]
+                       [--calib-copy] [--prep-baseline] [--no-peaks] [--no-graph]
 """
 import argparse
 import hashlib
@@ -281,6 +281,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the decode steps replayed from a HIP graph")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the achievable HBM and matrix-core rates")
     ap.add_argument("--only", choices=WORKLOADS, default=None,
@@ -491,6 +493,37 @@ def main():
             "us_per_step": us, "tokens_per_s": dc.B / (us / 1e6),
             "roofline": roofline(dbytes, us / 1e3, kname),
         }
+        if not args.no_graph:
+            # the same 100 steps captured once in a HIP graph and replayed: checked against
+            # the eager steps from the same start, then timed over 5 replays
+            ge = ddc["state"].clone()
+            for t in range(dc.steps):
+                dstep(t, ge)
+            torch.cuda.synchronize()
+            oe = od.clone()
+            gs = ddc["state"].clone()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for t in range(dc.steps):
+                    dstep(t, gs)
+            graph.replay()
+            torch.cuda.synchronize()
+            same = bool(torch.equal(gs, ge) and torch.equal(od, oe))
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for _ in range(5):
+                graph.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            gus = g0.elapsed_time(g1) * 1e3 / (5 * dc.steps)
+            out["decode"]["graph"] = {
+                "what": "the 100 steps captured in one HIP graph, 5 replays timed",
+                "us_per_step": gus, "tokens_per_s": dc.B / (gus / 1e6),
+                "achieved_GBs": decode_bytes(dc.B, dc.H, dc.dk, dc.dv, gate=gate, ges=ges) /
+                (gus / 1e6) / 1e9, "replay_equals_eager": same}
+            out["decode"]["graph"]["frac"] = out["decode"]["graph"]["achieved_GBs"] / HBM_PEAK_GBS
+            del ge, gs, oe, graph
         if not args.no_flush:
             cnt = [0]
 
