@@ -59,3 +59,37 @@ def test_decode_steps_replayed_from_a_graph(kda):
         ro, st_r = oracle.step(*[a.cpu() for a in args[t]], st_r)
         assert rel(o_e[t], ro) <= TOL["bf16"]
     assert rel(st_e, st_r) <= TOL["bf16"]
+
+
+def test_two_segment_forward_replayed_from_a_graph(kda):
+    """The two-segment path forks onto the library's own streams with events and
+    joins back; captured from the caller's stream it becomes one graph, whose
+    replays give the eager call's outputs and final state bit for bit."""
+    dev = torch.device("cuda:0")
+    d = gen.draw_chunk(1, 4200, 2, 128, 128, "bf16", alpha_mu=4.0, s0_std=0.05, seed=21,
+                       device=dev)
+    n = kda.kda_chunk_fwd_split_workspace_size(1, 4200, 2, 128, 128)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    call = lambda o, fs: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                           d["initial_state"], o=o, final_state=fs, workspace=ws)
+    o_e = torch.empty_like(d["v"])
+    fs_e = torch.empty_like(d["initial_state"])
+    call(o_e, fs_e)  # eager first: the library's streams and events exist before the capture
+    torch.cuda.synchronize()
+
+    o_g = torch.empty_like(o_e)
+    fs_g = torch.empty_like(fs_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(o_g, fs_g)
+    for rep in range(3):
+        o_g.fill_(0)     # eager work between replays
+        fs_g.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), "replay %d: outputs differ from the eager call" % rep
+        assert torch.equal(fs_g, fs_e), "replay %d: final state differs from the eager call" % rep
+    ro, rs = oracle.forward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["initial_state"])
+    assert rel(o_e, ro) <= TOL["bf16"] and rel(fs_e, rs) <= TOL["bf16"]
